@@ -1,0 +1,28 @@
+"""MI355X-native blockwise online-softmax attention forward.
+
+The compute lives in ``libringattn.so`` (HIP kernels for gfx950 behind the C
+ABI of ``include/ringattn.h``); :mod:`.ringattn` is its ctypes binding and
+:mod:`.ring` the one-GPU ring driver that orders its calls.
+"""
+
+from .ringattn import (  # noqa: F401
+    DUAL_CHUNK,
+    STRIPED,
+    TILE_FULL,
+    TILE_PARTIAL,
+    TILE_SKIP,
+    RingAttnError,
+    attn_fwd,
+    attn_merge,
+    check_support,
+    classify_tiles,
+    inverse_reorder,
+    load_library,
+    make_desc,
+    reorder,
+    reorder_index,
+    tile_shape,
+    version,
+    workspace_size,
+)
+from .ring import RingBuffers, ring_forward  # noqa: F401

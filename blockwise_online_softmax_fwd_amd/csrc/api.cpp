@@ -1,0 +1,444 @@
+// C-ABI front end of libringattn: argument validation (host only, before any
+// HIP call), workspace carving and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "internal.h"
+#include "reorder_map.h"
+#include "ringattn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ra_status fail(ra_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ra_status hip_fail(hipError_t e, const char *what) {
+  return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t dtype_size(int32_t dt) { return dt == RA_BF16 ? 2 : 4; }
+bool dtype_ok(int32_t dt) { return dt == RA_BF16 || dt == RA_F32; }
+
+constexpr int64_t kMaxKeyTiles = 32768;  // class bytes of one query tile fit in LDS
+
+struct Resolved {
+  int64_t q_bs, kv_bs, o_bs, lse_bs, qm_bs, km_bs;
+  int32_t bm, bn, nqt, nkt, nt;
+};
+
+int64_t pick(int64_t given, int64_t dense) { return given == 0 ? dense : given; }
+
+ra_status check_desc(const ra_attn_desc *d, Resolved *r) {
+  if (!d) return fail(RA_ERR_NULL, "desc is NULL");
+  if (d->batch < 0 || d->q_len < 0 || d->kv_len < 0)
+    return fail(RA_ERR_SHAPE, "batch, q_len and kv_len must be >= 0 (got %d, %d, %d)", d->batch,
+                d->q_len, d->kv_len);
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(RA_ERR_SHAPE, "head counts must be >= 1 (got %d, %d)", d->num_q_heads,
+                d->num_kv_heads);
+  if (d->num_q_heads % d->num_kv_heads)
+    return fail(RA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->head_dim <= 0) return fail(RA_ERR_SHAPE, "head_dim must be > 0 (got %d)", d->head_dim);
+  if (!dtype_ok(d->qkv_dtype)) return fail(RA_ERR_DTYPE, "unknown qkv_dtype %d", d->qkv_dtype);
+  if (!dtype_ok(d->out_dtype)) return fail(RA_ERR_DTYPE, "unknown out_dtype %d", d->out_dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (!(d->scale > 0.0f) || !isfinite(d->scale))
+    return fail(RA_ERR_SHAPE, "scale must be finite and > 0");
+  if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_SHAPE, "causal must be 0 or 1");
+  if (d->window_left < -1 || d->window_right < -1)
+    return fail(RA_ERR_SHAPE, "window sizes must be -1 or >= 0 (got %d, %d)", d->window_left,
+                d->window_right);
+  const int64_t B = d->batch, Tq = d->q_len, Tk = d->kv_len, Hq = d->num_q_heads,
+                Hkv = d->num_kv_heads, D = d->head_dim;
+  const int64_t strides[6] = {d->q_batch_stride,   d->kv_batch_stride,     d->o_batch_stride,
+                              d->lse_batch_stride, d->q_meta_batch_stride, d->kv_meta_batch_stride};
+  for (int i = 0; i < 6; ++i)
+    if (strides[i] < 0) return fail(RA_ERR_SHAPE, "batch strides must be >= 0");
+  r->q_bs = pick(d->q_batch_stride, Tq * Hq * D);
+  r->kv_bs = pick(d->kv_batch_stride, Tk * Hkv * D);
+  r->o_bs = pick(d->o_batch_stride, Tq * Hq * D);
+  r->lse_bs = pick(d->lse_batch_stride, Tq * Hq);
+  r->qm_bs = pick(d->q_meta_batch_stride, Tq);
+  r->km_bs = pick(d->kv_meta_batch_stride, Tk);
+  if (B > 1) {
+    if (r->q_bs < Tq * Hq * D || r->o_bs < Tq * Hq * D || r->kv_bs < Tk * Hkv * D ||
+        r->lse_bs < Tq * Hq || r->qm_bs < Tq || r->km_bs < Tk)
+      return fail(RA_ERR_SHAPE, "a batch stride is smaller than one batch row");
+  }
+  if (d->qkv_dtype == RA_BF16) {
+    r->nt = ra::bf16_token_subtiles(d->num_q_heads / d->num_kv_heads);
+    r->bm = 32 * r->nt;
+    r->bn = ra::kBnBf16;
+  } else {
+    r->nt = 0;
+    r->bm = ra::kBmF32;
+    r->bn = ra::kBnF32;
+  }
+  const int64_t nqt = (Tq + r->bm - 1) / r->bm, nkt = (Tk + r->bn - 1) / r->bn;
+  if (nkt > kMaxKeyTiles)
+    return fail(RA_ERR_UNSUPPORTED, "kv_len %lld exceeds %lld key tiles of %d tokens",
+                (long long)Tk, (long long)kMaxKeyTiles, r->bn);
+  if (B * Hq * nqt >= (int64_t)1 << 31)
+    return fail(RA_ERR_UNSUPPORTED, "too many query tiles for one launch");
+  r->nqt = (int32_t)nqt;
+  r->nkt = (int32_t)nkt;
+  return RA_OK;
+}
+
+bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+size_t span_bytes(int64_t batch, int64_t bs, int64_t row_elems, size_t es) {
+  if (batch <= 0 || row_elems <= 0) return 0;
+  return (size_t)((batch - 1) * bs + row_elems) * es;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+ra_status check_meta(const ra_attn_desc *d, const Resolved &r, const int32_t *qid,
+                     const int32_t *qpos, const int32_t *kid, const int32_t *kpos) {
+  if (d->batch > 0 && d->q_len > 0 && (!qid || !qpos))
+    return fail(RA_ERR_NULL, "query segment ids / positions are NULL");
+  if (d->batch > 0 && d->kv_len > 0 && (!kid || !kpos))
+    return fail(RA_ERR_NULL, "key segment ids / positions are NULL");
+  if (!aligned(qid, 4) || !aligned(qpos, 4) || !aligned(kid, 4) || !aligned(kpos, 4))
+    return fail(RA_ERR_ALIGN, "segment metadata must be 4-byte aligned");
+  (void)r;
+  return RA_OK;
+}
+
+ra_status check_workspace(const Resolved &r, int32_t batch, const void *ws, size_t ws_bytes) {
+  const ra::WorkspaceLayout L = ra::workspace_layout(batch, r.nqt, r.nkt);
+  if (L.total > 0 && !ws) return fail(RA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (ws_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, L.total);
+  if (!aligned(ws, 256)) return fail(RA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return RA_OK;
+}
+
+ra::Schedule carve(void *ws, const Resolved &r, int32_t batch) {
+  const ra::WorkspaceLayout L = ra::workspace_layout(batch, r.nqt, r.nkt);
+  char *base = (char *)ws;
+  ra::Schedule s;
+  s.qsum = (ra::TileSum *)(base + L.qsum);
+  s.ksum = (ra::TileSum *)(base + L.ksum);
+  s.count = (int32_t *)(base + L.count);
+  s.pairs = (int64_t *)(base + L.pairs);
+  s.list = (uint32_t *)(base + L.list);
+  return s;
+}
+
+ra::MaskParams mask_of(const ra_attn_desc *d) {
+  ra::MaskParams m;
+  m.causal = d->causal;
+  m.wl = d->window_left;
+  m.wr = d->window_right;
+  return m;
+}
+
+ra_status run_schedule(const ra_attn_desc *d, const Resolved &r, const ra::Schedule &s,
+                       const int32_t *qid, const int32_t *qpos, const int32_t *kid,
+                       const int32_t *kpos, int8_t *classes, hipStream_t st) {
+  hipError_t e = ra::launch_summaries(qid, qpos, r.qm_bs, d->batch, d->q_len, r.bm, r.nqt, s.qsum, st);
+  if (e != hipSuccess) return hip_fail(e, "tile summaries (queries)");
+  e = ra::launch_summaries(kid, kpos, r.km_bs, d->batch, d->kv_len, r.bn, r.nkt, s.ksum, st);
+  if (e != hipSuccess) return hip_fail(e, "tile summaries (keys)");
+  e = ra::launch_classify(s, qid, qpos, kid, kpos, r.qm_bs, r.km_bs, d->batch, d->q_len, d->kv_len,
+                          r.bm, r.bn, r.nqt, r.nkt, mask_of(d), classes, st);
+  if (e != hipSuccess) return hip_fail(e, "tile classification");
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ra_version(void) { return "libringattn 0.1.0 (gfx950)"; }
+
+const char *ra_status_string(ra_status s) {
+  switch (s) {
+    case RA_OK: return "ok";
+    case RA_ERR_NULL: return "null pointer";
+    case RA_ERR_SHAPE: return "bad shape, stride or window";
+    case RA_ERR_DTYPE: return "bad dtype";
+    case RA_ERR_ALIGN: return "misaligned pointer or stride";
+    case RA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case RA_ERR_WORKSPACE: return "workspace missing or too small";
+    case RA_ERR_ALIAS: return "overlapping buffers";
+    case RA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *ra_last_error(void) { return g_last_error.c_str(); }
+
+ra_status ra_check_support(const ra_attn_desc *desc) {
+  Resolved r;
+  return check_desc(desc, &r);
+}
+
+ra_status ra_tile_shape(const ra_attn_desc *desc, int32_t *bm, int32_t *bn) {
+  Resolved r;
+  const ra_status st = check_desc(desc, &r);
+  if (st != RA_OK) return st;
+  if (!bm || !bn) return fail(RA_ERR_NULL, "output pointer is NULL");
+  *bm = r.bm;
+  *bn = r.bn;
+  return RA_OK;
+}
+
+ra_status ra_attn_fwd_workspace_size(const ra_attn_desc *desc, size_t *bytes) {
+  Resolved r;
+  const ra_status st = check_desc(desc, &r);
+  if (st != RA_OK) return st;
+  if (!bytes) return fail(RA_ERR_NULL, "bytes is NULL");
+  *bytes = ra::workspace_layout(desc->batch, r.nqt, r.nkt).total;
+  return RA_OK;
+}
+
+ra_status ra_attn_fwd(const ra_attn_desc *d, const void *q, const void *k, const void *v,
+                      const int32_t *qid, const int32_t *qpos, const int32_t *kid,
+                      const int32_t *kpos, void *o, float *lse, void *workspace,
+                      size_t workspace_bytes, ra_stream_t stream) {
+  Resolved r;
+  ra_status st = check_desc(d, &r);
+  if (st != RA_OK) return st;
+  const bool has_q = d->batch > 0 && d->q_len > 0;
+  const bool has_k = d->batch > 0 && d->kv_len > 0;
+  if (has_q && (!q || !o || !lse)) return fail(RA_ERR_NULL, "q, o or lse is NULL");
+  if (has_k && (!k || !v)) return fail(RA_ERR_NULL, "k or v is NULL");
+  st = check_meta(d, r, qid, qpos, kid, kpos);
+  if (st != RA_OK) return st;
+  const size_t es = dtype_size(d->qkv_dtype), os = dtype_size(d->out_dtype);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(RA_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if ((r.q_bs * es) % 16 || (r.kv_bs * es) % 16 || (r.o_bs * os) % 16)
+    return fail(RA_ERR_ALIGN, "batch strides of q, k, v and o must be multiples of 16 bytes");
+  if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
+  const int64_t D = d->head_dim;
+  const size_t q_span = span_bytes(d->batch, r.q_bs, (int64_t)d->q_len * d->num_q_heads * D, es);
+  const size_t kv_span = span_bytes(d->batch, r.kv_bs, (int64_t)d->kv_len * d->num_kv_heads * D, es);
+  const size_t o_span = span_bytes(d->batch, r.o_bs, (int64_t)d->q_len * d->num_q_heads * D, os);
+  const size_t l_span = span_bytes(d->batch, r.lse_bs, (int64_t)d->q_len * d->num_q_heads, 4);
+  if (overlaps(o, o_span, q, q_span) || overlaps(o, o_span, k, kv_span) ||
+      overlaps(o, o_span, v, kv_span) || overlaps(lse, l_span, o, o_span) ||
+      overlaps(lse, l_span, q, q_span) || overlaps(lse, l_span, k, kv_span) ||
+      overlaps(lse, l_span, v, kv_span))
+    return fail(RA_ERR_ALIAS, "o / lse overlap an input or each other");
+  if (!has_q) return RA_OK;
+  st = check_workspace(r, d->batch, workspace, workspace_bytes);
+  if (st != RA_OK) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  const ra::Schedule sch = carve(workspace, r, d->batch);
+  st = run_schedule(d, r, sch, qid, qpos, kid, kpos, nullptr, s);
+  if (st != RA_OK) return st;
+
+  ra::AttnParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.qid = qid;
+  p.qpos = qpos;
+  p.kid = kid;
+  p.kpos = kpos;
+  p.o = o;
+  p.lse = lse;
+  p.list = sch.list;
+  p.count = sch.count;
+  p.q_bs = r.q_bs;
+  p.kv_bs = r.kv_bs;
+  p.o_bs = r.o_bs;
+  p.lse_bs = r.lse_bs;
+  p.qm_bs = r.qm_bs;
+  p.km_bs = r.km_bs;
+  p.batch = d->batch;
+  p.tq = d->q_len;
+  p.tk = d->kv_len;
+  p.hq = d->num_q_heads;
+  p.hkv = d->num_kv_heads;
+  p.group = d->num_q_heads / d->num_kv_heads;
+  p.nqt = r.nqt;
+  p.nkt = r.nkt;
+  p.scale = d->scale;
+  p.scale_log2 = d->scale * 1.4426950408889634f;
+  p.mask = mask_of(d);
+  const bool out_bf16 = d->out_dtype == RA_BF16;
+  const hipError_t e = d->qkv_dtype == RA_BF16
+                           ? ra::launch_attn_bf16(p, d->head_dim, r.nt, out_bf16, s)
+                           : ra::launch_attn_f32(p, d->head_dim, out_bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "attention forward");
+  return RA_OK;
+}
+
+ra_status ra_classify_tiles(const ra_attn_desc *d, const int32_t *qid, const int32_t *qpos,
+                            const int32_t *kid, const int32_t *kpos, int8_t *classes,
+                            int64_t *visible_pairs, void *workspace, size_t workspace_bytes,
+                            ra_stream_t stream) {
+  Resolved r;
+  ra_status st = check_desc(d, &r);
+  if (st != RA_OK) return st;
+  st = check_meta(d, r, qid, qpos, kid, kpos);
+  if (st != RA_OK) return st;
+  if (!aligned(visible_pairs, 8)) return fail(RA_ERR_ALIGN, "visible_pairs must be 8-byte aligned");
+  if (d->batch == 0) return RA_OK;
+  st = check_workspace(r, d->batch, workspace, workspace_bytes);
+  if (st != RA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const ra::Schedule sch = carve(workspace, r, d->batch);
+  st = run_schedule(d, r, sch, qid, qpos, kid, kpos, classes, s);
+  if (st != RA_OK) return st;
+  if (visible_pairs) {
+    const hipError_t e = ra::launch_pair_sums(sch.pairs, d->batch, r.nqt, visible_pairs, s);
+    if (e != hipSuccess) return hip_fail(e, "visible pair sums");
+  }
+  return RA_OK;
+}
+
+ra_status ra_attn_merge(const ra_merge_desc *d, const void *o_a, const float *lse_a,
+                        const void *o_b, const float *lse_b, void *o_out, float *lse_out,
+                        ra_stream_t stream) {
+  if (!d) return fail(RA_ERR_NULL, "desc is NULL");
+  if (d->batch < 0 || d->seq_len < 0 || d->num_heads < 1)
+    return fail(RA_ERR_SHAPE, "batch and seq_len must be >= 0, num_heads >= 1");
+  if (!dtype_ok(d->a_dtype) || !dtype_ok(d->b_dtype) || !dtype_ok(d->out_dtype))
+    return fail(RA_ERR_DTYPE, "unknown dtype");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  const int64_t strides[6] = {d->o_a_batch_stride,   d->o_b_batch_stride,   d->o_out_batch_stride,
+                              d->lse_a_batch_stride, d->lse_b_batch_stride, d->lse_out_batch_stride};
+  for (int i = 0; i < 6; ++i)
+    if (strides[i] < 0) return fail(RA_ERR_SHAPE, "batch strides must be >= 0");
+  const int64_t rows = (int64_t)d->seq_len * d->num_heads, elems = rows * d->head_dim;
+  const int64_t oa_bs = pick(d->o_a_batch_stride, elems), ob_bs = pick(d->o_b_batch_stride, elems),
+                oo_bs = pick(d->o_out_batch_stride, elems), la_bs = pick(d->lse_a_batch_stride, rows),
+                lb_bs = pick(d->lse_b_batch_stride, rows), lo_bs = pick(d->lse_out_batch_stride, rows);
+  if (d->batch > 1 && (oa_bs < elems || ob_bs < elems || oo_bs < elems || la_bs < rows ||
+                       lb_bs < rows || lo_bs < rows))
+    return fail(RA_ERR_SHAPE, "a batch stride is smaller than one batch row");
+  if (d->batch == 0 || rows == 0) return RA_OK;
+  if (!o_a || !o_b || !o_out || !lse_a || !lse_b || !lse_out)
+    return fail(RA_ERR_NULL, "a merge operand is NULL");
+  const size_t as = dtype_size(d->a_dtype), bs = dtype_size(d->b_dtype), os = dtype_size(d->out_dtype);
+  const size_t need_a = as * 4, need_b = bs * 4, need_o = os * 4;  // 4-element vectors
+  if (!aligned(o_a, need_a) || !aligned(o_b, need_b) || !aligned(o_out, need_o) ||
+      (oa_bs * as) % need_a || (ob_bs * bs) % need_b || (oo_bs * os) % need_o)
+    return fail(RA_ERR_ALIGN, "merge outputs/inputs must be aligned to 4 elements");
+  if (!aligned(lse_a, 4) || !aligned(lse_b, 4) || !aligned(lse_out, 4))
+    return fail(RA_ERR_ALIGN, "lse pointers must be 4-byte aligned");
+  const size_t sa = span_bytes(d->batch, oa_bs, elems, as), sb = span_bytes(d->batch, ob_bs, elems, bs),
+               so = span_bytes(d->batch, oo_bs, elems, os);
+  const size_t la = span_bytes(d->batch, la_bs, rows, 4), lb = span_bytes(d->batch, lb_bs, rows, 4),
+               lo = span_bytes(d->batch, lo_bs, rows, 4);
+  auto same = [](const void *x, const void *y, int64_t xs, int64_t ys, int xd, int yd) {
+    return x == y && xs == ys && xd == yd;
+  };
+  if (!same(o_out, o_a, oo_bs, oa_bs, d->out_dtype, d->a_dtype) && overlaps(o_out, so, o_a, sa))
+    return fail(RA_ERR_ALIAS, "o_out overlaps o_a without being the same tensor");
+  if (!same(o_out, o_b, oo_bs, ob_bs, d->out_dtype, d->b_dtype) && overlaps(o_out, so, o_b, sb))
+    return fail(RA_ERR_ALIAS, "o_out overlaps o_b without being the same tensor");
+  if (!same(lse_out, lse_a, lo_bs, la_bs, 0, 0) && overlaps(lse_out, lo, lse_a, la))
+    return fail(RA_ERR_ALIAS, "lse_out overlaps lse_a without being the same tensor");
+  if (!same(lse_out, lse_b, lo_bs, lb_bs, 0, 0) && overlaps(lse_out, lo, lse_b, lb))
+    return fail(RA_ERR_ALIAS, "lse_out overlaps lse_b without being the same tensor");
+  if (overlaps(lse_out, lo, o_out, so) || overlaps(lse_out, lo, o_a, sa) ||
+      overlaps(lse_out, lo, o_b, sb) || overlaps(o_out, so, lse_a, la) || overlaps(o_out, so, lse_b, lb))
+    return fail(RA_ERR_ALIAS, "an lse buffer overlaps an output buffer");
+  ra::MergeParams p;
+  p.oa = o_a;
+  p.ob = o_b;
+  p.la = lse_a;
+  p.lb = lse_b;
+  p.oo = o_out;
+  p.lo = lse_out;
+  p.oa_bs = oa_bs;
+  p.ob_bs = ob_bs;
+  p.oo_bs = oo_bs;
+  p.la_bs = la_bs;
+  p.lb_bs = lb_bs;
+  p.lo_bs = lo_bs;
+  p.batch = d->batch;
+  p.seq = d->seq_len;
+  p.heads = d->num_heads;
+  p.d = d->head_dim;
+  const hipError_t e = ra::launch_merge(p, d->a_dtype, d->b_dtype, d->out_dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "merge");
+  return RA_OK;
+}
+
+static ra_status check_reorder(int32_t batch, int32_t seq, int64_t row_bytes, int32_t cp,
+                               int32_t kind, int32_t stripe) {
+  if (batch < 0 || seq < 0) return fail(RA_ERR_SHAPE, "batch and seq_len must be >= 0");
+  if (row_bytes < 1) return fail(RA_ERR_SHAPE, "row_bytes must be >= 1");
+  if (cp < 1) return fail(RA_ERR_SHAPE, "cp_size must be >= 1");
+  if (kind == RA_REORDER_DUAL_CHUNK) {
+    if (seq % (2 * cp)) return fail(RA_ERR_SHAPE, "dual chunk needs seq_len %% (2*cp_size) == 0");
+  } else if (kind == RA_REORDER_STRIPED) {
+    if (stripe < 1) return fail(RA_ERR_SHAPE, "stripe_size must be >= 1");
+    if (seq % ((int64_t)cp * stripe))
+      return fail(RA_ERR_SHAPE, "striped needs seq_len %% (cp_size*stripe_size) == 0");
+  } else {
+    return fail(RA_ERR_SHAPE, "unknown reorder kind %d", kind);
+  }
+  return RA_OK;
+}
+
+static ra_status do_reorder(const void *src, void *dst, int32_t batch, int32_t seq, int64_t row_bytes,
+                            int32_t cp, int32_t kind, int32_t stripe, bool inverse,
+                            ra_stream_t stream) {
+  ra_status st = check_reorder(batch, seq, row_bytes, cp, kind, stripe);
+  if (st != RA_OK) return st;
+  if (batch == 0 || seq == 0) return RA_OK;
+  if (!src || !dst) return fail(RA_ERR_NULL, "src or dst is NULL");
+  const size_t bytes = (size_t)batch * seq * row_bytes;
+  if (overlaps(src, bytes, dst, bytes)) return fail(RA_ERR_ALIAS, "src and dst overlap");
+  const hipError_t e = ra::launch_reorder(src, dst, batch, seq, row_bytes, cp,
+                                          kind == RA_REORDER_STRIPED ? 1 : 0, stripe, inverse,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reorder");
+  return RA_OK;
+}
+
+ra_status ra_reorder(const void *src, void *dst, int32_t batch, int32_t seq_len, int64_t row_bytes,
+                     int32_t cp_size, int32_t kind, int32_t stripe_size, ra_stream_t stream) {
+  return do_reorder(src, dst, batch, seq_len, row_bytes, cp_size, kind, stripe_size, false, stream);
+}
+
+ra_status ra_inverse_reorder(const void *src, void *dst, int32_t batch, int32_t seq_len,
+                             int64_t row_bytes, int32_t cp_size, int32_t kind, int32_t stripe_size,
+                             ra_stream_t stream) {
+  return do_reorder(src, dst, batch, seq_len, row_bytes, cp_size, kind, stripe_size, true, stream);
+}
+
+ra_status ra_reorder_index(int32_t seq_len, int32_t cp_size, int32_t kind, int32_t stripe_size,
+                           int32_t inverse, int32_t *host_map) {
+  ra_status st = check_reorder(1, seq_len, 1, cp_size, kind, stripe_size);
+  if (st != RA_OK) return st;
+  if (seq_len > 0 && !host_map) return fail(RA_ERR_NULL, "host_map is NULL");
+  const int32_t k = kind == RA_REORDER_STRIPED ? 1 : 0;
+  for (int64_t p = 0; p < seq_len; ++p)
+    host_map[p] = (int32_t)(inverse ? ra::reorder_dst(p, seq_len, cp_size, k, stripe_size)
+                                    : ra::reorder_src(p, seq_len, cp_size, k, stripe_size));
+  return RA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Internal interface between the C-ABI front end (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ringattn.h"
+
+namespace ra {
+
+// Token tiles.  The bf16 MFMA forward works on query tiles of 32*NT tokens
+// (NT token sub-tiles of 32 per workgroup, 8/NT heads) and key tiles of 64;
+// the fp32 forward on 64 x 32.
+constexpr int kBnBf16 = 64;
+constexpr int kBnF32 = 32;
+constexpr int kBmF32 = 64;
+constexpr int kWaves = 8;  // waves per bf16 workgroup
+
+// Per-tile summary of a run of tokens (over valid, in-range tokens).
+struct TileSum {
+  int32_t nvalid;  // tokens with id != 0
+  int32_t ninr;    // in-range tokens
+  int32_t idmin, idmax;
+  int32_t posmin, posmax;
+  int32_t pad0, pad1;
+};
+
+struct MaskParams {
+  int32_t causal;
+  int32_t wl, wr;
+};
+
+struct Schedule {
+  TileSum *qsum;      // [B, nqt]
+  TileSum *ksum;      // [B, nkt]
+  int32_t *count;     // [B, nqt] non-skip key tiles per query tile
+  int64_t *pairs;     // [B, nqt] visible pairs per query tile
+  uint32_t *list;     // [B, nqt, nkt] key tile | 0x80000000 if partial
+};
+
+struct WorkspaceLayout {
+  size_t qsum, ksum, count, pairs, list, total;
+};
+
+WorkspaceLayout workspace_layout(int32_t batch, int32_t nqt, int32_t nkt);
+
+struct AttnParams {
+  const void *q, *k, *v;
+  const int32_t *qid, *qpos, *kid, *kpos;
+  void *o;
+  float *lse;
+  const uint32_t *list;
+  const int32_t *count;
+  int64_t q_bs, kv_bs, o_bs, lse_bs, qm_bs, km_bs;  // batch strides (elements)
+  int32_t batch, tq, tk, hq, hkv, group;
+  int32_t nqt, nkt;
+  float scale;       // score scale
+  float scale_log2;  // scale * log2(e)
+  MaskParams mask;
+};
+
+// Launchers (return the launch's hipError_t).
+hipError_t launch_summaries(const int32_t *ids, const int32_t *pos, int64_t meta_bs, int32_t batch,
+                            int32_t len, int32_t tile, int32_t ntiles, TileSum *out,
+                            hipStream_t stream);
+hipError_t launch_classify(const Schedule &s, const int32_t *qid, const int32_t *qpos,
+                           const int32_t *kid, const int32_t *kpos, int64_t qm_bs, int64_t km_bs,
+                           int32_t batch, int32_t tq, int32_t tk, int32_t bm, int32_t bn,
+                           int32_t nqt, int32_t nkt, MaskParams mask, int8_t *classes,
+                           hipStream_t stream);
+hipError_t launch_pair_sums(const int64_t *pairs, int32_t batch, int32_t nqt, int64_t *out,
+                            hipStream_t stream);
+// bf16 MFMA forward; nt = token sub-tiles per workgroup (1, 2, 4 or 8).
+hipError_t launch_attn_bf16(const AttnParams &p, int32_t head_dim, int32_t nt, bool out_bf16,
+                            hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams &p, int32_t head_dim, bool out_bf16,
+                           hipStream_t stream);
+
+struct MergeParams {
+  const void *oa, *ob;
+  const float *la, *lb;
+  void *oo;
+  float *lo;
+  int64_t oa_bs, ob_bs, oo_bs, la_bs, lb_bs, lo_bs;
+  int32_t batch, seq, heads, d;
+};
+hipError_t launch_merge(const MergeParams &p, int32_t a_dtype, int32_t b_dtype, int32_t out_dtype,
+                        hipStream_t stream);
+
+hipError_t launch_reorder(const void *src, void *dst, int32_t batch, int32_t seq, int64_t row_bytes,
+                          int32_t cp, int32_t kind, int32_t stripe, bool inverse,
+                          hipStream_t stream);
+
+// Heads per bf16 workgroup for a GQA group size, and the token sub-tiles.
+inline int32_t bf16_heads_per_wg(int32_t group) {
+  int32_t nh = 8;
+  while (nh > 1 && group % nh) nh >>= 1;
+  return nh;
+}
+inline int32_t bf16_token_subtiles(int32_t group) { return kWaves / bf16_heads_per_wg(group); }
+
+}  // namespace ra

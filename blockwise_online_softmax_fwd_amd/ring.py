@@ -1,0 +1,137 @@
+"""One-GPU ring driver: context-parallel ring attention's per-device loop, run
+for every rank in turn on one GPU.
+
+"Context parallelism and ring attention", section "Ring attention": a device
+keeps its query shard and, at each step, attends to the key/value block it
+holds, folds the result into a running softmax state ("Online softmax") and
+passes the block on; after R steps every local query has seen every allowed
+key.  Here the exchange is replaced by indexing: at step s rank r holds the
+chunk that started on rank (r - s) mod R (step 0 is its own chunk).  Before the
+loop the sequence is permuted for causal load balance and cut into R shards
+(TransformerEngine JAX tutorial, section 4); afterwards the output and the LSE
+are permuted back.  Every step is a call into libringattn; this module only
+slices views and orders the calls.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import ringattn as ra
+
+
+@dataclass
+class RingBuffers:
+    """Device buffers of one ring forward, reusable across calls of one shape."""
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    ids: torch.Tensor
+    pos: torch.Tensor
+    o: torch.Tensor
+    lse: torch.Tensor
+    acc: torch.Tensor
+    acc_lse: torch.Tensor
+    part: torch.Tensor
+    part_lse: torch.Tensor
+    workspace: torch.Tensor | None = None
+
+    @classmethod
+    def like(cls, q, k, ids, cp_size, partial_dtype=torch.float32, out_dtype=None):
+        b, t, hq, d = q.shape
+        n = t // cp_size
+        dev = q.device
+        od = q.dtype if out_dtype is None else out_dtype
+        return cls(
+            q=torch.empty_like(q), k=torch.empty_like(k), v=torch.empty_like(k),
+            ids=torch.empty_like(ids), pos=torch.empty_like(ids),
+            o=torch.empty((b, t, hq, d), dtype=od, device=dev),
+            lse=torch.empty((b, t, hq), dtype=torch.float32, device=dev),
+            acc=torch.empty((b, n, hq, d), dtype=partial_dtype, device=dev),
+            acc_lse=torch.empty((b, n, hq), dtype=torch.float32, device=dev),
+            part=torch.empty((b, n, hq, d), dtype=partial_dtype, device=dev),
+            part_lse=torch.empty((b, n, hq), dtype=torch.float32, device=dev),
+        )
+
+
+def reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs: RingBuffers):
+    ra.reorder(q, cp_size, kind, stripe_size, out=bufs.q)
+    ra.reorder(k, cp_size, kind, stripe_size, out=bufs.k)
+    ra.reorder(v, cp_size, kind, stripe_size, out=bufs.v)
+    ra.reorder(ids, cp_size, kind, stripe_size, out=bufs.ids)
+    ra.reorder(pos, cp_size, kind, stripe_size, out=bufs.pos)
+
+
+def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, window=(-1, -1),
+               step_hook=None):
+    """Rank ``rank``'s R ring steps on the reordered buffers; the merged result
+    lands in rank's shard of ``bufs.o`` / ``bufs.lse`` (reordered order)."""
+    t = bufs.q.shape[1]
+    n = t // cp_size
+    rows = slice(rank * n, (rank + 1) * n)
+    q_r, id_r, pos_r = bufs.q[:, rows], bufs.ids[:, rows], bufs.pos[:, rows]
+    o_r, lse_r = bufs.o[:, rows], bufs.lse[:, rows]
+    for s in range(cp_size):
+        c = (rank - s) % cp_size
+        cols = slice(c * n, (c + 1) * n)
+        if cp_size == 1:
+            dst, dst_lse = o_r, lse_r
+        elif s == 0:
+            dst, dst_lse = bufs.acc, bufs.acc_lse
+        else:
+            dst, dst_lse = bufs.part, bufs.part_lse
+        if step_hook:
+            step_hook("attn_fwd", rank, s, True)
+        _, _ = ra.attn_fwd(q_r, bufs.k[:, cols], bufs.v[:, cols], id_r, pos_r, bufs.ids[:, cols],
+                           bufs.pos[:, cols], scale=scale, causal=causal, window=window,
+                           out_dtype=dst.dtype, out=dst, lse=dst_lse, workspace=bufs.workspace)
+        if step_hook:
+            step_hook("attn_fwd", rank, s, False)
+        if s == 0:
+            continue
+        last = s == cp_size - 1
+        if step_hook:
+            step_hook("attn_merge", rank, s, True)
+        ra.attn_merge(bufs.acc, bufs.acc_lse, bufs.part, bufs.part_lse,
+                      out=o_r if last else bufs.acc, lse_out=lse_r if last else bufs.acc_lse)
+        if step_hook:
+            step_hook("attn_merge", rank, s, False)
+
+
+def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, scale=None,
+                 causal=True, window=(-1, -1), ranks=None, bufs: RingBuffers | None = None,
+                 partial_dtype=torch.float32, out_dtype=None, step_hook=None):
+    """Ring-decomposed attention forward of self-attention inputs on one GPU.
+
+    q ``[B,T,Hq,D]``, k/v ``[B,T,Hkv,D]``, ids/pos ``int32 [B,T]`` in the
+    original token order.  Returns ``(o, lse)`` in the original order.  With
+    ``ranks`` a subset of ranks, only those shards of the output are computed
+    (the others are left as they were in ``bufs``).
+    """
+    if q.shape[1] != k.shape[1]:
+        raise ValueError("the ring driver runs self-attention (Tq == Tk)")
+    if bufs is None:
+        bufs = RingBuffers.like(q, k, ids, cp_size, partial_dtype, out_dtype)
+    if bufs.workspace is None:
+        b, t = ids.shape
+        n = t // cp_size
+        desc = ra.make_desc(b, n, n, q.shape[2], k.shape[2], q.shape[3],
+                            ra._dtype_code(q.dtype), None, scale, causal, window)
+        bufs.workspace = torch.empty(max(1, ra.workspace_size(desc)), dtype=torch.uint8,
+                                     device=q.device)
+    if step_hook:
+        step_hook("reorder", -1, -1, True)
+    reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs)
+    if step_hook:
+        step_hook("reorder", -1, -1, False)
+    for r in (range(cp_size) if ranks is None else ranks):
+        rank_steps(r, cp_size, bufs, scale=scale, causal=causal, window=window, step_hook=step_hook)
+    if step_hook:
+        step_hook("inverse_reorder", -1, -1, True)
+    o = ra.inverse_reorder(bufs.o, cp_size, kind, stripe_size)
+    lse = ra.inverse_reorder(bufs.lse, cp_size, kind, stripe_size)
+    if step_hook:
+        step_hook("inverse_reorder", -1, -1, False)
+    return o, lse

@@ -1,0 +1,210 @@
+/*
+ * libringattn -- blockwise online-softmax attention forward for AMD MI355X (gfx950).
+ *
+ * Plain C ABI: device pointers and sizes in, status codes out.  No entry point
+ * allocates device memory, synchronises the device, prints, throws or aborts.
+ * Every argument is validated on the host before any HIP call; on a bad
+ * argument the call returns a status, leaves all buffers untouched and records a
+ * message for ra_last_error().  Kernel launches are enqueued on the caller's
+ * stream (a hipStream_t; NULL is the default stream); faults inside a kernel
+ * surface at the caller's next synchronisation.
+ *
+ * Tensor layouts ("THD": batch, tokens, heads, head_dim; head_dim contiguous):
+ *   q  [B, Tq, Hq,  D]    k, v  [B, Tk, Hkv, D]    o  [B, Tq, Hq, D]
+ *   lse [B, Tq, Hq] (fp32)   segment ids / positions [B, T] (int32)
+ * Rows of one batch entry are contiguous; only the batch stride may differ from
+ * the dense value, so sequence shards and ring chunks can be passed as views.
+ *
+ * Sources (web pages; sections named, no line numbers):
+ *   [TUT] TransformerEngine JAX tutorial "JAX: Context-Parallel Attention with
+ *         TransformerEngine": s1 packed THD inputs (segment ids / positions,
+ *         padding id 0), s3 fused attention call (scaling_factor,
+ *         PADDING_CAUSAL_MASK, window_size, THD_THD_THD, vanilla softmax),
+ *         s4 striped load balancing (reorder_causal_load_balancing and its
+ *         inverse, cp_size, seq_dim, stripe_size).
+ *   [CPP] "Implementation: NVIDIA TransformerEngine JAX Cpp Attention":
+ *         I/O contract (outputs: output, softmax_aux); FusedAttnHelper
+ *         backend query.
+ *   [RA]  "Context parallelism and ring attention": "The attention problem",
+ *         "Ring attention", "Online softmax", "Causal attention", "Load balance".
+ */
+#ifndef RINGATTN_H
+#define RINGATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t *ra_stream_t;
+
+typedef enum ra_status {
+  RA_OK = 0,
+  RA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  RA_ERR_SHAPE = 2,       /* a size, stride or window is out of range            */
+  RA_ERR_DTYPE = 3,       /* unknown or unsupported dtype                        */
+  RA_ERR_ALIGN = 4,       /* pointer or stride breaks the alignment rules        */
+  RA_ERR_UNSUPPORTED = 5, /* valid request outside what the kernels implement    */
+  RA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required             */
+  RA_ERR_ALIAS = 7,       /* buffers overlap where they must not                 */
+  RA_ERR_HIP = 8          /* a HIP call or launch failed (text in ra_last_error) */
+} ra_status;
+
+typedef enum ra_dtype { RA_BF16 = 0, RA_F32 = 1 } ra_dtype;
+
+typedef enum ra_reorder_kind {
+  RA_REORDER_DUAL_CHUNK = 0, /* 2R stripes; rank r holds stripe r, then stripe 2R-1-r ([RA] Load balance) */
+  RA_REORDER_STRIPED = 1     /* stripes of stripe_size tokens; stripe j goes to rank j mod R ([TUT] s4)  */
+} ra_reorder_kind;
+
+/* Tile classes written by ra_classify_tiles ([RA] "Causal attention"). */
+enum { RA_TILE_SKIP = 0, RA_TILE_PARTIAL = 1, RA_TILE_FULL = 2 };
+
+/*
+ * Attention problem description (the static configuration of one forward).
+ *
+ * Masking ([TUT] s1, s3): query i and key j of batch row b are visible to each
+ * other iff  ids_q[i] != 0 && ids_q[i] == ids_kv[j]            (same segment, not padding)
+ *        && (!causal || pos_kv[j] <= pos_q[i])                  (positions, never array indices)
+ *        && (window_left  < 0 || pos_q[i] - pos_kv[j] <= window_left)
+ *        && (window_right < 0 || pos_kv[j] - pos_q[i] <= window_right).
+ * Query head h reads K/V head h / (Hq / Hkv).
+ * Batch strides are in elements of the tensor they describe; 0 selects the dense
+ * value (Tq*Hq*D for q and o, Tk*Hkv*D for k and v, Tq*Hq for lse, Tq / Tk for
+ * the int32 metadata).
+ */
+typedef struct ra_attn_desc {
+  int32_t batch;          /* B  >= 0                                           */
+  int32_t q_len;          /* Tq >= 0                                           */
+  int32_t kv_len;         /* Tk >= 0                                           */
+  int32_t num_q_heads;    /* Hq >= 1                                           */
+  int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0                           */
+  int32_t head_dim;       /* D: 64 or 128                                      */
+  int32_t qkv_dtype;      /* ra_dtype of q, k and v                            */
+  int32_t out_dtype;      /* ra_dtype of o                                     */
+  float scale;            /* score scale, finite and > 0; head_dim^-1/2 in [TUT] s3 */
+  int32_t causal;         /* 0 or 1                                            */
+  int32_t window_left;    /* -1 (unbounded) or >= 0                            */
+  int32_t window_right;   /* -1 (unbounded) or >= 0                            */
+  int64_t q_batch_stride;
+  int64_t kv_batch_stride;
+  int64_t o_batch_stride;
+  int64_t lse_batch_stride;
+  int64_t q_meta_batch_stride;
+  int64_t kv_meta_batch_stride;
+} ra_attn_desc;
+
+/* Library identification and diagnostics.  The returned strings are static
+ * (ra_last_error: thread-local, valid until the thread's next failing call). */
+const char *ra_version(void);
+const char *ra_status_string(ra_status status);
+const char *ra_last_error(void);
+
+/*
+ * Host-only support query (the role of FusedAttnHelper's backend query in
+ * [CPP]): RA_OK if ra_attn_fwd implements this description, otherwise the
+ * status it would return.  Supported: bf16 q/k/v (MFMA path) or fp32 q/k/v,
+ * D in {64, 128}, bf16 or fp32 output, any Hq/Hkv group size, any lengths up to
+ * 2^22 key tokens per call.  Makes no HIP call.
+ */
+ra_status ra_check_support(const ra_attn_desc *desc);
+
+/* Token tile sizes (query tile, key tile) that the forward and ra_classify_tiles
+ * use for this description.  Host only. */
+ra_status ra_tile_shape(const ra_attn_desc *desc, int32_t *bm_tokens, int32_t *bn_tokens);
+
+/* Bytes of device workspace that ra_attn_fwd and ra_classify_tiles need for
+ * this description (tile summaries and per-query-tile work lists).  Host only. */
+ra_status ra_attn_fwd_workspace_size(const ra_attn_desc *desc, size_t *bytes);
+
+/*
+ * Exact masked softmax attention forward ([RA] "The attention problem";
+ * [TUT] s3 fused_attn with PADDING_CAUSAL_MASK, window_size, no bias, no
+ * dropout, vanilla softmax), evaluated blockwise over key tiles with the
+ * online-softmax running max / sum / weighted sum ([RA] "Online softmax").
+ * Key tiles with no visible pair are skipped, tiles that are all visible run
+ * unmasked, and only the rest are masked ([RA] "Causal attention").
+ *
+ * Outputs ([CPP] I/O contract: output and softmax_aux):
+ *   o   [B,Tq,Hq,D] out_dtype:  softmax(scale * q k^T + M) v
+ *   lse [B,Tq,Hq]   fp32:       natural-log log-sum-exp of the visible scaled
+ *                               scores; a query with no visible key gets
+ *                               o = 0 and lse = -inf.
+ * Both are fully overwritten.  q, k, v, o: 16-byte aligned, batch strides a
+ * multiple of 16 bytes; metadata and lse 4-byte aligned.  o must not overlap
+ * q, k or v.  workspace: device memory of at least
+ * ra_attn_fwd_workspace_size() bytes, 256-byte aligned, owned by the caller,
+ * overwritten; calls that share a workspace must be ordered on one stream.
+ */
+ra_status ra_attn_fwd(const ra_attn_desc *desc, const void *q, const void *k, const void *v,
+                      const int32_t *q_segment_ids, const int32_t *q_segment_pos,
+                      const int32_t *kv_segment_ids, const int32_t *kv_segment_pos, void *o,
+                      float *lse, void *workspace, size_t workspace_bytes, ra_stream_t stream);
+
+/*
+ * The exact tile classes of the mask at the tile shape of ra_tile_shape()
+ * ([RA] "Causal attention": skip / full / partial), and the number of visible
+ * (query, key) pairs of every batch row.  classes: int8 [B, ceil(Tq/bm),
+ * ceil(Tk/bn)] with RA_TILE_* values (a tile's class is decided over its
+ * in-range pairs only); visible_pairs: int64 [B].  Either output may be NULL.
+ * Only the metadata fields of desc matter (dtypes and head_dim select the tile
+ * shape).  Same workspace rules as ra_attn_fwd.
+ */
+ra_status ra_classify_tiles(const ra_attn_desc *desc, const int32_t *q_segment_ids,
+                            const int32_t *q_segment_pos, const int32_t *kv_segment_ids,
+                            const int32_t *kv_segment_pos, int8_t *classes,
+                            int64_t *visible_pairs, void *workspace, size_t workspace_bytes,
+                            ra_stream_t stream);
+
+/*
+ * Merge of two partial results over disjoint key sets ([RA] "Online softmax",
+ * written over (output, log-sum-exp) pairs):
+ *   lse = log(exp(lse_a) + exp(lse_b));  o = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b.
+ * A row whose two inputs are both -inf gets o = 0, lse = -inf; a row with one
+ * -inf input gets the other input unchanged (converted to out_dtype).  Never NaN
+ * for finite inputs.  o_out may be exactly o_a or o_b (same dtype and strides;
+ * lse likewise) for in-place accumulation; any other overlap is RA_ERR_ALIAS.
+ * o_*: 16-byte aligned (8 for bf16 with D=64 strides), batch strides in
+ * elements (0 = dense seq_len*num_heads*head_dim; lse: seq_len*num_heads).
+ */
+typedef struct ra_merge_desc {
+  int32_t batch, seq_len, num_heads, head_dim; /* head_dim: 64 or 128        */
+  int32_t a_dtype, b_dtype, out_dtype;         /* ra_dtype of o_a, o_b, o_out */
+  int64_t o_a_batch_stride, o_b_batch_stride, o_out_batch_stride;
+  int64_t lse_a_batch_stride, lse_b_batch_stride, lse_out_batch_stride;
+} ra_merge_desc;
+
+ra_status ra_attn_merge(const ra_merge_desc *desc, const void *o_a, const float *lse_a,
+                        const void *o_b, const float *lse_b, void *o_out, float *lse_out,
+                        ra_stream_t stream);
+
+/*
+ * Causal load-balancing permutation of the sequence axis of a dense
+ * [batch, seq_len, row_bytes] tensor (any of q, k, v, segment ids/positions, o,
+ * lse) -- [TUT] s4 reorder_causal_load_balancing with seq_dim 1:
+ *   ra_reorder:          dst[b, p] = src[b, map(p)]
+ *   ra_inverse_reorder:  dst[b, map(p)] = src[b, p]
+ * where map is RA_REORDER_DUAL_CHUNK (needs seq_len % (2*cp_size) == 0) or
+ * RA_REORDER_STRIPED (needs seq_len % (cp_size*stripe_size) == 0).  After a
+ * reorder, rank r's shard is the contiguous token range [r*T/R, (r+1)*T/R).
+ * src and dst must not overlap.  Rows are copied as bytes (row_bytes >= 1).
+ */
+ra_status ra_reorder(const void *src, void *dst, int32_t batch, int32_t seq_len, int64_t row_bytes,
+                     int32_t cp_size, int32_t kind, int32_t stripe_size, ra_stream_t stream);
+ra_status ra_inverse_reorder(const void *src, void *dst, int32_t batch, int32_t seq_len,
+                             int64_t row_bytes, int32_t cp_size, int32_t kind, int32_t stripe_size,
+                             ra_stream_t stream);
+
+/* Host-side copy of the same map (host_map[p] = map(p), or its inverse when
+ * inverse != 0), computed by the function the kernels use.  host_map: int32 [seq_len]. */
+ra_status ra_reorder_index(int32_t seq_len, int32_t cp_size, int32_t kind, int32_t stripe_size,
+                           int32_t inverse, int32_t *host_map);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGATTN_H */

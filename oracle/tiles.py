@@ -29,16 +29,17 @@ def classify_tiles_exact(qid, qpos, kid, kpos, bm, bn, causal=True, window=(-1, 
     nqt = -(-tq // bm)
     nkt = -(-tk // bn)
     out = np.zeros((b_, nqt, nkt), np.int8)
+    pad = nkt * bn - tk
     for b in range(b_):
         for qt in range(nqt):
             i0, i1 = qt * bm, min((qt + 1) * bm, tq)
             vis = visible(qid[b, i0:i1], qpos[b, i0:i1], kid[b], kpos[b], causal, window)
-            for kt in range(nkt):
-                blk = vis[:, kt * bn:min((kt + 1) * bn, tk)]
-                if blk.all():
-                    out[b, qt, kt] = FULL
-                elif blk.any():
-                    out[b, qt, kt] = PARTIAL
+            # out-of-range key slots count as invisible for "any" and visible for "all"
+            any_v = np.pad(vis, ((0, 0), (0, pad)), constant_values=False)
+            all_v = np.pad(vis, ((0, 0), (0, pad)), constant_values=True)
+            some = any_v.reshape(i1 - i0, nkt, bn).any(axis=(0, 2))
+            every = all_v.reshape(i1 - i0, nkt, bn).all(axis=(0, 2))
+            out[b, qt] = np.where(every, FULL, np.where(some, PARTIAL, SKIP))
     return out
 
 

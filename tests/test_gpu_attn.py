@@ -1,0 +1,291 @@
+"""GPU parity of the attention forward against the fp64 oracle.
+
+Every case feeds the same seeded host (or torch-RNG device) tensors to the
+HIP path through the C ABI and to the oracle, and holds the result to the bar
+in ``_parity.compare``.  Small cases span several tiles with ragged tails,
+all GQA group sizes (every workgroup shape of the bf16 kernel), both head
+dims, both input dtypes, masked and unmasked, windows at their edges,
+cross-attention with unrelated layouts, and empty inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_online_softmax_fwd_amd as bosf
+import oracle
+from _parity import compare, to64
+from workloads import get, packed_metadata, random_layout, random_qkv
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bosf.load_library()
+
+
+def _dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+# (B, Tq, Tk, Hq, Hkv, D, dtype, causal, window, self_attention)
+SMALL = [
+    (1, 1, 1, 1, 1, 64, "bf16", True, (-1, -1), True),
+    (1, 33, 33, 8, 8, 128, "bf16", True, (-1, -1), True),
+    (2, 257, 257, 16, 2, 128, "bf16", True, (-1, -1), True),
+    (2, 300, 300, 16, 2, 128, "bf16", True, (40, 0), True),
+    (1, 517, 517, 64, 8, 128, "bf16", True, (100, 0), True),
+    (2, 200, 200, 32, 2, 128, "bf16", True, (0, 0), True),
+    (2, 190, 190, 4, 1, 64, "bf16", False, (-1, -1), True),
+    (1, 250, 250, 8, 4, 64, "bf16", False, (17, 9), True),
+    (2, 129, 129, 3, 1, 128, "bf16", True, (-1, 5), True),
+    (1, 300, 300, 12, 1, 128, "bf16", True, (-1, -1), True),
+    (2, 161, 161, 6, 3, 64, "bf16", True, (30, 30), True),
+    (1, 96, 96, 1, 1, 128, "bf16", True, (-1, -1), True),
+    (2, 300, 517, 16, 2, 128, "bf16", True, (-1, -1), False),
+    (1, 517, 300, 8, 2, 64, "bf16", False, (50, 50), False),
+    (2, 64, 640, 16, 1, 128, "bf16", True, (200, 0), False),
+    (1, 256, 256, 4, 4, 64, "f32", True, (-1, -1), True),
+    (2, 111, 111, 4, 2, 128, "f32", True, (20, 0), True),
+    (1, 99, 140, 6, 1, 64, "f32", False, (-1, 3), False),
+    (2, 70, 70, 2, 2, 128, "f32", True, (0, 0), True),
+]
+
+
+def _case_id(c):
+    b, tq, tk, hq, hkv, d, dt, causal, w, self_ = c
+    return f"B{b}_Tq{tq}_Tk{tk}_H{hq}-{hkv}_D{d}_{dt}_{'c' if causal else 'nc'}_w{w[0]}.{w[1]}_{'self' if self_ else 'cross'}"
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_case_id(c) for c in SMALL])
+@pytest.mark.parametrize("out", ["same", "f32"])
+def test_small_random_layouts(case, out):
+    b, tq, tk, hq, hkv, d, dt, causal, window, self_ = case
+    rng = np.random.default_rng(tq * 7 + tk + hq)
+    q_ids, q_pos = random_layout(rng, b, tq, max_segments=4, pad_prob=0.25, pos_offset_max=3)
+    if self_:
+        kv_ids, kv_pos = q_ids, q_pos
+    else:
+        kv_ids, kv_pos = random_layout(rng, b, tk, max_segments=3, pad_prob=0.25, pos_offset_max=40)
+    q, k, v = random_qkv(b, tq, tk, hq, hkv, d, dt, seed=tq + tk)
+    out_dtype = torch.float32 if out == "f32" else None
+    o, lse = bosf.attn_fwd(*_dev(q, k, v, q_ids, q_pos, kv_ids, kv_pos), causal=causal,
+                           window=window, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q, k, v, q_ids, q_pos, kv_ids, kv_pos, causal=causal, window=window)
+    compare(o, lse, ro, rl, dt, _case_id(case))
+
+
+def test_packed_layout_scale_and_window_edges():
+    """Packed slots with padding; a non-default scale; window exactly at 31/32/33."""
+    ids, pos = packed_metadata(2, 512, 2, 200)
+    q, k, v = random_qkv(2, 512, 512, 16, 2, 128, "bf16", seed=3)
+    for window in [(31, 0), (32, 0), (33, 0)]:
+        o, lse = bosf.attn_fwd(*_dev(q, k, v, ids, pos, ids, pos), scale=0.05, window=window)
+        ro, rl = oracle.attention(q, k, v, ids, pos, ids, pos, scale=0.05, window=window)
+        compare(o, lse, ro, rl, "bf16", f"window {window}")
+
+
+def test_empty_inputs():
+    q, k, v = random_qkv(2, 40, 0, 8, 2, 128, "bf16", seed=1)
+    ids = torch.ones(2, 40, dtype=torch.int32)
+    pos = torch.arange(40, dtype=torch.int32).repeat(2, 1)
+    kid = torch.ones(2, 0, dtype=torch.int32)
+    o, lse = bosf.attn_fwd(*_dev(q, k, v, ids, pos, kid, kid))
+    assert (o == 0).all() and torch.isneginf(lse).all()
+    # no queries / no batch: nothing to do, must not fail
+    q0 = torch.zeros(2, 0, 8, 128, dtype=torch.bfloat16)
+    e = torch.zeros(2, 0, dtype=torch.int32)
+    k1, v1 = random_qkv(2, 8, 8, 8, 2, 128, "bf16")[1:]
+    i1 = torch.ones(2, 8, dtype=torch.int32)
+    o0, l0 = bosf.attn_fwd(*_dev(q0, k1, v1, e, e, i1, i1))
+    assert o0.shape == (2, 0, 8, 128)
+    qb = torch.zeros(0, 5, 8, 128, dtype=torch.bfloat16)
+    eb = torch.zeros(0, 5, dtype=torch.int32)
+    ob, lb = bosf.attn_fwd(*_dev(qb, qb[:, :, :2], qb[:, :, :2], eb, eb, eb, eb))
+    assert ob.numel() == 0
+
+
+def test_all_padding_queries():
+    ids = torch.zeros(1, 100, dtype=torch.int32)
+    pos = torch.arange(100, dtype=torch.int32)[None]
+    q, k, v = random_qkv(1, 100, 100, 8, 1, 128, "bf16", seed=2)
+    o, lse = bosf.attn_fwd(*_dev(q, k, v, ids, pos, ids, pos))
+    assert (o == 0).all() and torch.isneginf(lse).all()
+
+
+def test_batch_strided_views():
+    """Q/K/V/O/LSE and metadata as views into longer sequences (ring shards)."""
+    ids, pos = packed_metadata(2, 1024, 2, 400)
+    q, k, v = random_qkv(2, 1024, 1024, 16, 2, 128, "bf16", seed=5)
+    qd, kd, vd, idd, posd = _dev(q, k, v, ids, pos)
+    o_full = torch.full((2, 1024, 16, 128), 7.0, dtype=torch.float32, device=DEV)
+    l_full = torch.full((2, 1024, 16), 7.0, dtype=torch.float32, device=DEV)
+    qs, ks = slice(256, 512), slice(512, 1024)
+    o, lse = bosf.attn_fwd(qd[:, qs], kd[:, ks], vd[:, ks], idd[:, qs], posd[:, qs], idd[:, ks],
+                           posd[:, ks], causal=False, window=(300, 300), out_dtype=torch.float32,
+                           out=o_full[:, qs], lse=l_full[:, qs])
+    ro, rl = oracle.attention(q[:, qs], k[:, ks], v[:, ks], ids[:, qs], pos[:, qs], ids[:, ks],
+                              pos[:, ks], causal=False, window=(300, 300))
+    compare(o_full[:, qs], l_full[:, qs], ro, rl, "bf16", "views")
+    # untouched outside the view
+    assert (o_full[:, :256] == 7).all() and (o_full[:, 512:] == 7).all()
+    assert (l_full[:, :256] == 7).all() and (l_full[:, 512:] == 7).all()
+
+
+def test_deterministic():
+    ids, pos = packed_metadata(2, 2048, 2, 900)
+    q, k, v = _dev(*random_qkv(2, 2048, 2048, 16, 2, 128, "bf16", seed=9))
+    idd, posd = _dev(ids, pos)
+    o1, l1 = bosf.attn_fwd(q, k, v, idd, posd, idd, posd, window=(500, 0))
+    o2, l2 = bosf.attn_fwd(q, k, v, idd, posd, idd, posd, window=(500, 0))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# --------------------------------------------------------------------------- workloads 1 and 2
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_workload_full(cfg):
+    w = get(cfg)
+    ids, pos = packed_metadata(w.batch, w.seq_len, w.slots, w.valid_per_slot)
+    q, k, v = random_qkv(w.batch, w.seq_len, w.seq_len, w.num_q_heads, w.num_kv_heads,
+                         w.head_dim, w.dtype, seed=w.seed)
+    o, lse = bosf.attn_fwd(*_dev(q, k, v, ids, pos, ids, pos), causal=w.causal, window=w.window)
+    ro, rl = oracle.attention(q, k, v, ids, pos, ids, pos, causal=w.causal, window=w.window)
+    e = compare(o, lse, ro, rl, w.dtype, w.name)
+    print(f"{w.name}: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
+
+
+def test_workload3_ring_emulation():
+    """Workload 3: dual-chunk reorder, 4 shards x 4 ring steps with merges,
+    inverse reorder -- against one unsplit oracle attention."""
+    w = get(3)
+    ids, pos = packed_metadata(w.batch, w.seq_len, w.slots, w.valid_per_slot)
+    q, k, v = random_qkv(w.batch, w.seq_len, w.seq_len, w.num_q_heads, w.num_kv_heads,
+                         w.head_dim, w.dtype, seed=w.seed)
+    o, lse = bosf.ring_forward(*_dev(q, k, v, ids, pos), w.cp_size, w.reorder, w.stripe,
+                               causal=w.causal, window=w.window)
+    ro, rl = oracle.attention(q, k, v, ids, pos, ids, pos, causal=w.causal, window=w.window)
+    e = compare(o, lse, ro, rl, "bf16", w.name)
+    print(f"{w.name}: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
+
+
+@pytest.mark.parametrize("kind,stripe,window,partial", [
+    ("striped", 1, (-1, -1), torch.float32), ("dual_chunk", 1, (700, 0), torch.bfloat16),
+    ("striped", 64, (300, 0), torch.float32)])
+def test_ring_variants(kind, stripe, window, partial):
+    ids, pos = packed_metadata(2, 2048, 4, 400)
+    q, k, v = random_qkv(2, 2048, 2048, 16, 2, 128, "bf16", seed=12)
+    o, lse = bosf.ring_forward(*_dev(q, k, v, ids, pos), 4, kind, stripe, window=window,
+                               partial_dtype=partial)
+    ro, rl = oracle.attention(q, k, v, ids, pos, ids, pos, window=window)
+    compare(o, lse, ro, rl, "bf16", f"ring {kind} {stripe}")
+
+
+# --------------------------------------------------------------------------- workloads 4 and 5
+
+def _sample_rows(w, rng, extra_positions, n_random=64):
+    rows = set()
+    for b in range(w.batch):
+        for s in range(w.slots):
+            base = s * w.slot_len
+            for p in extra_positions:
+                if 0 <= p < w.slot_len:
+                    rows.add((b, base + p))
+    for _ in range(n_random):
+        rows.add((int(rng.integers(w.batch)), int(rng.integers(w.seq_len))))
+    return sorted(rows)
+
+
+def _device_inputs(w, zero_q=False, uniform_v=None):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(w.seed)
+    dt = torch.bfloat16
+    q = torch.randn((w.batch, w.seq_len, w.num_q_heads, w.head_dim), generator=g, device=DEV).to(dt)
+    k = torch.randn((w.batch, w.seq_len, w.num_kv_heads, w.head_dim), generator=g, device=DEV).to(dt)
+    v = torch.randn((w.batch, w.seq_len, w.num_kv_heads, w.head_dim), generator=g, device=DEV).to(dt)
+    if zero_q:
+        q.zero_()
+    if uniform_v is not None:
+        v.copy_(uniform_v.to(DEV, dt)[None, None].expand_as(v))
+    ids, pos = packed_metadata(w.batch, w.seq_len, w.slots, w.valid_per_slot)
+    return q, k, v, ids.to(DEV), pos.to(DEV)
+
+
+def _run_workload(w, q, k, v, ids, pos):
+    if w.cp_size > 1:
+        return bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe,
+                                 causal=w.causal, window=w.window)
+    return bosf.attn_fwd(q, k, v, ids, pos, ids, pos, causal=w.causal, window=w.window)
+
+
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_workload_full_size_sampled(cfg):
+    """Full-size run in the configuration the benchmark times; sampled rows
+    (segment starts, window edges, padding, shard boundaries, random) against
+    the oracle, every head."""
+    w = get(cfg)
+    q, k, v, ids, pos = _device_inputs(w)
+    o, lse = _run_workload(w, q, k, v, ids, pos)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg)
+    left = w.window[0]
+    edges = [0, 1, 2, 31, 32, 63, 64, left - 1, left, left + 1, left + 2,
+             w.valid_per_slot - 1, w.valid_per_slot, w.slot_len - 1]
+    rows = _sample_rows(w, rng, edges)
+    if w.cp_size > 1:  # rows on both sides of every shard boundary after reordering
+        m = oracle.reorder_map(w.seq_len, w.cp_size, w.reorder, w.stripe)
+        n = w.seq_len // w.cp_size
+        for r in range(1, w.cp_size):
+            for p in (r * n - 1, r * n, r * n + n // 2 - 1, r * n + n // 2):
+                rows.append((0, int(m[p])))
+    kc, vc = k.cpu(), v.cpu()
+    ro, rl = oracle.attention_rows(q, kc, vc, ids.cpu(), pos.cpu(), ids.cpu(), pos.cpu(), rows,
+                                   causal=w.causal, window=w.window)
+    bi = torch.tensor([r[0] for r in rows])
+    ti = torch.tensor([r[1] for r in rows])
+    e = compare(o[bi, ti], lse[bi, ti], ro, rl, "bf16", w.name)
+    print(f"{w.name}: {len(rows)} rows x {w.num_q_heads} heads: max|dO|={e[0]:.2e} "
+          f"max|dLSE|={e[1]:.2e}")
+
+
+def _closed_form_counts(w, pos_row, ids_row):
+    """Visible keys of each query on the packed layouts: min(pos+1, left+1)."""
+    p = pos_row.to(torch.float64)
+    n = p + 1 if w.window[0] < 0 else torch.clamp(p + 1, max=w.window[0] + 1)
+    return torch.where(ids_row != 0, n, torch.zeros_like(n))
+
+
+@pytest.mark.parametrize("cfg", [2, 4, 5])
+def test_workload_zero_queries_every_row(cfg):
+    """Q = 0: every row's LSE is ln(visible keys), known in closed form for
+    every row at full size; padding rows are -inf."""
+    w = get(cfg)
+    q, k, v, ids, pos = _device_inputs(w, zero_q=True)
+    o, lse = _run_workload(w, q, k, v, ids, pos)
+    n = _closed_form_counts(w, pos, ids)                 # [B, T]
+    ref = torch.where(n > 0, torch.log(n), torch.full_like(n, -np.inf))
+    got = lse.to(torch.float64)
+    live = n > 0
+    assert torch.equal(torch.isneginf(got), ~live[:, :, None].expand_as(got))
+    err = (got - ref[:, :, None])[live[:, :, None].expand_as(got)].abs().max().item()
+    assert err <= 1e-5, err
+    assert (o[~live] == 0).all()
+
+
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_workload_uniform_v_every_row(cfg):
+    """v[b, j, g, :] = c_g: every live row's output is c_g of its head's group."""
+    w = get(cfg)
+    c = torch.randn((w.num_kv_heads, w.head_dim), generator=torch.Generator().manual_seed(1))
+    c = c.to(torch.bfloat16)
+    q, k, v, ids, pos = _device_inputs(w, uniform_v=c)
+    o, lse = _run_workload(w, q, k, v, ids, pos)
+    ref = c.to(DEV, torch.float32).repeat_interleave(w.group, dim=0)   # [Hq, D]
+    live = ids != 0
+    err = (o[live].float() - ref[None]).abs().max().item()
+    assert err <= 2e-2, err
+    assert torch.isneginf(lse[~live]).all() and (o[~live] == 0).all()
