@@ -1,0 +1,240 @@
+"""Benchmark: attention forward TFLOP/s on visible (query, key) pairs, one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM.  For the default workload (one device's share of the
+TransformerEngine tutorial's long-context case, run as a 4-shard ring) that is:
+causal load-balancing reorder of Q, K, V, segment ids and positions; for each
+of the 4 shards, 4 ring steps of attn_fwd (tile classification + attention)
+with 3 merges; inverse reorder of O and LSE.  All four shards are computed, so
+a step is the complete forward of B=2 x 65536 tokens; FLOPs count only visible
+pairs (4 * head_dim * Hq flops per pair).
+
+Prints one JSON line.  ``roofline`` is measured live with HIP events around
+every attn_fwd call (on the stream the library launches on); ``cpu_baseline``
+times the fp64 oracle on a bounded row sample of the same inputs.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import blockwise_online_softmax_fwd_amd as bosf  # noqa: E402
+from workloads import get, packed_metadata  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s (visible pairs) + % of bf16 MFMA peak, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_inputs(w, dev):
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    shp_q = (w.batch, w.seq_len, w.num_q_heads, w.head_dim)
+    shp_kv = (w.batch, w.seq_len, w.num_kv_heads, w.head_dim)
+    q = torch.randn(shp_q, generator=g, device=dev).to(dt)
+    k = torch.randn(shp_kv, generator=g, device=dev).to(dt)
+    v = torch.randn(shp_kv, generator=g, device=dev).to(dt)
+    ids, pos = packed_metadata(w.batch, w.seq_len, w.slots, w.valid_per_slot)
+    return q, k, v, ids.to(dev), pos.to(dev)
+
+
+class EventLog:
+    """Event pairs around library calls, grouped by call name."""
+
+    def __init__(self):
+        self.open = {}
+        self.done = {}
+        self.enabled = False
+
+    def hook(self, name, rank, step, begin):
+        if not self.enabled:
+            return
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        if begin:
+            self.open[name] = ev
+        else:
+            self.done.setdefault(name, []).append((self.open.pop(name), ev))
+
+    def ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.done.get(name, [])]
+
+
+def cpu_baseline(w, q, k, v, ids, pos, budget_s):
+    """Oracle (fp64, host) on a bounded random row sample of the same inputs."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    kc, vc, idc, posc = k.cpu(), v.cpu(), ids.cpu(), pos.cpu()
+    rng = np.random.default_rng(0)
+    valid = np.argwhere(idc.numpy() != 0)
+    order = rng.permutation(len(valid))
+    rows, pairs, t0 = [], 0, time.perf_counter()
+    for j in order:
+        b, i = int(valid[j][0]), int(valid[j][1])
+        oracle.attention_rows(q, kc, vc, idc, posc, idc, posc, [(b, i)], causal=w.causal,
+                              window=w.window)
+        n = int(oracle.visible(idc[b, i:i + 1], posc[b, i:i + 1], idc[b], posc[b], w.causal,
+                               w.window).sum())
+        rows.append((b, i))
+        pairs += n
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.head_dim * w.num_q_heads * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} random valid query rows x all {w.num_q_heads} heads "
+                      f"({pairs} visible pairs, {flops / 1e9:.1f} GFLOP fp64) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=5, help="workload number (1-5)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the ring is "
+              "emulated shard by shard on a single device", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = get(args.workload)
+    bosf.load_library()
+    log(f"workload {w.cfg} {w.name}: {w.describe()}")
+    q, k, v, ids, pos = make_inputs(w, dev)
+
+    # Work of one step: visible pairs of the unsplit problem, counted by the
+    # library's own classification pass (the ring decomposition covers every
+    # visible pair exactly once).
+    _, pairs = bosf.classify_tiles(ids, pos, ids, pos, num_q_heads=w.num_q_heads,
+                                   num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                                   dtype=q.dtype, causal=w.causal, window=w.window)
+    visible = int(pairs.sum().item())
+    flops = 4.0 * w.head_dim * w.num_q_heads * visible
+    log(f"visible pairs {visible}, {flops / 1e12:.3f} TFLOP per step")
+
+    ev = EventLog()
+    if w.cp_size > 1:
+        bufs = bosf.RingBuffers.like(q, k, ids, w.cp_size)
+
+        def step():
+            bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe, causal=w.causal,
+                              window=w.window, bufs=bufs, step_hook=ev.hook)
+    else:
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        desc = bosf.make_desc(w.batch, w.seq_len, w.seq_len, w.num_q_heads, w.num_kv_heads,
+                              w.head_dim, 0 if w.dtype == "bf16" else 1)
+        wsp = torch.empty(bosf.workspace_size(desc), dtype=torch.uint8, device=dev)
+
+        def step():
+            ev.hook("attn_fwd", 0, 0, True)
+            bosf.attn_fwd(q, k, v, ids, pos, ids, pos, causal=w.causal, window=w.window, out=o,
+                          lse=lse, workspace=wsp)
+            ev.hook("attn_fwd", 0, 0, False)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev.enabled = True
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ev.enabled = False
+    ms_step = (t1 - t0) * 1000.0 / args.steps
+    value = flops / (ms_step / 1000.0) / 1e12
+    log(f"{ms_step:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    attn_ms = ev.ms("attn_fwd")
+    n_attn = len(attn_ms)
+    attn_total_ms = float(sum(attn_ms))
+    per_launch_flops = flops * args.steps / n_attn
+    achieved = flops * args.steps / (attn_total_ms / 1000.0) / 1e12
+    detail = {"attn_fwd_launches_per_step": n_attn // args.steps,
+              "attn_fwd_ms_per_step": attn_total_ms / args.steps,
+              "attn_fwd_avg_ms_per_launch": attn_total_ms / n_attn,
+              "visible_pairs_per_step": visible,
+              "pct_of_bf16_peak_whole_step": 100.0 * value / PEAK_BF16_TFLOPS}
+    if w.cp_size > 1:
+        b, t, hq, d = q.shape
+        n = t // w.cp_size
+        rows = b * n * hq
+        merges = ev.ms("attn_merge")
+        # per shard: 2 merges fp32+fp32->fp32, 1 merge fp32+fp32->bf16 (bytes: 2 reads + write + lse)
+        merge_bytes = w.cp_size * rows * ((2 * (3 * 4 * d + 12)) + (2 * 4 * d + 2 * d + 12))
+        reorder_ms = sum(ev.ms("reorder")) / args.steps
+        inv_ms = sum(ev.ms("inverse_reorder")) / args.steps
+        fwd_bytes = 2 * (q.numel() * 2 + 2 * k.numel() * 2 + 2 * ids.numel() * 4)
+        inv_bytes = 2 * (q.numel() * 2 + b * t * hq * 4)
+        detail.update({
+            "attn_merge_ms_per_step": sum(merges) / args.steps,
+            "attn_merge_GBs": merge_bytes / (sum(merges) / args.steps / 1000.0) / 1e9,
+            "reorder_ms_per_step": reorder_ms,
+            "reorder_GBs": fwd_bytes / (reorder_ms / 1000.0) / 1e9,
+            "inverse_reorder_ms_per_step": inv_ms,
+            "inverse_reorder_GBs": inv_bytes / (inv_ms / 1000.0) / 1e9,
+        })
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "kernel": "attn_fwd (tile classification + bf16 MFMA forward)",
+                "per_launch_flops": per_launch_flops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a host row sample")
+        cpu = cpu_baseline(w, q, k, v, ids, pos, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "config": {"workload": f"{w.name}: {w.describe()}", "batch": w.batch,
+                   "seq_len": w.seq_len, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "window": list(w.window), "cp_shards": w.cp_size, "reorder": w.reorder},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

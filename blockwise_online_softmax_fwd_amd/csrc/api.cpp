@@ -126,8 +126,14 @@ ra_status check_meta(const ra_attn_desc *d, const Resolved &r, const int32_t *qi
   return RA_OK;
 }
 
-ra_status check_workspace(const Resolved &r, int32_t batch, const void *ws, size_t ws_bytes) {
-  const ra::WorkspaceLayout L = ra::workspace_layout(batch, r.nqt, r.nkt);
+ra::WorkspaceLayout layout_of(const ra_attn_desc *d, const Resolved &r) {
+  const int32_t pd = d->qkv_dtype == RA_BF16 ? d->head_dim : 0;
+  return ra::workspace_layout(d->batch, r.nqt, r.nkt, d->num_kv_heads, pd);
+}
+
+ra_status check_workspace(const ra_attn_desc *d, const Resolved &r, const void *ws,
+                          size_t ws_bytes) {
+  const ra::WorkspaceLayout L = layout_of(d, r);
   if (L.total > 0 && !ws) return fail(RA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
   if (ws_bytes < L.total)
     return fail(RA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, L.total);
@@ -135,8 +141,7 @@ ra_status check_workspace(const Resolved &r, int32_t batch, const void *ws, size
   return RA_OK;
 }
 
-ra::Schedule carve(void *ws, const Resolved &r, int32_t batch) {
-  const ra::WorkspaceLayout L = ra::workspace_layout(batch, r.nqt, r.nkt);
+ra::Schedule carve(void *ws, const ra::WorkspaceLayout &L) {
   char *base = (char *)ws;
   ra::Schedule s;
   s.qsum = (ra::TileSum *)(base + L.qsum);
@@ -211,7 +216,7 @@ ra_status ra_attn_fwd_workspace_size(const ra_attn_desc *desc, size_t *bytes) {
   const ra_status st = check_desc(desc, &r);
   if (st != RA_OK) return st;
   if (!bytes) return fail(RA_ERR_NULL, "bytes is NULL");
-  *bytes = ra::workspace_layout(desc->batch, r.nqt, r.nkt).total;
+  *bytes = layout_of(desc, r).total;
   return RA_OK;
 }
 
@@ -245,11 +250,12 @@ ra_status ra_attn_fwd(const ra_attn_desc *d, const void *q, const void *k, const
       overlaps(lse, l_span, v, kv_span))
     return fail(RA_ERR_ALIAS, "o / lse overlap an input or each other");
   if (!has_q) return RA_OK;
-  st = check_workspace(r, d->batch, workspace, workspace_bytes);
+  st = check_workspace(d, r, workspace, workspace_bytes);
   if (st != RA_OK) return st;
 
   hipStream_t s = (hipStream_t)stream;
-  const ra::Schedule sch = carve(workspace, r, d->batch);
+  const ra::WorkspaceLayout L = layout_of(d, r);
+  const ra::Schedule sch = carve(workspace, L);
   st = run_schedule(d, r, sch, qid, qpos, kid, kpos, nullptr, s);
   if (st != RA_OK) return st;
 
@@ -282,6 +288,27 @@ ra_status ra_attn_fwd(const ra_attn_desc *d, const void *q, const void *k, const
   p.scale = d->scale;
   p.scale_log2 = d->scale * 1.4426950408889634f;
   p.mask = mask_of(d);
+  p.kpack = (char *)workspace + L.kpack;
+  p.vpack = (char *)workspace + L.vpack;
+  p.mpack = (const int32_t *)((char *)workspace + L.mpack);
+  if (d->qkv_dtype == RA_BF16 && d->kv_len > 0) {
+    ra::PackParams pk;
+    pk.k = k;
+    pk.v = v;
+    pk.kid = kid;
+    pk.kpos = kpos;
+    pk.kpack = (char *)workspace + L.kpack;
+    pk.vpack = (char *)workspace + L.vpack;
+    pk.mpack = (int32_t *)((char *)workspace + L.mpack);
+    pk.kv_bs = r.kv_bs;
+    pk.km_bs = r.km_bs;
+    pk.batch = d->batch;
+    pk.tk = d->kv_len;
+    pk.hkv = d->num_kv_heads;
+    pk.nkt = r.nkt;
+    const hipError_t pe = ra::launch_pack_kv(pk, d->head_dim, s);
+    if (pe != hipSuccess) return hip_fail(pe, "K/V tile packing");
+  }
   const bool out_bf16 = d->out_dtype == RA_BF16;
   const hipError_t e = d->qkv_dtype == RA_BF16
                            ? ra::launch_attn_bf16(p, d->head_dim, r.nt, out_bf16, s)
@@ -301,10 +328,10 @@ ra_status ra_classify_tiles(const ra_attn_desc *d, const int32_t *qid, const int
   if (st != RA_OK) return st;
   if (!aligned(visible_pairs, 8)) return fail(RA_ERR_ALIGN, "visible_pairs must be 8-byte aligned");
   if (d->batch == 0) return RA_OK;
-  st = check_workspace(r, d->batch, workspace, workspace_bytes);
+  st = check_workspace(d, r, workspace, workspace_bytes);
   if (st != RA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  const ra::Schedule sch = carve(workspace, r, d->batch);
+  const ra::Schedule sch = carve(workspace, layout_of(d, r));
   st = run_schedule(d, r, sch, qid, qpos, kid, kpos, classes, s);
   if (st != RA_OK) return st;
   if (visible_pairs) {

@@ -7,22 +7,30 @@
 // the classification pass left in the query tile's work list ("Causal
 // attention": skipped tiles never load, full tiles run unmasked).
 //
-// Workgroup: 8 waves = NH heads of one GQA group x NT sub-tiles of 32 query
-// tokens (NH * NT = 8).  All waves share one K tile and one V tile in LDS, so
-// every K/V byte brought on chip feeds NH heads.  Each wave owns 32 query
-// tokens of one head and works on transposed scores S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16: a lane then holds one query column and 16 keys per
-// 32-key block, so the row max and row sum need one cross-half exchange and no
-// other lane traffic, and the transposed probabilities P^T are already laid out
-// as the B operand of O^T += V^T P^T.  V is written to LDS transposed, with the
-// keys of every 16-key chunk permuted to match that operand's lane layout, so
-// every MFMA operand read is one 16-byte LDS load.
+// Two kernels:
+//  * pack_kv: rewrites every 64-key tile of K and V (per batch row and K/V
+//    head) into a contiguous, LDS-ready block: K as [key][head_dim] and V
+//    transposed as [head_dim][key], 16-byte chunks XOR-swizzled by row so the
+//    MFMA operand reads below are bank-conflict free, plus the tile's segment
+//    ids and positions; keys past the end are zero.
+//  * forward: workgroup = 8 waves = NH heads of one GQA group x NT sub-tiles
+//    of 32 query tokens (NH * NT = 8).  The packed K, V^T and metadata blocks of
+//    the next tile stream straight from HBM into the other half of a
+//    double-buffered LDS (global_load_lds, no staging registers) while the
+//    current tile computes; all NH heads read the same LDS tile.  Each wave
+//    owns 32 query tokens of one head and computes transposed scores
+//    S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane then holds one query
+//    column and 16 keys per 32-key block, so the row max and row sum need one
+//    cross-half exchange and nothing else, and P^T is already the B operand of
+//    O^T += V^T P^T (the V^T key order inside each 16-key chunk is permuted to
+//    match the accumulator's row order).
 //
 // The running max is only raised when a new tile's max exceeds it by more than
 // 2^8 in probability terms; until then probabilities up to 256 are accumulated
-// against the stale max.  O = U / z and LSE = m + ln z are unchanged by which
-// reference max is used, and rescales of the 64-float accumulator become rare.
+// against the stale max.  O = U / z and LSE = m + ln z do not depend on which
+// reference max is used, and rescales of the accumulator become rare.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 
 #include "internal.h"
@@ -35,50 +43,106 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BN = kBnBf16;    // keys per tile
-constexpr int KPAD = 8;        // bf16 padding per K row (row stride 4 mod 64 banks)
-constexpr int VPAD = 8;        // bf16 padding per V^T row
-constexpr float kNoMax = -1e30f;         // finite "nothing seen yet" running max
-constexpr float kRescaleLog2 = 8.0f;     // raise the max only beyond 2^8
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+constexpr int BN = kBnBf16;          // keys per tile
+constexpr float kNoMax = -1e30f;     // finite "nothing seen yet" running max
+constexpr float kRescaleLog2 = 8.0f; // raise the max only beyond 2^8
+
+// Key (0..15) stored at V^T column x (0..15) of a 16-key chunk: a lane of half
+// h reads the 8 columns 8h..8h+7, which must hold keys 4h..4h+3 and
+// 8+4h..8+4h+3 -- the accumulator rows that half of the wave holds.
+__device__ __forceinline__ int vt_key(int x) {
+  const int h = (x >> 3) & 1, e = x & 7;
+  return (x & ~15) + (e < 4 ? 4 * h + e : 8 + 4 * h + (e - 4));
+}
+
+// ----------------------------------------------------------------------------- packing
 
 template <int D>
-struct Smem {
-  bf16 k[2][BN][D + KPAD];
-  bf16 vt[2][D][BN + VPAD];
-  int kid[2][BN];
-  int kpos[2][BN];
+__global__ __launch_bounds__(256) void pack_kv_kernel(PackParams p) {
+  constexpr int DV = D / 8;          // 16-byte chunks per K row
+  constexpr int KCH = BN * DV;       // 16-byte chunks per block
+  __shared__ __attribute__((aligned(16))) bf16 vs[BN][D + 8];
+  const int kt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int64_t tile = ((int64_t)b * p.hkv + g) * p.nkt + kt;
+  const bf16 *kb = (const bf16 *)p.k + b * p.kv_bs + (int64_t)g * D;
+  const bf16 *vb = (const bf16 *)p.v + b * p.kv_bs + (int64_t)g * D;
+  const int64_t tok = (int64_t)p.hkv * D;
+  bf16 *kout = (bf16 *)p.kpack + tile * (BN * D);
+  bf16 *vout = (bf16 *)p.vpack + tile * (BN * D);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  for (int u = tid; u < KCH; u += 256) {
+    const int r = u / DV, ph = u % DV;
+    const int key = kt * BN + r;
+    const int lc = ph ^ (r & 7);
+    u32x4 val = zero;
+    if (key < p.tk) val = *(const u32x4 *)(kb + key * tok + lc * 8);
+    *(u32x4 *)(kout + (int64_t)u * 8) = val;
+    u32x4 vv = zero;
+    if (key < p.tk) vv = *(const u32x4 *)(vb + key * tok + ph * 8);
+    *(u32x4 *)&vs[r][ph * 8] = vv;
+  }
+  if (tid < BN) {
+    const int key = kt * BN + tid;
+    int32_t *meta = p.mpack + tile * (2 * BN);
+    meta[tid] = key < p.tk ? p.kid[b * p.km_bs + key] : 0;
+    meta[BN + tid] = key < p.tk ? p.kpos[b * p.km_bs + key] : 0;
+  }
+  __syncthreads();
+  // V^T: D rows of BN keys, 8 chunks of 8 keys per row, swizzled by row.
+  const uint16_t *vsu = (const uint16_t *)&vs[0][0];
+  for (int u = tid; u < D * (BN / 8); u += 256) {
+    const int d = u / (BN / 8), ph = u % (BN / 8);
+    const int lc = ph ^ (d & 7);
+    u32x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = vsu[vt_key(lc * 8 + 2 * j) * (D + 8) + d];
+      const uint32_t hi = vsu[vt_key(lc * 8 + 2 * j + 1) * (D + 8) + d];
+      out[j] = lo | (hi << 16);
+    }
+    *(u32x4 *)(vout + (int64_t)u * 8) = out;
+  }
+}
+
+// ----------------------------------------------------------------------------- forward
+
+// Branch-free visibility test of one key against the lane's query.  With
+// non-negative ids and positions, the pair is visible iff kid == qkey (qkey is
+// -1 for a padding query) and lo <= qpos - kpos <= hi.
+struct LaneMask {
+  int qkey, qpos, lo, hi;
+  __device__ __forceinline__ bool operator()(int kid, int kpos) const {
+    const int d = qpos - kpos;
+    return (kid == qkey) & (d >= lo) & (d <= hi);
+  }
 };
 
-// LDS column of key kk (0..63) inside its V^T row: within each 16-key chunk a
-// lane of half h reads 8 consecutive columns 8h..8h+7, which must hold keys
-// 4h..4h+3 and 8+4h..8+4h+3 (the rows that half holds in the score accumulator).
-__device__ __forceinline__ int vt_col(int kk) {
-  return (kk & ~15) + ((kk >> 2) & 1) * 8 + ((kk >> 3) & 1) * 4 + (kk & 3);
-}
-
-__device__ __forceinline__ bool visible(int qid, int qpos, int kid, int kpos, const MaskParams &m) {
-  if (qid == 0 || qid != kid) return false;
-  const int64_t d = (int64_t)qpos - (int64_t)kpos;
-  if (m.causal && d < 0) return false;
-  if (m.wl >= 0 && d > m.wl) return false;
-  if (m.wr >= 0 && -d > m.wr) return false;
-  return true;
-}
+template <int D>
+struct Tile {
+  bf16 k[BN * D];
+  bf16 vt[D * BN];
+  int32_t meta[2 * BN];
+};
 
 template <int D, int NT, bool OUT_BF16>
-__global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+attn_fwd_bf16_kernel(AttnParams p) {
   constexpr int NH = kWaves / NT;
   constexpr int BM = 32 * NT;
-  constexpr int DC = D / 16;          // MFMA steps over head_dim for S^T
-  constexpr int DB = D / 32;          // 32-row blocks of O^T
-  constexpr int DV = D / 8;           // 16-byte chunks per K/V row
-  constexpr int KU = BN * DV;         // K tile units of 16 bytes
-  constexpr int KPT = (KU + 511) / 512;
-  constexpr int VU = (BN / 2) * DV;   // V tile units: 2 keys x 16 bytes
-  static_assert(VU <= 512, "one V unit per thread");
+  constexpr int DC = D / 16;               // MFMA steps over head_dim for S^T
+  constexpr int DB = D / 32;               // 32-row blocks of O^T
+  constexpr int BLK = BN * D * 2;          // bytes of one packed K (or V^T) block
+  constexpr int WPW = BLK / 1024 / kWaves; // 1 KB direct loads per wave per block
+  static_assert(WPW >= 1, "block too small for the wave count");
 
-  __shared__ Smem<D> sm;
+  __shared__ __attribute__((aligned(16))) Tile<D> t0;
+  __shared__ __attribute__((aligned(16))) Tile<D> t1;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -86,8 +150,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(AttnParams p) {
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  // Work item, with consecutive items kept on one XCD (blocks are dealt to the
-  // 8 XCDs round-robin; each XCD gets one contiguous run of items).
+  // Work item; consecutive items stay on one XCD (blocks are dealt to the 8
+  // XCDs round-robin, each XCD takes one contiguous run of items).
   const int hcn = p.group / NH;
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.nqt * hcn;
   const int64_t per_xcd = gridDim.x / 8;
@@ -105,143 +169,113 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(AttnParams p) {
   const int tq = qt * BM + (wave / NH) * 32 + col;
   const bool qvalid = tq < p.tq;
 
+  const int64_t row = (int64_t)b * p.nqt + qt;
+  const int n = p.count[row];
+  // The work list was written by an earlier kernel and is read-only here:
+  // read it through the constant address space so the loads are scalar and
+  // never wait behind the direct-to-LDS tile loads.
+  typedef const __attribute__((address_space(4))) uint32_t *const_list_t;
+  const const_list_t lst = (const_list_t)(p.list + row * p.nkt);
+  const int64_t tile0 = ((int64_t)b * p.hkv + g) * p.nkt;
+  const char *kpack = (const char *)p.kpack;
+  const char *vpack = (const char *)p.vpack;
+  const char *mpack = (const char *)p.mpack;
+
+  // Direct HBM -> LDS loads of one packed tile (1 KB per wave instruction).
+  auto issue = [&](Tile<D> &dst, int kt) {
+    const int64_t t = tile0 + kt;
+    const char *ks = kpack + t * BLK;
+    const char *vs = vpack + t * BLK;
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+      const int c = wave * WPW + i;
+      __builtin_amdgcn_global_load_lds((const void *)(ks + c * 1024 + lane * 16),
+                                       LDS_PTR((char *)dst.k + c * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vs + c * 1024 + lane * 16),
+                                       LDS_PTR((char *)dst.vt + c * 1024), 16, 0, 0);
+    }
+    if (wave < 2) {
+      const char *ms = mpack + t * (2 * BN * 4) + wave * (BN * 4);
+      __builtin_amdgcn_global_load_lds((const void *)(ms + lane * 4),
+                                       LDS_PTR((char *)dst.meta + wave * (BN * 4)), 4, 0, 0);
+    }
+  };
+
   // Q fragment (B operand of S^T = K Q^T): 8 consecutive head_dim values per step.
   bf16x8 qf[DC];
   {
     const bf16 *qrow = (const bf16 *)p.q + b * p.q_bs + (int64_t)tq * p.hq * D + (int64_t)h * D +
                        8 * half;
+#pragma unroll
     for (int c = 0; c < DC; ++c) {
       if (qvalid) {
         qf[c] = *(const bf16x8 *)(qrow + 16 * c);
       } else {
-        for (int e = 0; e < 8; ++e) qf[c][e] = (bf16)0.0f;
+        qf[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
       }
     }
   }
-  const int my_qid = qvalid ? p.qid[b * p.qm_bs + tq] : 0;
-  const int my_qpos = qvalid ? p.qpos[b * p.qm_bs + tq] : 0;
-
-  const int64_t row = (int64_t)b * p.nqt + qt;
-  const int n = p.count[row];
-  const uint32_t *lst = p.list + row * p.nkt;
-
-  const bf16 *kbase = (const bf16 *)p.k + b * p.kv_bs + (int64_t)g * D;
-  const bf16 *vbase = (const bf16 *)p.v + b * p.kv_bs + (int64_t)g * D;
-  const int32_t *kid_row = p.kid + b * p.km_bs;
-  const int32_t *kpos_row = p.kpos + b * p.km_bs;
-  const int64_t kv_tok = (int64_t)p.hkv * D;
+  LaneMask lm;
+  {
+    const int my_qid = qvalid ? p.qid[b * p.qm_bs + tq] : 0;
+    lm.qkey = my_qid != 0 ? my_qid : -1;
+    lm.qpos = qvalid ? p.qpos[b * p.qm_bs + tq] : 0;
+    lm.lo = p.mask.causal ? 0 : INT_MIN;
+    if (p.mask.wr >= 0) lm.lo = max(lm.lo, -p.mask.wr);
+    lm.hi = p.mask.wl >= 0 ? p.mask.wl : INT_MAX;
+  }
   const bool ragged = (p.tk % BN) != 0;
-
-  bf16x8 kreg[KPT];
-  bf16x8 vreg0, vreg1;
-  int idreg = 0, posreg = 0;
-
-  auto load_tile = [&](int kt) {
-    for (int i = 0; i < KPT; ++i) {
-      const int u = tid + 512 * i;
-      if (u < KU) {
-        const int r = u / DV, dc = u % DV;
-        const int key = kt * BN + r;
-        if (key < p.tk) {
-          kreg[i] = *(const bf16x8 *)(kbase + key * kv_tok + dc * 8);
-        } else {
-          for (int e = 0; e < 8; ++e) kreg[i][e] = (bf16)0.0f;
-        }
-      }
-    }
-    if (tid < VU) {
-      const int dc = tid % DV, kp = tid / DV;
-      const int key0 = kt * BN + 2 * kp;
-      if (key0 < p.tk) {
-        vreg0 = *(const bf16x8 *)(vbase + key0 * kv_tok + dc * 8);
-      } else {
-        for (int e = 0; e < 8; ++e) vreg0[e] = (bf16)0.0f;
-      }
-      if (key0 + 1 < p.tk) {
-        vreg1 = *(const bf16x8 *)(vbase + (key0 + 1) * kv_tok + dc * 8);
-      } else {
-        for (int e = 0; e < 8; ++e) vreg1[e] = (bf16)0.0f;
-      }
-    }
-    if (tid < BN) {
-      const int key = kt * BN + tid;
-      idreg = key < p.tk ? kid_row[key] : 0;
-      posreg = key < p.tk ? kpos_row[key] : 0;
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    for (int i = 0; i < KPT; ++i) {
-      const int u = tid + 512 * i;
-      if (u < KU) {
-        const int r = u / DV, dc = u % DV;
-        *(bf16x8 *)&sm.k[buf][r][dc * 8] = kreg[i];
-      }
-    }
-    if (tid < VU) {
-      const int dc = tid % DV, kp = tid / DV;
-      const int c = vt_col(2 * kp);
-      for (int e = 0; e < 8; ++e) {
-        union {
-          bf16 h2[2];
-          uint32_t u;
-        } pk;
-        pk.h2[0] = vreg0[e];
-        pk.h2[1] = vreg1[e];
-        *(uint32_t *)&sm.vt[buf][dc * 8 + e][c] = pk.u;
-      }
-    }
-    if (tid < BN) {
-      sm.kid[buf][tid] = idreg;
-      sm.kpos[buf][tid] = posreg;
-    }
+  auto entry_tile = [&](int it) { return (int)(lst[it] & 0x7fffffffu); };
+  auto entry_masked = [&](int it) {
+    const uint32_t e = lst[it];
+    return (e >> 31) != 0 || (ragged && (int)(e & 0x7fffffffu) == p.nkt - 1);
   };
 
   f32x16 o[DB];
+#pragma unroll
   for (int db = 0; db < DB; ++db)
+#pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m = kNoMax;   // running max of raw scores q.k
-  float z = 0.0f;     // this lane's share of the running sum
+  float m = kNoMax;  // running max of raw scores q.k
+  float z = 0.0f;    // this lane's share of the running sum
   const float c2 = p.scale_log2;
+  const int sw = col & 7;  // XOR swizzle of this lane's LDS rows
 
-  if (n > 0) {
-    load_tile((int)(lst[0] & 0x7fffffffu));
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < n; ++it) {
-    const uint32_t e = lst[it];
-    const int kt = (int)(e & 0x7fffffffu);
-    const bool masked = (e >> 31) || (ragged && kt == p.nkt - 1);
-    const int buf = it & 1;
-    if (it + 1 < n) load_tile((int)(lst[it + 1] & 0x7fffffffu));
-
-    // S^T for the two 32-key blocks.
+  // One tile: S^T = K Q^T, mask (boundary tiles only), online softmax, O^T += V^T P^T.
+  auto compute = [&](const Tile<D> &tl, bool masked) {
     f32x16 s[2];
+#pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      const bf16 *krow = tl.k + (kb * 32 + col) * D;
+      bf16x8 ka[DC];
+#pragma unroll
+      for (int c = 0; c < DC; ++c) ka[c] = *(const bf16x8 *)(krow + 8 * ((2 * c + half) ^ sw));
+#pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-      for (int c = 0; c < DC; ++c) {
-        const bf16x8 a = *(const bf16x8 *)&sm.k[buf][kb * 32 + col][16 * c + 8 * half];
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
-      }
+#pragma unroll
+      for (int c = 0; c < DC; ++c)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[c], s[kb], 0, 0, 0);
     }
     if (masked) {
+#pragma unroll
       for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int kk = kb * 32 + 8 * r4 + 4 * half;
-          const int4 ids = *(const int4 *)&sm.kid[buf][kk];
-          const int4 pss = *(const int4 *)&sm.kpos[buf][kk];
-          if (!visible(my_qid, my_qpos, ids.x, pss.x, p.mask)) s[kb][4 * r4 + 0] = -INFINITY;
-          if (!visible(my_qid, my_qpos, ids.y, pss.y, p.mask)) s[kb][4 * r4 + 1] = -INFINITY;
-          if (!visible(my_qid, my_qpos, ids.z, pss.z, p.mask)) s[kb][4 * r4 + 2] = -INFINITY;
-          if (!visible(my_qid, my_qpos, ids.w, pss.w, p.mask)) s[kb][4 * r4 + 3] = -INFINITY;
+          const int4 ids = *(const int4 *)&tl.meta[kk];
+          const int4 pss = *(const int4 *)&tl.meta[BN + kk];
+          s[kb][4 * r4 + 0] = lm(ids.x, pss.x) ? s[kb][4 * r4 + 0] : -INFINITY;
+          s[kb][4 * r4 + 1] = lm(ids.y, pss.y) ? s[kb][4 * r4 + 1] : -INFINITY;
+          s[kb][4 * r4 + 2] = lm(ids.z, pss.z) ? s[kb][4 * r4 + 2] : -INFINITY;
+          s[kb][4 * r4 + 3] = lm(ids.w, pss.w) ? s[kb][4 * r4 + 3] : -INFINITY;
         }
     }
 
     // Row max over this tile (the lane's 32 keys, then the other half's).
     float mx = s[0][0];
+#pragma unroll
     for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const bool raise = (mx - m) * c2 > kRescaleLog2;
@@ -250,7 +284,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(AttnParams p) {
         const float alpha = __builtin_amdgcn_exp2f((m - mx) * c2);
         m = mx;
         z *= alpha;
+#pragma unroll
         for (int db = 0; db < DB; ++db)
+#pragma unroll
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
     }
@@ -259,7 +295,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(AttnParams p) {
     // P^T = exp2(s * c2 - m * c2), summed and packed to bf16 B operands.
     bf16x8 pf[4];
     float zs = 0.0f;
+#pragma unroll
     for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -mc));
         zs += pv;
@@ -268,14 +306,39 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(AttnParams p) {
     z += zs;
 
     // O^T += V^T P^T over the four 16-key chunks.
-    for (int db = 0; db < DB; ++db)
-      for (int ch = 0; ch < 4; ++ch) {
-        const bf16x8 a = *(const bf16x8 *)&sm.vt[buf][db * 32 + col][ch * 16 + 8 * half];
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ch], o[db], 0, 0, 0);
-      }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16 *vrow = tl.vt + (db * 32 + col) * BN;
+      bf16x8 va[4];
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) va[ch] = *(const bf16x8 *)(vrow + 8 * ((2 * ch + half) ^ sw));
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ch], pf[ch], o[db], 0, 0, 0);
+    }
+  };
 
-    if (it + 1 < n) store_tile(buf ^ 1);
+  // Double-buffered loop, unrolled by two so each half names its LDS buffer
+  // statically: while tile it computes from one buffer, tile it+1 streams
+  // into the other.
+  if (n > 0) {
+    issue(t0, entry_tile(0));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  for (int it = 0; it < n;) {
+    if (it + 1 < n) issue(t1, entry_tile(it + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t0, entry_masked(it));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (++it >= n) break;
+    if (it + 1 < n) issue(t0, entry_tile(it + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t1, entry_masked(it));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    ++it;
   }
 
   // Epilogue: O = U / z, LSE = scale * m + ln z; empty rows get 0 and -inf.
@@ -284,7 +347,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(AttnParams p) {
   const bool live = zt > 0.0f;
   const float inv = live ? 1.0f / zt : 0.0f;
   const int64_t obase = b * p.o_bs + (int64_t)tq * p.hq * D + (int64_t)h * D + 4 * half;
+#pragma unroll
   for (int db = 0; db < DB; ++db)
+#pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d = db * 32 + 8 * r4;
       f32x4 val;
@@ -334,6 +399,22 @@ hipError_t launch_d(const AttnParams &p, int32_t nt, bool out_bf16, hipStream_t 
 }
 
 }  // namespace
+
+size_t packed_kv_bytes(int32_t batch, int32_t hkv, int32_t nkt, int32_t head_dim) {
+  return (size_t)batch * hkv * nkt * (2 * (size_t)BN * head_dim * 2 + 2 * BN * 4);
+}
+
+hipError_t launch_pack_kv(const PackParams &p, int32_t head_dim, hipStream_t stream) {
+  if (p.batch == 0 || p.nkt == 0) return hipSuccess;
+  dim3 grid(p.nkt, p.hkv, p.batch);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(pack_kv_kernel<128>, grid, dim3(256), 0, stream, p);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(pack_kv_kernel<64>, grid, dim3(256), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_bf16(const AttnParams &p, int32_t head_dim, int32_t nt, bool out_bf16,
                             hipStream_t stream) {

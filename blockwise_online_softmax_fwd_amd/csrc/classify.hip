@@ -228,7 +228,8 @@ __global__ __launch_bounds__(256) void pair_sum_kernel(const int64_t *__restrict
 
 }  // namespace
 
-WorkspaceLayout workspace_layout(int32_t batch, int32_t nqt, int32_t nkt) {
+WorkspaceLayout workspace_layout(int32_t batch, int32_t nqt, int32_t nkt, int32_t hkv,
+                                 int32_t packed_head_dim) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WorkspaceLayout w;
   size_t off = 0;
@@ -242,6 +243,13 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t nqt, int32_t nkt) {
   off = up(off + (size_t)batch * nqt * sizeof(int64_t));
   w.list = off;
   off = up(off + (size_t)batch * nqt * nkt * sizeof(uint32_t));
+  const size_t tiles = packed_head_dim > 0 ? (size_t)batch * hkv * nkt : 0;
+  w.kpack = off;
+  off = up(off + tiles * kBnBf16 * packed_head_dim * 2);
+  w.vpack = off;
+  off = up(off + tiles * kBnBf16 * packed_head_dim * 2);
+  w.mpack = off;
+  off = up(off + tiles * 2 * kBnBf16 * sizeof(int32_t));
   w.total = off;
   return w;
 }

@@ -40,10 +40,24 @@ struct Schedule {
 };
 
 struct WorkspaceLayout {
-  size_t qsum, ksum, count, pairs, list, total;
+  size_t qsum, ksum, count, pairs, list, kpack, vpack, mpack, total;
 };
 
-WorkspaceLayout workspace_layout(int32_t batch, int32_t nqt, int32_t nkt);
+// packed_head_dim > 0 adds room for the packed K / V^T / metadata tiles of the
+// bf16 forward (batch * hkv * nkt tiles).
+WorkspaceLayout workspace_layout(int32_t batch, int32_t nqt, int32_t nkt, int32_t hkv = 0,
+                                 int32_t packed_head_dim = 0);
+
+// Packed K/V tiles of the bf16 forward.
+struct PackParams {
+  const void *k, *v;
+  const int32_t *kid, *kpos;
+  void *kpack, *vpack;
+  int32_t *mpack;
+  int64_t kv_bs, km_bs;
+  int32_t batch, tk, hkv, nkt;
+};
+hipError_t launch_pack_kv(const PackParams &p, int32_t head_dim, hipStream_t stream);
 
 struct AttnParams {
   const void *q, *k, *v;
@@ -52,6 +66,8 @@ struct AttnParams {
   float *lse;
   const uint32_t *list;
   const int32_t *count;
+  const void *kpack, *vpack;   // bf16 path: packed tiles written by pack_kv
+  const int32_t *mpack;
   int64_t q_bs, kv_bs, o_bs, lse_bs, qm_bs, km_bs;  // batch strides (elements)
   int32_t batch, tq, tk, hq, hkv, group;
   int32_t nqt, nkt;

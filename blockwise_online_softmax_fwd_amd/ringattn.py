@@ -116,6 +116,8 @@ def _torch_dtype(code: int):
 
 def _batch_stride(t, inner_dims: int) -> int:
     """Batch stride of a [B, T, ...] tensor whose non-batch dims are dense."""
+    if t.numel() == 0:
+        return 0
     expect = 1
     for d in range(t.dim() - 1, 0, -1):
         if t.size(d) > 1 and t.stride(d) != expect:

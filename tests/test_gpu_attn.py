@@ -105,7 +105,8 @@ def test_empty_inputs():
     assert o0.shape == (2, 0, 8, 128)
     qb = torch.zeros(0, 5, 8, 128, dtype=torch.bfloat16)
     eb = torch.zeros(0, 5, dtype=torch.int32)
-    ob, lb = bosf.attn_fwd(*_dev(qb, qb[:, :, :2], qb[:, :, :2], eb, eb, eb, eb))
+    kb = torch.zeros(0, 5, 2, 128, dtype=torch.bfloat16)
+    ob, lb = bosf.attn_fwd(*_dev(qb, kb, kb, eb, eb, eb, eb))
     assert ob.numel() == 0
 
 
