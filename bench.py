@@ -4,10 +4,13 @@ A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM.  For the default workload (one device's share of the
 TransformerEngine tutorial's long-context case, run as a 4-shard ring) that is:
 causal load-balancing reorder of Q, K, V, segment ids and positions; for each
-of the 4 shards, 4 ring steps of attn_fwd (tile classification + attention)
-with 3 merges; inverse reorder of O and LSE.  All four shards are computed, so
-a step is the complete forward of B=2 x 65536 tokens; FLOPs count only visible
-pairs (4 * head_dim * Hq flops per pair).
+of the 4 shards, 4 ring steps -- attn_fwd for the shard's own chunk, then
+attn_fwd_accumulate for the 3 chunks that arrive next, each folding its block
+into the running fp32 partial in its epilogue (the merge of the ring update,
+fused; ``--unfused`` runs attn_fwd + attn_merge instead); inverse reorder of O
+and LSE.  All four shards are computed, so a step is the complete forward of
+B=2 x 65536 tokens; FLOPs count only visible pairs (4 * head_dim * Hq per pair).
+attn_merge is also timed on its own at the shard partials' shape.
 
 Prints one JSON line.  ``roofline`` is measured live with HIP events around
 every attn_fwd call (on the stream the library launches on); ``cpu_baseline``
@@ -114,6 +117,8 @@ def main():
     ap.add_argument("--workload", type=int, default=5, help="workload number (1-5)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="ring steps write separate partials folded by attn_merge")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the ring is "
@@ -144,7 +149,8 @@ def main():
 
         def step():
             bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe, causal=w.causal,
-                              window=w.window, bufs=bufs, step_hook=ev.hook)
+                              window=w.window, bufs=bufs, step_hook=ev.hook,
+                              fused=not args.unfused)
     else:
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
@@ -185,22 +191,43 @@ def main():
     if w.cp_size > 1:
         b, t, hq, d = q.shape
         n = t // w.cp_size
-        rows = b * n * hq
-        merges = ev.ms("attn_merge")
-        # per shard: 2 merges fp32+fp32->fp32, 1 merge fp32+fp32->bf16 (bytes: 2 reads + write + lse)
-        merge_bytes = w.cp_size * rows * ((2 * (3 * 4 * d + 12)) + (2 * 4 * d + 2 * d + 12))
         reorder_ms = sum(ev.ms("reorder")) / args.steps
         inv_ms = sum(ev.ms("inverse_reorder")) / args.steps
         fwd_bytes = 2 * (q.numel() * 2 + 2 * k.numel() * 2 + 2 * ids.numel() * 4)
         inv_bytes = 2 * (q.numel() * 2 + b * t * hq * 4)
         detail.update({
-            "attn_merge_ms_per_step": sum(merges) / args.steps,
-            "attn_merge_GBs": merge_bytes / (sum(merges) / args.steps / 1000.0) / 1e9,
+            "ring_merge": "unfused: attn_merge per step" if args.unfused
+                          else "fused into attn_fwd_accumulate epilogues",
             "reorder_ms_per_step": reorder_ms,
             "reorder_GBs": fwd_bytes / (reorder_ms / 1000.0) / 1e9,
             "inverse_reorder_ms_per_step": inv_ms,
             "inverse_reorder_GBs": inv_bytes / (inv_ms / 1000.0) / 1e9,
         })
+        if args.unfused:
+            merges = ev.ms("attn_merge")
+            detail["attn_merge_ms_per_step"] = sum(merges) / args.steps
+        # attn_merge on its own: two fp32 shard partials with finite LSE (every
+        # row reads both operands): 3 * D * 4 + 12 bytes per (b, t, h) row.
+        pa = torch.randn((b, n, hq, d), device=dev)
+        pb = torch.randn_like(pa)
+        la = torch.randn((b, n, hq), device=dev)
+        lb = torch.randn_like(la)
+        outm = torch.empty_like(pa)
+        outl = torch.empty_like(la)
+        for _ in range(2):
+            bosf.attn_merge(pa, la, pb, lb, out=outm, lse_out=outl)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            bosf.attn_merge(pa, la, pb, lb, out=outm, lse_out=outl)
+        e1.record()
+        torch.cuda.synchronize()
+        mms = e0.elapsed_time(e1) / 5
+        mbytes = b * n * hq * (3 * 4 * d + 12)
+        detail.update({"attn_merge_ms_per_call": mms,
+                       "attn_merge_GBs": mbytes / (mms / 1000.0) / 1e9,
+                       "attn_merge_bytes_per_call": mbytes})
+        del pa, pb, la, lb, outm, outl
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
                 "kernel": "attn_fwd (tile classification + bf16 MFMA forward)",

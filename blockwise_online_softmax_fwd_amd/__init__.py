@@ -13,6 +13,7 @@ from .ringattn import (  # noqa: F401
     TILE_SKIP,
     RingAttnError,
     attn_fwd,
+    attn_fwd_accumulate,
     attn_merge,
     check_support,
     classify_tiles,

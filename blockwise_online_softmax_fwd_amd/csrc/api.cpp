@@ -220,10 +220,14 @@ ra_status ra_attn_fwd_workspace_size(const ra_attn_desc *desc, size_t *bytes) {
   return RA_OK;
 }
 
-ra_status ra_attn_fwd(const ra_attn_desc *d, const void *q, const void *k, const void *v,
-                      const int32_t *qid, const int32_t *qpos, const int32_t *kid,
-                      const int32_t *kpos, void *o, float *lse, void *workspace,
-                      size_t workspace_bytes, ra_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, const void *v,
+                        const int32_t *qid, const int32_t *qpos, const int32_t *kid,
+                        const int32_t *kpos, const ra_partial *acc, void *o, float *lse,
+                        void *workspace, size_t workspace_bytes, ra_stream_t stream) {
   Resolved r;
   ra_status st = check_desc(d, &r);
   if (st != RA_OK) return st;
@@ -249,6 +253,30 @@ ra_status ra_attn_fwd(const ra_attn_desc *d, const void *q, const void *k, const
       overlaps(lse, l_span, q, q_span) || overlaps(lse, l_span, k, kv_span) ||
       overlaps(lse, l_span, v, kv_span))
     return fail(RA_ERR_ALIAS, "o / lse overlap an input or each other");
+  int64_t acc_o_bs = 0, acc_lse_bs = 0;
+  bool in_place = false;
+  if (acc) {
+    if (!dtype_ok(acc->dtype)) return fail(RA_ERR_DTYPE, "unknown partial dtype %d", acc->dtype);
+    if (acc->o_batch_stride < 0 || acc->lse_batch_stride < 0)
+      return fail(RA_ERR_SHAPE, "partial batch strides must be >= 0");
+    const int64_t rows = (int64_t)d->q_len * d->num_q_heads;
+    acc_o_bs = pick(acc->o_batch_stride, rows * D);
+    acc_lse_bs = pick(acc->lse_batch_stride, rows);
+    if (d->batch > 1 && (acc_o_bs < rows * D || acc_lse_bs < rows))
+      return fail(RA_ERR_SHAPE, "a partial batch stride is smaller than one batch row");
+    if (has_q && (!acc->o || !acc->lse)) return fail(RA_ERR_NULL, "partial o or lse is NULL");
+    const size_t as = dtype_size(acc->dtype);
+    if (!aligned(acc->o, 16) || (acc_o_bs * as) % 16 || !aligned(acc->lse, 4))
+      return fail(RA_ERR_ALIGN, "partial o must be 16-byte aligned (lse 4-byte)");
+    const size_t a_span = span_bytes(d->batch, acc_o_bs, rows * D, as);
+    const size_t al_span = span_bytes(d->batch, acc_lse_bs, rows, 4);
+    const bool same_o = acc->o == o && acc->dtype == d->out_dtype && acc_o_bs == r.o_bs;
+    const bool same_l = acc->lse == lse && acc_lse_bs == r.lse_bs;
+    in_place = same_o && same_l;
+    if (!in_place && (overlaps(o, o_span, acc->o, a_span) || overlaps(lse, l_span, acc->lse, al_span) ||
+                      overlaps(o, o_span, acc->lse, al_span) || overlaps(lse, l_span, acc->o, a_span)))
+      return fail(RA_ERR_ALIAS, "o / lse overlap the partial without being it");
+  }
   if (!has_q) return RA_OK;
   st = check_workspace(d, r, workspace, workspace_bytes);
   if (st != RA_OK) return st;
@@ -288,6 +316,12 @@ ra_status ra_attn_fwd(const ra_attn_desc *d, const void *q, const void *k, const
   p.scale = d->scale;
   p.scale_log2 = d->scale * 1.4426950408889634f;
   p.mask = mask_of(d);
+  p.acc_o = acc ? acc->o : nullptr;
+  p.acc_lse = acc ? acc->lse : nullptr;
+  p.acc_o_bs = acc_o_bs;
+  p.acc_lse_bs = acc_lse_bs;
+  p.acc_mode = acc ? (acc->dtype == RA_BF16 ? 2 : 1) : 0;
+  p.acc_in_place = in_place ? 1 : 0;
   p.kpack = (char *)workspace + L.kpack;
   p.vpack = (char *)workspace + L.vpack;
   p.mpack = (const int32_t *)((char *)workspace + L.mpack);
@@ -315,6 +349,28 @@ ra_status ra_attn_fwd(const ra_attn_desc *d, const void *q, const void *k, const
                            : ra::launch_attn_f32(p, d->head_dim, out_bf16, s);
   if (e != hipSuccess) return hip_fail(e, "attention forward");
   return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status ra_attn_fwd(const ra_attn_desc *d, const void *q, const void *k, const void *v,
+                      const int32_t *qid, const int32_t *qpos, const int32_t *kid,
+                      const int32_t *kpos, void *o, float *lse, void *workspace,
+                      size_t workspace_bytes, ra_stream_t stream) {
+  return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, nullptr, o, lse, workspace,
+                       workspace_bytes, stream);
+}
+
+ra_status ra_attn_fwd_accumulate(const ra_attn_desc *d, const void *q, const void *k,
+                                 const void *v, const int32_t *qid, const int32_t *qpos,
+                                 const int32_t *kid, const int32_t *kpos,
+                                 const ra_partial *partial, void *o, float *lse, void *workspace,
+                                 size_t workspace_bytes, ra_stream_t stream) {
+  if (!partial) return fail(RA_ERR_NULL, "partial is NULL");
+  return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, partial, o, lse, workspace,
+                       workspace_bytes, stream);
 }
 
 ra_status ra_classify_tiles(const ra_attn_desc *d, const int32_t *qid, const int32_t *qpos,

@@ -34,6 +34,7 @@
 #include <math.h>
 
 #include "internal.h"
+#include "lse_merge.h"
 
 namespace ra {
 namespace {
@@ -171,6 +172,9 @@ attn_fwd_bf16_kernel(AttnParams p) {
 
   const int64_t row = (int64_t)b * p.nqt + qt;
   const int n = p.count[row];
+  // Accumulating in place into a partial: a query tile with nothing visible in
+  // this call keeps its partial as it is.
+  if (p.acc_in_place && n == 0) return;
   // The work list was written by an earlier kernel and is read-only here:
   // read it through the constant address space so the loads are scalar and
   // never wait behind the direct-to-LDS tile loads.
@@ -342,21 +346,46 @@ attn_fwd_bf16_kernel(AttnParams p) {
   }
 
   // Epilogue: O = U / z, LSE = scale * m + ln z; empty rows get 0 and -inf.
+  // With a running partial (O_a, L_a): L = log(e^LSE + e^L_a) and
+  // O = e^(LSE - L) U / z + e^(L_a - L) O_a.
   const float zt = z + __shfl_xor(z, 32);
   if (!qvalid) return;
   const bool live = zt > 0.0f;
-  const float inv = live ? 1.0f / zt : 0.0f;
-  const int64_t obase = b * p.o_bs + (int64_t)tq * p.hq * D + (int64_t)h * D + 4 * half;
+  const float l_own = live ? p.scale * m + logf(zt) : -INFINITY;
+  float w_own = live ? 1.0f / zt : 0.0f;
+  float w_acc = 0.0f, l_out = l_own;
+  const int64_t rel = (int64_t)tq * p.hq * D + (int64_t)h * D + 4 * half;
+  if (p.acc_mode) {
+    const float la = p.acc_lse[b * p.acc_lse_bs + (int64_t)tq * p.hq + h];
+    l_out = lse_add(l_own, la);
+    w_acc = lse_weight(la, l_out);
+    w_own = live ? lse_weight(l_own, l_out) / zt : 0.0f;
+  }
+  const int64_t obase = b * p.o_bs + rel;
+  const int64_t abase = b * p.acc_o_bs + rel;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d = db * 32 + 8 * r4;
       f32x4 val;
-      val[0] = o[db][4 * r4 + 0] * inv;
-      val[1] = o[db][4 * r4 + 1] * inv;
-      val[2] = o[db][4 * r4 + 2] * inv;
-      val[3] = o[db][4 * r4 + 3] * inv;
+      val[0] = o[db][4 * r4 + 0] * w_own;
+      val[1] = o[db][4 * r4 + 1] * w_own;
+      val[2] = o[db][4 * r4 + 2] * w_own;
+      val[3] = o[db][4 * r4 + 3] * w_own;
+      if (w_acc != 0.0f) {
+        f32x4 a;
+        if (p.acc_mode == 2) {
+          const bf16x4 ah = *(const bf16x4 *)((const bf16 *)p.acc_o + abase + d);
+          a[0] = (float)ah[0];
+          a[1] = (float)ah[1];
+          a[2] = (float)ah[2];
+          a[3] = (float)ah[3];
+        } else {
+          a = *(const f32x4 *)((const float *)p.acc_o + abase + d);
+        }
+        val += w_acc * a;
+      }
       if (OUT_BF16) {
         bf16x4 hv;
         hv[0] = (bf16)val[0];
@@ -368,8 +397,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
         *(f32x4 *)((float *)p.o + obase + d) = val;
       }
     }
-  if (half == 0)
-    p.lse[b * p.lse_bs + (int64_t)tq * p.hq + h] = live ? p.scale * m + logf(zt) : -INFINITY;
+  if (half == 0) p.lse[b * p.lse_bs + (int64_t)tq * p.hq + h] = l_out;
 }
 
 template <int D, int NT>

@@ -11,6 +11,7 @@
 #include <math.h>
 
 #include "internal.h"
+#include "lse_merge.h"
 
 namespace ra {
 namespace {
@@ -57,6 +58,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
 
   const int64_t row = (int64_t)b * p.nqt + qt;
   const int n = p.count[row];
+  if (p.acc_in_place && n == 0) return;  // partial stays as it is
   const uint32_t *lst = p.list + row * p.nkt;
   const float *kb = (const float *)p.k + b * p.kv_bs + (int64_t)g * D;
   const float *vb = (const float *)p.v + b * p.kv_bs + (int64_t)g * D;
@@ -108,16 +110,31 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
 
   if (!qvalid) return;
   const bool live = z > 0.0f;
-  const float inv = live ? 1.0f / z : 0.0f;
-  const int64_t obase = b * p.o_bs + (int64_t)tq * p.hq * D + (int64_t)h * D + half * DH;
+  const float l_own = live ? m + logf(z) : -INFINITY;
+  float w_own = live ? 1.0f / z : 0.0f;
+  float w_acc = 0.0f, l_out = l_own;
+  const int64_t rel = (int64_t)tq * p.hq * D + (int64_t)h * D + half * DH;
+  if (p.acc_mode) {
+    const float la = p.acc_lse[b * p.acc_lse_bs + (int64_t)tq * p.hq + h];
+    l_out = lse_add(l_own, la);
+    w_acc = lse_weight(la, l_out);
+    w_own = live ? lse_weight(l_own, l_out) / z : 0.0f;
+  }
+  const int64_t obase = b * p.o_bs + rel;
+  const int64_t abase = b * p.acc_o_bs + rel;
   for (int d = 0; d < DH; ++d) {
-    const float val = o[d] * inv;
+    float val = o[d] * w_own;
+    if (w_acc != 0.0f) {
+      const float a = p.acc_mode == 2 ? (float)((const __bf16 *)p.acc_o)[abase + d]
+                                      : ((const float *)p.acc_o)[abase + d];
+      val += w_acc * a;
+    }
     if (OUT_BF16)
       ((__bf16 *)p.o)[obase + d] = (__bf16)val;
     else
       ((float *)p.o)[obase + d] = val;
   }
-  if (half == 0) p.lse[b * p.lse_bs + (int64_t)tq * p.hq + h] = live ? m + logf(z) : -INFINITY;
+  if (half == 0) p.lse[b * p.lse_bs + (int64_t)tq * p.hq + h] = l_out;
 }
 
 template <int D>

@@ -74,6 +74,12 @@ struct AttnParams {
   float scale;       // score scale
   float scale_log2;  // scale * log2(e)
   MaskParams mask;
+  // Optional running partial merged into the result in the epilogue.
+  const void *acc_o;
+  const float *acc_lse;
+  int64_t acc_o_bs, acc_lse_bs;
+  int32_t acc_mode;      // 0 none, 1 fp32 partial, 2 bf16 partial
+  int32_t acc_in_place;  // o/lse are the partial itself: untouched tiles are skipped
 };
 
 // Launchers (return the launch's hipError_t).

@@ -65,9 +65,16 @@ def reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs: RingBuff
 
 
 def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, window=(-1, -1),
-               step_hook=None):
+               step_hook=None, fused=True):
     """Rank ``rank``'s R ring steps on the reordered buffers; the merged result
-    lands in rank's shard of ``bufs.o`` / ``bufs.lse`` (reordered order)."""
+    lands in rank's shard of ``bufs.o`` / ``bufs.lse`` (reordered order).
+
+    ``fused``: each step after the first folds its block into the running
+    partial inside the forward's epilogue (``attn_fwd_accumulate``, in place in
+    the fp32 partial, the last step writing the final output); otherwise every
+    step writes its own partial and ``attn_merge`` folds it in."""
+    if fused:
+        return _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook)
     t = bufs.q.shape[1]
     n = t // cp_size
     rows = slice(rank * n, (rank + 1) * n)
@@ -100,9 +107,34 @@ def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, win
             step_hook("attn_merge", rank, s, False)
 
 
+def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook):
+    t = bufs.q.shape[1]
+    n = t // cp_size
+    rows = slice(rank * n, (rank + 1) * n)
+    q_r, id_r, pos_r = bufs.q[:, rows], bufs.ids[:, rows], bufs.pos[:, rows]
+    o_r, lse_r = bufs.o[:, rows], bufs.lse[:, rows]
+    for s in range(cp_size):
+        c = (rank - s) % cp_size
+        cols = slice(c * n, (c + 1) * n)
+        args = (q_r, bufs.k[:, cols], bufs.v[:, cols], id_r, pos_r, bufs.ids[:, cols],
+                bufs.pos[:, cols])
+        last = s == cp_size - 1
+        dst, dst_lse = (o_r, lse_r) if last else (bufs.acc, bufs.acc_lse)
+        if step_hook:
+            step_hook("attn_fwd", rank, s, True)
+        if s == 0:
+            ra.attn_fwd(*args, scale=scale, causal=causal, window=window, out_dtype=dst.dtype,
+                        out=dst, lse=dst_lse, workspace=bufs.workspace)
+        else:
+            ra.attn_fwd_accumulate(*args, bufs.acc, bufs.acc_lse, scale=scale, causal=causal,
+                                   window=window, out=dst, lse=dst_lse, workspace=bufs.workspace)
+        if step_hook:
+            step_hook("attn_fwd", rank, s, False)
+
+
 def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, scale=None,
                  causal=True, window=(-1, -1), ranks=None, bufs: RingBuffers | None = None,
-                 partial_dtype=torch.float32, out_dtype=None, step_hook=None):
+                 partial_dtype=torch.float32, out_dtype=None, step_hook=None, fused=True):
     """Ring-decomposed attention forward of self-attention inputs on one GPU.
 
     q ``[B,T,Hq,D]``, k/v ``[B,T,Hkv,D]``, ids/pos ``int32 [B,T]`` in the
@@ -127,7 +159,8 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     if step_hook:
         step_hook("reorder", -1, -1, False)
     for r in (range(cp_size) if ranks is None else ranks):
-        rank_steps(r, cp_size, bufs, scale=scale, causal=causal, window=window, step_hook=step_hook)
+        rank_steps(r, cp_size, bufs, scale=scale, causal=causal, window=window, step_hook=step_hook,
+                   fused=fused)
     if step_hook:
         step_hook("inverse_reorder", -1, -1, True)
     o = ra.inverse_reorder(bufs.o, cp_size, kind, stripe_size)

@@ -26,8 +26,9 @@ STATUS = {0: "RA_OK", 1: "RA_ERR_NULL", 2: "RA_ERR_SHAPE", 3: "RA_ERR_DTYPE", 4:
           5: "RA_ERR_UNSUPPORTED", 6: "RA_ERR_WORKSPACE", 7: "RA_ERR_ALIAS", 8: "RA_ERR_HIP"}
 
 EXPORTS = ["ra_version", "ra_status_string", "ra_last_error", "ra_check_support", "ra_tile_shape",
-           "ra_attn_fwd_workspace_size", "ra_attn_fwd", "ra_classify_tiles", "ra_attn_merge",
-           "ra_reorder", "ra_inverse_reorder", "ra_reorder_index"]
+           "ra_attn_fwd_workspace_size", "ra_attn_fwd", "ra_attn_fwd_accumulate",
+           "ra_classify_tiles", "ra_attn_merge", "ra_reorder", "ra_inverse_reorder",
+           "ra_reorder_index"]
 
 
 class RingAttnError(RuntimeError):
@@ -44,6 +45,12 @@ class AttnDesc(ctypes.Structure):
         (n, ctypes.c_int64) for n in (
             "q_batch_stride", "kv_batch_stride", "o_batch_stride", "lse_batch_stride",
             "q_meta_batch_stride", "kv_meta_batch_stride")]
+
+
+class Partial(ctypes.Structure):
+    _fields_ = [("o", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("o_batch_stride", ctypes.c_int64),
+                ("lse_batch_stride", ctypes.c_int64)]
 
 
 class MergeDesc(ctypes.Structure):
@@ -75,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ra_tile_shape": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(I32), ctypes.POINTER(I32)], I32),
         "ra_attn_fwd_workspace_size": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)], I32),
         "ra_attn_fwd": ([ctypes.POINTER(AttnDesc)] + [P] * 9 + [P, SZ, P], I32),
+        "ra_attn_fwd_accumulate": ([ctypes.POINTER(AttnDesc)] + [P] * 7 +
+                                   [ctypes.POINTER(Partial)] + [P] * 2 + [P, SZ, P], I32),
         "ra_classify_tiles": ([ctypes.POINTER(AttnDesc)] + [P] * 6 + [P, SZ, P], I32),
         "ra_attn_merge": ([ctypes.POINTER(MergeDesc)] + [P] * 6 + [P], I32),
         "ra_reorder": ([P, P, I32, I32, I64, I32, I32, I32, P], I32),
@@ -222,6 +231,46 @@ def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_segment_ids), _ptr(q_segment_pos),
         _ptr(kv_segment_ids), _ptr(kv_segment_pos), _ptr(out), _ptr(lse), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), _stream(q)))
+    return out, lse
+
+
+def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos,
+                        partial_o, partial_lse, *, scale=None, causal=True, window=(-1, -1),
+                        out_dtype=None, out=None, lse=None, workspace=None):
+    """Attention forward merged with a running partial ``(partial_o, partial_lse)``
+    over other key sets.  ``out``/``lse`` default to the partial itself (in-place
+    update); query tiles with no visible pair in this call are then untouched.
+    Returns ``(out, lse)``."""
+    _require_gpu(q, k, v, partial_o, partial_lse)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape or _batch_stride(v, 3) != _batch_stride(k, 3):
+        raise ValueError("k and v must have the same shape and batch stride")
+    b, tq, hq, d = q.shape
+    if tuple(partial_o.shape) != (b, tq, hq, d) or tuple(partial_lse.shape) != (b, tq, hq):
+        raise ValueError("the partial must have o's and lse's shapes")
+    if partial_lse.dtype != torch.float32:
+        raise TypeError("partial lse must be float32")
+    if out is None:
+        out = partial_o
+    if lse is None:
+        lse = partial_lse
+    oc = _dtype_code(out.dtype) if out_dtype is None else _dtype_code(out_dtype)
+    if _dtype_code(out.dtype) != oc:
+        raise TypeError("out has the wrong dtype")
+    desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window, oc, out, lse)
+    part = Partial()
+    part.o, part.lse = partial_o.data_ptr(), partial_lse.data_ptr()
+    part.dtype = _dtype_code(partial_o.dtype)
+    part.o_batch_stride = _batch_stride(partial_o, 3)
+    part.lse_batch_stride = _batch_stride(partial_lse, 2)
+    ws_bytes = workspace_size(desc)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _check(load_library().ra_attn_fwd_accumulate(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_segment_ids), _ptr(q_segment_pos),
+        _ptr(kv_segment_ids), _ptr(kv_segment_pos), ctypes.byref(part), _ptr(out), _ptr(lse),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(q)))
     return out, lse
 
 

@@ -108,7 +108,8 @@ const char *ra_last_error(void);
  * [CPP]): RA_OK if ra_attn_fwd implements this description, otherwise the
  * status it would return.  Supported: bf16 q/k/v (MFMA path) or fp32 q/k/v,
  * D in {64, 128}, bf16 or fp32 output, any Hq/Hkv group size, any lengths up to
- * 2^22 key tokens per call.  Makes no HIP call.
+ * 2^21 key tokens per call (2^20 for fp32).  Segment ids and positions must
+ * be non-negative.  Makes no HIP call.
  */
 ra_status ra_check_support(const ra_attn_desc *desc);
 
@@ -143,6 +144,36 @@ ra_status ra_attn_fwd(const ra_attn_desc *desc, const void *q, const void *k, co
                       const int32_t *q_segment_ids, const int32_t *q_segment_pos,
                       const int32_t *kv_segment_ids, const int32_t *kv_segment_pos, void *o,
                       float *lse, void *workspace, size_t workspace_bytes, ra_stream_t stream);
+
+/*
+ * Accumulating forward: the same attention as ra_attn_fwd, merged in the
+ * epilogue with a running partial result over other key sets ([RA] "Online
+ * softmax": the ring's per-step update, fused into the step that produces the
+ * new block):
+ *   L = log(exp(LSE) + exp(partial.lse));  o = exp(LSE - L) O + exp(partial.lse - L) partial.o
+ * where (O, LSE) is this call's attention; rows where either side is empty take
+ * the other side unchanged (converted to out_dtype).  o/lse may be exactly
+ * partial.o/partial.lse (same dtype and strides): the update is then in place
+ * and query tiles with no visible pair in this call are not touched at all.
+ * Any other overlap between o/lse and the partial is RA_ERR_ALIAS.  The partial
+ * has o's shape [B,Tq,Hq,D] (dtype partial.dtype, 16-byte aligned) and lse's
+ * shape [B,Tq,Hq] (fp32); its batch strides are in elements, 0 = dense.  All
+ * other arguments, rules and the workspace are those of ra_attn_fwd.
+ */
+typedef struct ra_partial {
+  const void *o;
+  const float *lse;
+  int32_t dtype; /* ra_dtype of o */
+  int32_t reserved;
+  int64_t o_batch_stride, lse_batch_stride;
+} ra_partial;
+
+ra_status ra_attn_fwd_accumulate(const ra_attn_desc *desc, const void *q, const void *k,
+                                 const void *v, const int32_t *q_segment_ids,
+                                 const int32_t *q_segment_pos, const int32_t *kv_segment_ids,
+                                 const int32_t *kv_segment_pos, const ra_partial *partial, void *o,
+                                 float *lse, void *workspace, size_t workspace_bytes,
+                                 ra_stream_t stream);
 
 /*
  * The exact tile classes of the mask at the tile shape of ra_tile_shape()

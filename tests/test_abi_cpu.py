@@ -170,6 +170,31 @@ def test_fwd_rejects_aliasing(lib):
     assert _fwd(lib, d, lse=_p((7 << 32) + 4096)) == ALIAS  # lse inside o
 
 
+def test_accumulate_validation(lib):
+    d = _desc()
+    part = ra.Partial()
+    part.o, part.lse, part.dtype = FAKE + (10 << 32), FAKE + (11 << 32), ra.RA_F32
+
+    def call(pp, o=_p(7 << 32), lse=_p(8 << 32)):
+        return lib.ra_attn_fwd_accumulate(ctypes.byref(d), _p(0), _p(1 << 32), _p(2 << 32),
+                                          _p(3 << 32), _p(4 << 32), _p(5 << 32), _p(6 << 32),
+                                          pp, o, lse, _p(9 << 32), ctypes.c_size_t(1 << 30), None)
+    assert call(None) == NULL
+    bad = ra.Partial()
+    bad.o, bad.lse, bad.dtype = FAKE + (10 << 32), None, ra.RA_F32
+    assert call(ctypes.byref(bad)) == NULL
+    bad.lse, bad.dtype = FAKE + (11 << 32), 9
+    assert call(ctypes.byref(bad)) == DTYPE
+    bad.dtype, bad.o = ra.RA_F32, FAKE + (10 << 32) + 8
+    assert call(ctypes.byref(bad)) == ALIGN
+    bad.o, bad.o_batch_stride = FAKE + (10 << 32), 3
+    assert call(ctypes.byref(bad)) == SHAPE
+    # o overlapping the partial without being it (shifted, or other dtype)
+    assert call(ctypes.byref(part), o=_p((10 << 32) + 256)) == ALIAS
+    d.out_dtype = ra.RA_BF16
+    assert call(ctypes.byref(part), o=_p(10 << 32), lse=_p(11 << 32)) == ALIAS
+
+
 def _merge(lib, md, **over):
     args = dict(oa=_p(0), la=_p(1 << 32), ob=_p(2 << 32), lb=_p(3 << 32), oo=_p(4 << 32),
                 lo=_p(5 << 32))

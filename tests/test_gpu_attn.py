@@ -160,30 +160,88 @@ def test_workload_full(cfg):
     print(f"{w.name}: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
 
 
-def test_workload3_ring_emulation():
-    """Workload 3: dual-chunk reorder, 4 shards x 4 ring steps with merges,
-    inverse reorder -- against one unsplit oracle attention."""
+@pytest.mark.parametrize("fused", [True, False])
+def test_workload3_ring_emulation(fused):
+    """Workload 3: dual-chunk reorder, 4 shards x 4 ring steps (merged in the
+    forward's epilogue, or by attn_merge), inverse reorder -- against one
+    unsplit oracle attention."""
     w = get(3)
     ids, pos = packed_metadata(w.batch, w.seq_len, w.slots, w.valid_per_slot)
     q, k, v = random_qkv(w.batch, w.seq_len, w.seq_len, w.num_q_heads, w.num_kv_heads,
                          w.head_dim, w.dtype, seed=w.seed)
     o, lse = bosf.ring_forward(*_dev(q, k, v, ids, pos), w.cp_size, w.reorder, w.stripe,
-                               causal=w.causal, window=w.window)
+                               causal=w.causal, window=w.window, fused=fused)
     ro, rl = oracle.attention(q, k, v, ids, pos, ids, pos, causal=w.causal, window=w.window)
     e = compare(o, lse, ro, rl, "bf16", w.name)
-    print(f"{w.name}: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
+    print(f"{w.name} fused={fused}: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
 
 
-@pytest.mark.parametrize("kind,stripe,window,partial", [
-    ("striped", 1, (-1, -1), torch.float32), ("dual_chunk", 1, (700, 0), torch.bfloat16),
-    ("striped", 64, (300, 0), torch.float32)])
-def test_ring_variants(kind, stripe, window, partial):
+@pytest.mark.parametrize("kind,stripe,window,partial,fused", [
+    ("striped", 1, (-1, -1), torch.float32, True), ("striped", 1, (-1, -1), torch.float32, False),
+    ("dual_chunk", 1, (700, 0), torch.bfloat16, True),
+    ("dual_chunk", 1, (700, 0), torch.bfloat16, False),
+    ("striped", 64, (300, 0), torch.float32, True)])
+def test_ring_variants(kind, stripe, window, partial, fused):
     ids, pos = packed_metadata(2, 2048, 4, 400)
     q, k, v = random_qkv(2, 2048, 2048, 16, 2, 128, "bf16", seed=12)
     o, lse = bosf.ring_forward(*_dev(q, k, v, ids, pos), 4, kind, stripe, window=window,
-                               partial_dtype=partial)
+                               partial_dtype=partial, fused=fused)
     ro, rl = oracle.attention(q, k, v, ids, pos, ids, pos, window=window)
-    compare(o, lse, ro, rl, "bf16", f"ring {kind} {stripe}")
+    compare(o, lse, ro, rl, "bf16", f"ring {kind} {stripe} fused={fused}")
+
+
+def _random_partial(b, t, h, d, dtype, seed, empty_frac=0.25):
+    g = torch.Generator().manual_seed(seed)
+    o = torch.randn((b, t, h, d), generator=g).to(dtype)
+    lse = torch.randn((b, t, h), generator=g) * 3
+    empty = torch.rand((b, t, h), generator=g) < empty_frac
+    lse[empty] = -np.inf
+    o[empty] = 0
+    return o, lse
+
+
+@pytest.mark.parametrize("qkv_dt,part_dt,out_dt,in_place", [
+    ("bf16", torch.float32, torch.float32, True), ("bf16", torch.float32, torch.bfloat16, False),
+    ("bf16", torch.bfloat16, torch.bfloat16, True), ("bf16", torch.bfloat16, torch.float32, False),
+    ("f32", torch.float32, torch.float32, True), ("f32", torch.float32, torch.bfloat16, False)])
+def test_accumulate_equals_merge_of_attention_and_partial(qkv_dt, part_dt, out_dt, in_place):
+    """attn_fwd_accumulate = merge(attention over this call's keys, partial)."""
+    rng = np.random.default_rng(7)
+    b, tq, tk, hq, hkv, d = 2, 300, 260, 8, 2, 128
+    q_ids, q_pos = random_layout(rng, b, tq, max_segments=3, pad_prob=0.2)
+    k_ids, k_pos = random_layout(rng, b, tk, max_segments=3, pad_prob=0.2, pos_offset_max=50)
+    q, k, v = random_qkv(b, tq, tk, hq, hkv, d, qkv_dt, seed=8)
+    po, pl = _random_partial(b, tq, hq, d, part_dt, 9)
+    po_d, pl_d = po.to(DEV), pl.to(DEV)
+    kw = dict(window=(40, 0))
+    if in_place:
+        o, lse = bosf.attn_fwd_accumulate(*_dev(q, k, v, q_ids, q_pos, k_ids, k_pos), po_d, pl_d,
+                                          **kw)
+        assert o.data_ptr() == po_d.data_ptr()
+    else:
+        out = torch.empty((b, tq, hq, d), dtype=out_dt, device=DEV)
+        lout = torch.empty((b, tq, hq), device=DEV)
+        o, lse = bosf.attn_fwd_accumulate(*_dev(q, k, v, q_ids, q_pos, k_ids, k_pos), po_d, pl_d,
+                                          out=out, lse=lout, **kw)
+    ao, al = oracle.attention(q, k, v, q_ids, q_pos, k_ids, k_pos, **kw)
+    ro, rl = oracle.merge(ao, al, po, pl)
+    compare(o, lse, ro, rl, "bf16", f"accumulate {qkv_dt} {part_dt}->{out_dt} in_place={in_place}")
+
+
+def test_accumulate_in_place_leaves_untouched_tiles_bit_exact():
+    """Query tiles with nothing visible in this call keep their partial bits."""
+    ids, pos = packed_metadata(1, 512, 1, 512)
+    q, k, v = random_qkv(1, 512, 512, 8, 1, 128, "bf16", seed=4)
+    po, pl = _random_partial(1, 512, 8, 128, torch.float32, 5, empty_frac=0.0)
+    po_d, pl_d = po.to(DEV), pl.to(DEV)
+    # keys are the last 64 positions: query tokens 0..447 see nothing (causal)
+    bosf.attn_fwd_accumulate(*_dev(q, k[:, 448:], v[:, 448:], ids, pos, ids[:, 448:],
+                                   pos[:, 448:]), po_d, pl_d)
+    assert torch.equal(po_d[:, :448].cpu(), po[:, :448])
+    assert torch.equal(pl_d[:, :448].cpu(), pl[:, :448])
+    ao, al = oracle.attention(q, k[:, 448:], v[:, 448:], ids, pos, ids[:, 448:], pos[:, 448:])
+    ro, rl = oracle.merge(ao, al, po, pl)
+    compare(po_d, pl_d, ro, rl, "bf16", "accumulate tail")
 
 
 # --------------------------------------------------------------------------- workloads 4 and 5
