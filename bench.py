@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="ring steps write separate partials folded by attn_merge")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy this many MiB with a plain device copy kernel "
+                         "(a known-size reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the ring is "
@@ -232,6 +235,16 @@ def main():
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
                 "kernel": "attn_fwd (tile classification + bf16 MFMA forward)",
                 "per_launch_flops": per_launch_flops}
+
+    if args.copy_probe_mib > 0:
+        n_el = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n_el, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        detail["copy_probe_bytes_each_way"] = n_el * 4
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -10,8 +10,8 @@
 // Two kernels:
 //  * pack_kv: rewrites every 64-key tile of K and V (per batch row and K/V
 //    head) into a contiguous, LDS-ready block: K as [key][head_dim] and V
-//    transposed as [head_dim][key], 16-byte chunks XOR-swizzled by row so the
-//    MFMA operand reads below are bank-conflict free, plus the tile's segment
+//    transposed as [head_dim][key], 16-byte chunks XOR-swizzled by row (swz) so
+//    the MFMA operand reads below are bank-conflict free, plus the tile's segment
 //    ids and positions; keys past the end are zero.
 //  * forward: workgroup = 8 waves = NH heads of one GQA group x NT sub-tiles
 //    of 32 query tokens (NH * NT = 8).  The packed K, V^T and metadata blocks of
@@ -60,6 +60,17 @@ __device__ __forceinline__ int vt_key(int x) {
   return (x & ~15) + (e < 4 ? 4 * h + e : 8 + 4 * h + (e - 4));
 }
 
+// XOR swizzle of the 16-byte chunks of a packed row.  LDS serves a 16-byte
+// read for 16 lanes per cycle across 256 bytes of banks; the MFMA operand
+// reads have 16 lanes on 16 consecutive rows at the same logical chunk, so the
+// physical chunk is XORed with the row's index among the rows that share one
+// 256-byte bank line.  cpr = 16-byte chunks per row (8 or 16).
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  static_assert(CPR == 8 || CPR == 16, "rows of 128 or 256 bytes");
+  return CPR == 16 ? (chunk ^ (row & 15)) : (chunk ^ ((row >> 1) & 7));
+}
+
 // ----------------------------------------------------------------------------- packing
 
 template <int D>
@@ -80,7 +91,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(PackParams p) {
   for (int u = tid; u < KCH; u += 256) {
     const int r = u / DV, ph = u % DV;
     const int key = kt * BN + r;
-    const int lc = ph ^ (r & 7);
+    const int lc = swz<DV>(r, ph);
     u32x4 val = zero;
     if (key < p.tk) val = *(const u32x4 *)(kb + key * tok + lc * 8);
     *(u32x4 *)(kout + (int64_t)u * 8) = val;
@@ -99,7 +110,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(PackParams p) {
   const uint16_t *vsu = (const uint16_t *)&vs[0][0];
   for (int u = tid; u < D * (BN / 8); u += 256) {
     const int d = u / (BN / 8), ph = u % (BN / 8);
-    const int lc = ph ^ (d & 7);
+    const int lc = swz<BN / 8>(d, ph);
     u32x4 out;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -144,6 +155,11 @@ attn_fwd_bf16_kernel(AttnParams p) {
 
   __shared__ __attribute__((aligned(16))) Tile<D> t0;
   __shared__ __attribute__((aligned(16))) Tile<D> t1;
+  // Epilogue staging: each wave's 32 x 64 slice of O (fp32, rows padded to
+  // 68 floats so the column-wise writes spread over the banks) and the per-row
+  // weight of the running partial.
+  __shared__ __attribute__((aligned(16))) float stage[kWaves][32][68];
+  __shared__ float stage_w[kWaves][32];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -212,7 +228,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
                        8 * half;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      if (qvalid) {
+      if (qvalid && n > 0) {
         qf[c] = *(const bf16x8 *)(qrow + 16 * c);
       } else {
         qf[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
@@ -243,7 +259,6 @@ attn_fwd_bf16_kernel(AttnParams p) {
   float m = kNoMax;  // running max of raw scores q.k
   float z = 0.0f;    // this lane's share of the running sum
   const float c2 = p.scale_log2;
-  const int sw = col & 7;  // XOR swizzle of this lane's LDS rows
 
   // One tile: S^T = K Q^T, mask (boundary tiles only), online softmax, O^T += V^T P^T.
   auto compute = [&](const Tile<D> &tl, bool masked) {
@@ -253,7 +268,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
       const bf16 *krow = tl.k + (kb * 32 + col) * D;
       bf16x8 ka[DC];
 #pragma unroll
-      for (int c = 0; c < DC; ++c) ka[c] = *(const bf16x8 *)(krow + 8 * ((2 * c + half) ^ sw));
+      for (int c = 0; c < DC; ++c) ka[c] = *(const bf16x8 *)(krow + 8 * swz<D / 8>(col, 2 * c + half));
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
 #pragma unroll
@@ -315,7 +330,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
       const bf16 *vrow = tl.vt + (db * 32 + col) * BN;
       bf16x8 va[4];
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) va[ch] = *(const bf16x8 *)(vrow + 8 * ((2 * ch + half) ^ sw));
+      for (int ch = 0; ch < 4; ++ch) va[ch] = *(const bf16x8 *)(vrow + 8 * swz<BN / 8>(col, 2 * ch + half));
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ch], pf[ch], o[db], 0, 0, 0);
@@ -348,56 +363,74 @@ attn_fwd_bf16_kernel(AttnParams p) {
   // Epilogue: O = U / z, LSE = scale * m + ln z; empty rows get 0 and -inf.
   // With a running partial (O_a, L_a): L = log(e^LSE + e^L_a) and
   // O = e^(LSE - L) U / z + e^(L_a - L) O_a.
+  // The wave's O^T fragment goes through LDS in two 64-column halves so that
+  // every global access of O and O_a is a contiguous 16-byte piece of a row.
   const float zt = z + __shfl_xor(z, 32);
-  if (!qvalid) return;
   const bool live = zt > 0.0f;
   const float l_own = live ? p.scale * m + logf(zt) : -INFINITY;
   float w_own = live ? 1.0f / zt : 0.0f;
   float w_acc = 0.0f, l_out = l_own;
-  const int64_t rel = (int64_t)tq * p.hq * D + (int64_t)h * D + 4 * half;
-  if (p.acc_mode) {
+  if (p.acc_mode && qvalid) {
     const float la = p.acc_lse[b * p.acc_lse_bs + (int64_t)tq * p.hq + h];
     l_out = lse_add(l_own, la);
     w_acc = lse_weight(la, l_out);
     w_own = live ? lse_weight(l_own, l_out) / zt : 0.0f;
   }
-  const int64_t obase = b * p.o_bs + rel;
-  const int64_t abase = b * p.acc_o_bs + rel;
+  if (qvalid && half == 0) p.lse[b * p.lse_bs + (int64_t)tq * p.hq + h] = l_out;
+  if (half == 0) stage_w[wave][col] = w_acc;
+
+  const int tq0 = qt * BM + (wave / NH) * 32;   // first query token of this wave
+  const int rsub = lane >> 4;                   // row within a group of 4 rows
+  const int c4 = (lane & 15) * 4;               // first of this lane's 4 columns
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int hd = 0; hd < DB / 2; ++hd) {
+    // fragment columns of db = 2*hd, 2*hd+1 -> stage[wave][query][0..63]
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = db * 32 + 8 * r4;
-      f32x4 val;
-      val[0] = o[db][4 * r4 + 0] * w_own;
-      val[1] = o[db][4 * r4 + 1] * w_own;
-      val[2] = o[db][4 * r4 + 2] * w_own;
-      val[3] = o[db][4 * r4 + 3] * w_own;
-      if (w_acc != 0.0f) {
-        f32x4 a;
-        if (p.acc_mode == 2) {
-          const bf16x4 ah = *(const bf16x4 *)((const bf16 *)p.acc_o + abase + d);
-          a[0] = (float)ah[0];
-          a[1] = (float)ah[1];
-          a[2] = (float)ah[2];
-          a[3] = (float)ah[3];
-        } else {
-          a = *(const f32x4 *)((const float *)p.acc_o + abase + d);
-        }
-        val += w_acc * a;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 val;
+        val[0] = o[2 * hd + j][4 * r4 + 0] * w_own;
+        val[1] = o[2 * hd + j][4 * r4 + 1] * w_own;
+        val[2] = o[2 * hd + j][4 * r4 + 2] * w_own;
+        val[3] = o[2 * hd + j][4 * r4 + 3] * w_own;
+        *(f32x4 *)&stage[wave][col][32 * j + 8 * r4 + 4 * half] = val;
       }
-      if (OUT_BF16) {
-        bf16x4 hv;
-        hv[0] = (bf16)val[0];
-        hv[1] = (bf16)val[1];
-        hv[2] = (bf16)val[2];
-        hv[3] = (bf16)val[3];
-        *(bf16x4 *)((bf16 *)p.o + obase + d) = hv;
-      } else {
-        *(f32x4 *)((float *)p.o + obase + d) = val;
+    // read back 4 rows x 64 columns per pass, 16 bytes per lane
+#pragma unroll
+    for (int pass = 0; pass < 8; ++pass) {
+      const int qrow = 4 * pass + rsub;
+      const int t = tq0 + qrow;
+      f32x4 val = *(const f32x4 *)&stage[wave][qrow][c4];
+      if (t < p.tq) {
+        const int64_t rel = (int64_t)t * p.hq * D + (int64_t)h * D + 64 * hd + c4;
+        const float wa = stage_w[wave][qrow];
+        if (wa != 0.0f) {
+          f32x4 a;
+          if (p.acc_mode == 2) {
+            const bf16x4 ah = *(const bf16x4 *)((const bf16 *)p.acc_o + b * p.acc_o_bs + rel);
+            a[0] = (float)ah[0];
+            a[1] = (float)ah[1];
+            a[2] = (float)ah[2];
+            a[3] = (float)ah[3];
+          } else {
+            a = *(const f32x4 *)((const float *)p.acc_o + b * p.acc_o_bs + rel);
+          }
+          val += wa * a;
+        }
+        if (OUT_BF16) {
+          bf16x4 hv;
+          hv[0] = (bf16)val[0];
+          hv[1] = (bf16)val[1];
+          hv[2] = (bf16)val[2];
+          hv[3] = (bf16)val[3];
+          *(bf16x4 *)((bf16 *)p.o + b * p.o_bs + rel) = hv;
+        } else {
+          *(f32x4 *)((float *)p.o + b * p.o_bs + rel) = val;
+        }
       }
     }
-  if (half == 0) p.lse[b * p.lse_bs + (int64_t)tq * p.hq + h] = l_out;
+  }
 }
 
 template <int D, int NT>
