@@ -79,6 +79,28 @@ class EventLog:
         return [a.elapsed_time(b) for a, b in self.done.get(name, [])]
 
 
+def measured_traffic():
+    """HBM bytes per attn_fwd launch from the committed rocprofv3 counter runs.
+
+    ``profiles/attn_fwd_longctx_ring4_traffic.json`` records FETCH_SIZE and
+    WRITE_SIZE summed over the forward's launches of one step, already scaled
+    by the factors a plain copy kernel of known size gave, together with the
+    SHA-256 of the forward kernel's source at the time; if the kernel has
+    changed since, the figure no longer applies and None is returned.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_longctx_ring4_traffic.json")
+    src = os.path.join(ROOT, "blockwise_online_softmax_fwd_amd", "csrc", "attn_bf16.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def cpu_baseline(w, q, k, v, ids, pos, budget_s):
     """Oracle (fp64, host) on a bounded random row sample of the same inputs."""
     import oracle
@@ -232,7 +254,8 @@ def main():
                        "attn_merge_bytes_per_call": mbytes})
         del pa, pb, la, lb, outm, outl
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic() if args.workload == 5 else None,
                 "kernel": "attn_fwd (tile classification + bf16 MFMA forward)",
                 "per_launch_flops": per_launch_flops}
 

@@ -263,17 +263,30 @@ attn_fwd_bf16_kernel(AttnParams p) {
   // One tile: S^T = K Q^T, mask (boundary tiles only), online softmax, O^T += V^T P^T.
   auto compute = [&](const Tile<D> &tl, bool masked) {
     f32x16 s[2];
+    {
+      bf16x8 ka0[DC], ka1[DC];
+      const bf16 *krow0 = tl.k + col * D, *krow1 = tl.k + (32 + col) * D;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16 *krow = tl.k + (kb * 32 + col) * D;
-      bf16x8 ka[DC];
+      for (int c = 0; c < DC; ++c) ka0[c] = *(const bf16x8 *)(krow0 + 8 * swz<D / 8>(col, 2 * c + half));
 #pragma unroll
-      for (int c = 0; c < DC; ++c) ka[c] = *(const bf16x8 *)(krow + 8 * swz<D / 8>(col, 2 * c + half));
+      for (int c = 0; c < DC; ++c) ka1[c] = *(const bf16x8 *)(krow1 + 8 * swz<D / 8>(col, 2 * c + half));
+      const f32x16 zero16 = {};
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[0], qf[0], zero16, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+      for (int c = 1; c < DC; ++c)
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[c], qf[c], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1[0], qf[0], zero16, 0, 0, 0);
 #pragma unroll
-      for (int c = 0; c < DC; ++c)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[c], s[kb], 0, 0, 0);
+      for (int c = 1; c < DC; ++c)
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1[c], qf[c], s[1], 0, 0, 0);
+      // all of block 0's operand reads first, then block 1's reads one per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, DC, 0);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, DC, 0);
     }
     if (masked) {
 #pragma unroll
@@ -290,6 +303,14 @@ attn_fwd_bf16_kernel(AttnParams p) {
         }
     }
 
+    // V^T operands of this tile: issued now, consumed after the exps.
+    bf16x8 va[DB][4];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16 *vrow = tl.vt + (db * 32 + col) * BN;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) va[db][ch] = *(const bf16x8 *)(vrow + 8 * swz<BN / 8>(col, 2 * ch + half));
+    }
     // Row max over this tile (the lane's 32 keys, then the other half's).
     float mx = s[0][0];
 #pragma unroll
@@ -324,17 +345,13 @@ attn_fwd_bf16_kernel(AttnParams p) {
       }
     z += zs;
 
-    // O^T += V^T P^T over the four 16-key chunks.
+    // O^T += V^T P^T, chunk by chunk so chunk ch's MFMAs can start while the
+    // exps of chunk ch+1 are still running.
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const bf16 *vrow = tl.vt + (db * 32 + col) * BN;
-      bf16x8 va[4];
+    for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) va[ch] = *(const bf16x8 *)(vrow + 8 * swz<BN / 8>(col, 2 * ch + half));
-#pragma unroll
-      for (int ch = 0; ch < 4; ++ch)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ch], pf[ch], o[db], 0, 0, 0);
-    }
+      for (int db = 0; db < DB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][ch], pf[ch], o[db], 0, 0, 0);
   };
 
   // Double-buffered loop, unrolled by two so each half names its LDS buffer
