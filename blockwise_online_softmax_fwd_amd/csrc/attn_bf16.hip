@@ -127,6 +127,21 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(PackParams p) {
 // Branch-free visibility test of one key against the lane's query.  With
 // non-negative ids and positions, the pair is visible iff kid == qkey (qkey is
 // -1 for a padding query) and lo <= qpos - kpos <= hi.
+// Largest of x over lanes l and l ^ 32 (the two halves of a query's keys),
+// exchanged with v_permlane32_swap rather than through LDS.
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+}
+
+// Sum of x over lanes l and l ^ 32.
+__device__ __forceinline__ float pair_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
+}
+
 struct LaneMask {
   int qkey, qpos, lo, hi;
   __device__ __forceinline__ bool operator()(int kid, int kpos) const {
@@ -317,7 +332,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max(mx);
     const bool raise = (mx - m) * c2 > kRescaleLog2;
     if (__ballot(raise)) {
       if (raise) {
@@ -382,7 +397,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
   // O = e^(LSE - L) U / z + e^(L_a - L) O_a.
   // The wave's O^T fragment goes through LDS in two 64-column halves so that
   // every global access of O and O_a is a contiguous 16-byte piece of a row.
-  const float zt = z + __shfl_xor(z, 32);
+  const float zt = pair_sum(z);
   const bool live = zt > 0.0f;
   const float l_own = live ? p.scale * m + logf(zt) : -INFINITY;
   float w_own = live ? 1.0f / zt : 0.0f;
