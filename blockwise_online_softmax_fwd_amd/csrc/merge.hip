@@ -11,7 +11,8 @@
 //
 // HBM-bound: each (batch, token, head) row reads two D-vectors and two LSE
 // values and writes one D-vector and one LSE.  One thread moves 4 consecutive
-// elements (16 bytes of fp32 or 8 of bf16); D/4 threads share a row.
+// elements (16 bytes of fp32 or 8 of bf16); D/4 threads share a row, and a
+// thread issues the loads of four rows before it combines any of them.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -53,38 +54,47 @@ __device__ __forceinline__ void store4(void *base, int64_t off, f32x4 v) {
 
 template <int D, bool ABF, bool BBF, bool OBF>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  constexpr int TPR = D / 4;  // threads per row
+  constexpr int TPR = D / 4;        // threads per row
+  constexpr int RPB = 256 / TPR;    // rows per block and step
+  constexpr int U = 4;              // rows per thread per iteration, loads issued together
   const int64_t rows_per_batch = (int64_t)p.seq * p.heads;
   const int64_t total = rows_per_batch * p.batch;
   const int sub = threadIdx.x % TPR;
-  const int64_t stride = (int64_t)gridDim.x * (256 / TPR);
-  for (int64_t r = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR; r < total; r += stride) {
-    const int64_t b = r / rows_per_batch;
-    const int64_t rr = r - b * rows_per_batch;
-    const float la = p.la[b * p.la_bs + rr];
-    const float lb = p.lb[b * p.lb_bs + rr];
-    const int64_t col = rr * D + sub * 4;
-    f32x4 out;
-    float lo;
-    if (la == -INFINITY && lb == -INFINITY) {
-      out = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      lo = -INFINITY;
-    } else if (lb == -INFINITY) {
-      out = load4<ABF>(p.oa, b * p.oa_bs + col);
-      lo = la;
-    } else if (la == -INFINITY) {
-      out = load4<BBF>(p.ob, b * p.ob_bs + col);
-      lo = lb;
-    } else {
-      const float mx = fmaxf(la, lb);
-      lo = mx + log1pf(expf(-fabsf(la - lb)));
-      const float wa = expf(la - lo), wb = expf(lb - lo);
-      const f32x4 a = load4<ABF>(p.oa, b * p.oa_bs + col);
-      const f32x4 c = load4<BBF>(p.ob, b * p.ob_bs + col);
-      out = wa * a + wb * c;
+  const int64_t step = (int64_t)gridDim.x * RPB * U;
+  for (int64_t r0 = (int64_t)blockIdx.x * RPB * U + threadIdx.x / TPR; r0 < total; r0 += step) {
+    float la[U], lb[U];
+    f32x4 a[U], c[U];
+    int64_t bb[U], rr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = r0 + (int64_t)u * RPB;
+      bb[u] = r / rows_per_batch;
+      rr[u] = r - bb[u] * rows_per_batch;
+      if (r < total) {
+        la[u] = p.la[bb[u] * p.la_bs + rr[u]];
+        lb[u] = p.lb[bb[u] * p.lb_bs + rr[u]];
+        const int64_t col = rr[u] * D + sub * 4;
+        a[u] = load4<ABF>(p.oa, bb[u] * p.oa_bs + col);
+        c[u] = load4<BBF>(p.ob, bb[u] * p.ob_bs + col);
+      }
     }
-    store4<OBF>(p.oo, b * p.oo_bs + col, out);
-    if (sub == 0) p.lo[b * p.lo_bs + rr] = lo;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = r0 + (int64_t)u * RPB;
+      if (r >= total) break;
+      // A side at -inf contributes nothing and its O is never read into the
+      // result (select, not multiply), so an empty row is the identity.
+      const bool ea = la[u] == -INFINITY, eb = lb[u] == -INFINITY;
+      const float mx = fmaxf(la[u], lb[u]);
+      float lo = mx + log1pf(expf(-fabsf(la[u] - lb[u])));
+      const float wa = expf(la[u] - lo), wb = expf(lb[u] - lo);
+      f32x4 out = wa * a[u] + wb * c[u];
+      if (eb) { out = a[u]; lo = la[u]; }
+      if (ea) { out = c[u]; lo = lb[u]; }
+      if (ea && eb) { out = f32x4{0.0f, 0.0f, 0.0f, 0.0f}; lo = -INFINITY; }
+      store4<OBF>(p.oo, bb[u] * p.oo_bs + rr[u] * D + sub * 4, out);
+      if (sub == 0) p.lo[bb[u] * p.lo_bs + rr[u]] = lo;
+    }
   }
 }
 
@@ -92,7 +102,7 @@ template <int D, bool ABF, bool BBF, bool OBF>
 hipError_t launch4(const MergeParams &p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.batch * p.seq * p.heads;
   if (rows == 0) return hipSuccess;
-  constexpr int RPB = 256 / (D / 4);
+  constexpr int RPB = 256 / (D / 4) * 4;  // rows per block and iteration
   int64_t blocks = (rows + RPB - 1) / RPB;
   const int64_t cap = 256 * 64;  // enough blocks to fill 256 CUs many times over
   if (blocks > cap) blocks = cap;
