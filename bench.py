@@ -20,6 +20,7 @@ times the fp64 oracle on a bounded row sample of the same inputs.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -141,6 +142,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="ring steps write separate partials folded by attn_merge")
+    ap.add_argument("--strategy", choices=("ring", "allgather"), default="ring",
+                    help="context-parallel strategy of the sharded workloads: ring steps with "
+                         "partials, or each shard against the whole gathered K/V (striped)")
+    ap.add_argument("--stripe", type=int, default=512,
+                    help="stripe size of the all-gather strategy's striped reorder")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy this many MiB with a plain device copy kernel "
                          "(a known-size reference for hardware byte counters)")
@@ -154,8 +160,16 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     w = get(args.workload)
+    allgather = args.strategy == "allgather" and w.cp_size > 1
+    if allgather:
+        w = dataclasses.replace(w, reorder="striped", stripe=args.stripe)
     bosf.load_library()
-    log(f"workload {w.cfg} {w.name}: {w.describe()}")
+    desc = w.describe()
+    if allgather:
+        desc = desc.replace(f"{w.cp_size} shards x {w.cp_size} ring steps",
+                            f"{w.cp_size} shards (stripe {w.stripe}), each against the whole "
+                            "gathered K/V in one call")
+    log(f"workload {w.cfg} {w.name}: {desc}")
     q, k, v, ids, pos = make_inputs(w, dev)
 
     # Work of one step: visible pairs of the unsplit problem, counted by the
@@ -169,7 +183,14 @@ def main():
     log(f"visible pairs {visible}, {flops / 1e12:.3f} TFLOP per step")
 
     ev = EventLog()
-    if w.cp_size > 1:
+    if allgather:
+        bufs = bosf.RingBuffers.like(q, k, ids, w.cp_size, partials=False)
+
+        def step():
+            bosf.allgather_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe,
+                                   causal=w.causal, window=w.window, bufs=bufs,
+                                   step_hook=ev.hook)
+    elif w.cp_size > 1:
         bufs = bosf.RingBuffers.like(q, k, ids, w.cp_size)
 
         def step():
@@ -221,8 +242,9 @@ def main():
         fwd_bytes = 2 * (q.numel() * 2 + 2 * k.numel() * 2 + 2 * ids.numel() * 4)
         inv_bytes = 2 * (q.numel() * 2 + b * t * hq * 4)
         detail.update({
-            "ring_merge": "unfused: attn_merge per step" if args.unfused
-                          else "fused into attn_fwd_accumulate epilogues",
+            "strategy": ("all-gather: each shard against the whole K/V, no merge" if allgather
+                         else "ring: unfused, attn_merge per step" if args.unfused
+                         else "ring: merges fused into attn_fwd_accumulate epilogues"),
             "reorder_ms_per_step": reorder_ms,
             "reorder_GBs": fwd_bytes / (reorder_ms / 1000.0) / 1e9,
             "inverse_reorder_ms_per_step": inv_ms,
@@ -255,7 +277,8 @@ def main():
         del pa, pb, la, lb, outm, outl
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic() if args.workload == 5 else None,
+                "traffic": (measured_traffic() if args.workload == 5 and not allgather
+                            and not args.unfused else None),
                 "kernel": "attn_fwd (tile classification + bf16 MFMA forward)",
                 "per_launch_flops": per_launch_flops}
 
@@ -288,10 +311,12 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
-        "config": {"workload": f"{w.name}: {w.describe()}", "batch": w.batch,
+        "config": {"workload": f"{w.name}{' all-gather' if allgather else ''}: {desc}",
+                   "batch": w.batch,
                    "seq_len": w.seq_len, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                   "window": list(w.window), "cp_shards": w.cp_size, "reorder": w.reorder},
+                   "window": list(w.window), "cp_shards": w.cp_size, "reorder": w.reorder,
+                   "stripe": w.stripe, "strategy": "allgather" if allgather else "ring"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "detail": detail,

@@ -11,6 +11,13 @@ loop the sequence is permuted for causal load balance and cut into R shards
 (TransformerEngine JAX tutorial, section 4); afterwards the output and the LSE
 are permuted back.  Every step is a call into libringattn; this module only
 slices views and orders the calls.
+
+The all-gather strategy (TransformerEngine JAX tutorial, sections 4 and 5;
+"Context parallelism and ring attention", "Communication choices") is the
+other per-device computation: each rank keeps its query shard of the
+striped reorder and attends, in a single call, to the whole gathered K/V (in
+reordered order; the mask works on segment ids and positions, so the order
+of the keys does not matter).  No partials, no merge.
 """
 
 from __future__ import annotations
@@ -39,9 +46,9 @@ class RingBuffers:
     workspace: torch.Tensor | None = None
 
     @classmethod
-    def like(cls, q, k, ids, cp_size, partial_dtype=torch.float32, out_dtype=None):
+    def like(cls, q, k, ids, cp_size, partial_dtype=torch.float32, out_dtype=None, partials=True):
         b, t, hq, d = q.shape
-        n = t // cp_size
+        n = t // cp_size if partials else 0
         dev = q.device
         od = q.dtype if out_dtype is None else out_dtype
         return cls(
@@ -161,6 +168,51 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     for r in (range(cp_size) if ranks is None else ranks):
         rank_steps(r, cp_size, bufs, scale=scale, causal=causal, window=window, step_hook=step_hook,
                    fused=fused)
+    if step_hook:
+        step_hook("inverse_reorder", -1, -1, True)
+    o = ra.inverse_reorder(bufs.o, cp_size, kind, stripe_size)
+    lse = ra.inverse_reorder(bufs.lse, cp_size, kind, stripe_size)
+    if step_hook:
+        step_hook("inverse_reorder", -1, -1, False)
+    return o, lse
+
+
+def allgather_forward(q, k, v, ids, pos, cp_size, kind="striped", stripe_size=512, *, scale=None,
+                      causal=True, window=(-1, -1), ranks=None, bufs: RingBuffers | None = None,
+                      out_dtype=None, step_hook=None):
+    """All-gather context-parallel forward of self-attention inputs on one GPU.
+
+    The inputs are reordered (striped by default, as the tutorial's
+    all-gather run with stripe_size 512), every rank's query shard attends to
+    the full reordered K/V in one ``attn_fwd`` call, and O and the LSE are
+    permuted back.  Shapes and return value as :func:`ring_forward`.
+    """
+    if q.shape[1] != k.shape[1]:
+        raise ValueError("the all-gather driver runs self-attention (Tq == Tk)")
+    b, t = ids.shape
+    n = t // cp_size
+    if bufs is None:
+        bufs = RingBuffers.like(q, k, ids, cp_size, out_dtype=out_dtype, partials=False)
+    if bufs.workspace is None:
+        desc = ra.make_desc(b, n, t, q.shape[2], k.shape[2], q.shape[3],
+                            ra._dtype_code(q.dtype), None, scale, causal, window)
+        bufs.workspace = torch.empty(max(1, ra.workspace_size(desc)), dtype=torch.uint8,
+                                     device=q.device)
+    if step_hook:
+        step_hook("reorder", -1, -1, True)
+    reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs)
+    if step_hook:
+        step_hook("reorder", -1, -1, False)
+    for r in (range(cp_size) if ranks is None else ranks):
+        rows = slice(r * n, (r + 1) * n)
+        if step_hook:
+            step_hook("attn_fwd", r, 0, True)
+        ra.attn_fwd(bufs.q[:, rows], bufs.k, bufs.v, bufs.ids[:, rows], bufs.pos[:, rows],
+                    bufs.ids, bufs.pos, scale=scale, causal=causal, window=window,
+                    out_dtype=bufs.o.dtype, out=bufs.o[:, rows], lse=bufs.lse[:, rows],
+                    workspace=bufs.workspace)
+        if step_hook:
+            step_hook("attn_fwd", r, 0, False)
     if step_hook:
         step_hook("inverse_reorder", -1, -1, True)
     o = ra.inverse_reorder(bufs.o, cp_size, kind, stripe_size)

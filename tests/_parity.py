@@ -4,7 +4,8 @@ Bar for bf16 inputs: max |O_gpu - O_ref| <= 2e-2 and max |LSE_gpu - LSE_ref|
 <= 1e-3 over rows with a visible key; -inf in exactly the same LSE entries
 (rows with no visible key), where O must be exactly 0; no NaN or Inf
 anywhere else.  fp32 inputs are held to a tighter bar derived from fp32
-rounding: 1e-4 on O and 1e-4 on LSE.
+rounding: the length-D dot products and a sum over at most Tk terms stay
+below 1e-5 relative at these sizes, so 1e-4 on O and on LSE leaves margin.
 """
 
 import numpy as np

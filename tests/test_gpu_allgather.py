@@ -1,0 +1,109 @@
+"""GPU parity of the all-gather context-parallel forward against the fp64 oracle.
+
+Each rank's query shard of the striped reorder attends to the whole
+(reordered) K/V in one call; the result, permuted back, must equal plain
+attention over the original order.  Small cases cover several stripe sizes
+and windows; the full-size case is the long-context workload's shape with the
+tutorial's all-gather stripe size of 512, checked on sampled rows and, via
+Q = 0, on every row.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_online_softmax_fwd_amd as bosf
+import oracle
+from _parity import compare
+from _workload_io import closed_form_counts, device_inputs, sample_rows
+from workloads import get, packed_metadata, random_qkv
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bosf.load_library()
+
+
+def _dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+@pytest.mark.parametrize("stripe,window,cp", [(1, (-1, -1), 4), (64, (256, 0), 4), (512, (-1, -1), 2),
+                                              (32, (300, 0), 8)])
+def test_allgather_small(stripe, window, cp):
+    ids, pos = packed_metadata(2, 4096, 4, 700)
+    q, k, v = random_qkv(2, 4096, 4096, 16, 2, 128, "bf16", seed=21)
+    o, lse = bosf.allgather_forward(*_dev(q, k, v, ids, pos), cp, "striped", stripe, window=window)
+    ro, rl = oracle.attention(q, k, v, ids, pos, ids, pos, window=window)
+    compare(o, lse, ro, rl, "bf16", f"all-gather striped({stripe}) cp{cp} window {window}")
+
+
+def test_allgather_dual_chunk_and_subset_of_ranks():
+    """Any reorder works; ranks not run leave their shard of the buffers as it was."""
+    ids, pos = packed_metadata(1, 2048, 2, 900)
+    q, k, v = random_qkv(1, 2048, 2048, 8, 8, 64, "bf16", seed=22)
+    qd, kd, vd, idd, pod = _dev(q, k, v, ids, pos)
+    o, lse = bosf.allgather_forward(qd, kd, vd, idd, pod, 4, "dual_chunk", 1, window=(100, 0))
+    ro, rl = oracle.attention(q, k, v, ids, pos, ids, pos, window=(100, 0))
+    compare(o, lse, ro, rl, "bf16", "all-gather dual chunk")
+    bufs = bosf.RingBuffers.like(qd, kd, idd, 4, partials=False)
+    bufs.o.fill_(7.0)
+    o2, _ = bosf.allgather_forward(qd, kd, vd, idd, pod, 4, "dual_chunk", 1, window=(100, 0),
+                                   ranks=[1], bufs=bufs)
+    n = 2048 // 4
+    assert torch.equal(bufs.o[:, n:2 * n], o2[:, oracle.reorder_map(2048, 4, "dual_chunk", 1)[n:2 * n]])
+    assert (bufs.o[:, :n] == 7.0).all() and (bufs.o[:, 2 * n:] == 7.0).all()
+
+
+def _longctx_allgather():
+    return dataclasses.replace(get(5), reorder="striped", stripe=512)
+
+
+def test_allgather_full_size_sampled():
+    """The long-context workload under all-gather CP (striped 512, 4 ranks):
+    sampled rows (segment starts, window edges, padding, stripe and shard
+    boundaries, random) against the oracle, every head."""
+    w = _longctx_allgather()
+    q, k, v, ids, pos = device_inputs(w)
+    o, lse = bosf.allgather_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe,
+                                    causal=w.causal, window=w.window)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(55)
+    left = w.window[0]
+    edges = [0, 1, 63, 64, 511, 512, 513, left - 1, left, left + 1, w.valid_per_slot - 1,
+             w.valid_per_slot, w.slot_len - 1]
+    rows = sample_rows(w, rng, edges)
+    m = oracle.reorder_map(w.seq_len, w.cp_size, w.reorder, w.stripe)
+    n = w.seq_len // w.cp_size
+    for r in range(1, w.cp_size):
+        for p in (r * n - 1, r * n):
+            rows.append((1, int(m[p])))
+    ro, rl = oracle.attention_rows(q, k.cpu(), v.cpu(), ids.cpu(), pos.cpu(), ids.cpu(), pos.cpu(),
+                                   rows, causal=w.causal, window=w.window)
+    bi = torch.tensor([r[0] for r in rows])
+    ti = torch.tensor([r[1] for r in rows])
+    e = compare(o[bi, ti], lse[bi, ti], ro, rl, "bf16", "all-gather long context")
+    print(f"all-gather long context: {len(rows)} rows x {w.num_q_heads} heads: "
+          f"max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
+
+
+def test_allgather_full_size_zero_queries_every_row():
+    """Q = 0 at full size: LSE = ln(visible keys) on every row and head."""
+    w = _longctx_allgather()
+    q, k, v, ids, pos = device_inputs(w, zero_q=True)
+    o, lse = bosf.allgather_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe,
+                                    causal=w.causal, window=w.window)
+    nvis = closed_form_counts(w, pos, ids)
+    ref = torch.where(nvis > 0, torch.log(nvis), torch.full_like(nvis, -np.inf))
+    got = lse.to(torch.float64)
+    live = nvis > 0
+    assert torch.equal(torch.isneginf(got), ~live[:, :, None].expand_as(got))
+    err = (got - ref[:, :, None])[live[:, :, None].expand_as(got)].abs().max().item()
+    assert err <= 1e-5, err
+    assert (o[~live] == 0).all()

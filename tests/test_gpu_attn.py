@@ -15,6 +15,7 @@ import torch
 import blockwise_online_softmax_fwd_amd as bosf
 import oracle
 from _parity import compare, to64
+from _workload_io import closed_form_counts, device_inputs, sample_rows
 from workloads import get, packed_metadata, random_layout, random_qkv
 
 pytestmark = pytest.mark.gpu
@@ -246,34 +247,6 @@ def test_accumulate_in_place_leaves_untouched_tiles_bit_exact():
 
 # --------------------------------------------------------------------------- workloads 4 and 5
 
-def _sample_rows(w, rng, extra_positions, n_random=64):
-    rows = set()
-    for b in range(w.batch):
-        for s in range(w.slots):
-            base = s * w.slot_len
-            for p in extra_positions:
-                if 0 <= p < w.slot_len:
-                    rows.add((b, base + p))
-    for _ in range(n_random):
-        rows.add((int(rng.integers(w.batch)), int(rng.integers(w.seq_len))))
-    return sorted(rows)
-
-
-def _device_inputs(w, zero_q=False, uniform_v=None):
-    g = torch.Generator(device=DEV)
-    g.manual_seed(w.seed)
-    dt = torch.bfloat16
-    q = torch.randn((w.batch, w.seq_len, w.num_q_heads, w.head_dim), generator=g, device=DEV).to(dt)
-    k = torch.randn((w.batch, w.seq_len, w.num_kv_heads, w.head_dim), generator=g, device=DEV).to(dt)
-    v = torch.randn((w.batch, w.seq_len, w.num_kv_heads, w.head_dim), generator=g, device=DEV).to(dt)
-    if zero_q:
-        q.zero_()
-    if uniform_v is not None:
-        v.copy_(uniform_v.to(DEV, dt)[None, None].expand_as(v))
-    ids, pos = packed_metadata(w.batch, w.seq_len, w.slots, w.valid_per_slot)
-    return q, k, v, ids.to(DEV), pos.to(DEV)
-
-
 def _run_workload(w, q, k, v, ids, pos):
     if w.cp_size > 1:
         return bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe,
@@ -287,14 +260,14 @@ def test_workload_full_size_sampled(cfg):
     (segment starts, window edges, padding, shard boundaries, random) against
     the oracle, every head."""
     w = get(cfg)
-    q, k, v, ids, pos = _device_inputs(w)
+    q, k, v, ids, pos = device_inputs(w)
     o, lse = _run_workload(w, q, k, v, ids, pos)
     torch.cuda.synchronize()
     rng = np.random.default_rng(cfg)
     left = w.window[0]
     edges = [0, 1, 2, 31, 32, 63, 64, left - 1, left, left + 1, left + 2,
              w.valid_per_slot - 1, w.valid_per_slot, w.slot_len - 1]
-    rows = _sample_rows(w, rng, edges)
+    rows = sample_rows(w, rng, edges)
     if w.cp_size > 1:  # rows on both sides of every shard boundary after reordering
         m = oracle.reorder_map(w.seq_len, w.cp_size, w.reorder, w.stripe)
         n = w.seq_len // w.cp_size
@@ -311,21 +284,14 @@ def test_workload_full_size_sampled(cfg):
           f"max|dLSE|={e[1]:.2e}")
 
 
-def _closed_form_counts(w, pos_row, ids_row):
-    """Visible keys of each query on the packed layouts: min(pos+1, left+1)."""
-    p = pos_row.to(torch.float64)
-    n = p + 1 if w.window[0] < 0 else torch.clamp(p + 1, max=w.window[0] + 1)
-    return torch.where(ids_row != 0, n, torch.zeros_like(n))
-
-
 @pytest.mark.parametrize("cfg", [2, 4, 5])
 def test_workload_zero_queries_every_row(cfg):
     """Q = 0: every row's LSE is ln(visible keys), known in closed form for
     every row at full size; padding rows are -inf."""
     w = get(cfg)
-    q, k, v, ids, pos = _device_inputs(w, zero_q=True)
+    q, k, v, ids, pos = device_inputs(w, zero_q=True)
     o, lse = _run_workload(w, q, k, v, ids, pos)
-    n = _closed_form_counts(w, pos, ids)                 # [B, T]
+    n = closed_form_counts(w, pos, ids)                 # [B, T]
     ref = torch.where(n > 0, torch.log(n), torch.full_like(n, -np.inf))
     got = lse.to(torch.float64)
     live = n > 0
@@ -341,7 +307,7 @@ def test_workload_uniform_v_every_row(cfg):
     w = get(cfg)
     c = torch.randn((w.num_kv_heads, w.head_dim), generator=torch.Generator().manual_seed(1))
     c = c.to(torch.bfloat16)
-    q, k, v, ids, pos = _device_inputs(w, uniform_v=c)
+    q, k, v, ids, pos = device_inputs(w, uniform_v=c)
     o, lse = _run_workload(w, q, k, v, ids, pos)
     ref = c.to(DEV, torch.float32).repeat_interleave(w.group, dim=0)   # [Hq, D]
     live = ids != 0
