@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="ring steps write separate partials folded by attn_merge")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="launch every ring step, also those whose blocks hold no visible pair")
     ap.add_argument("--strategy", choices=("ring", "allgather"), default="ring",
                     help="context-parallel strategy of the sharded workloads: ring steps with "
                          "partials, or each shard against the whole gathered K/V (striped)")
@@ -192,11 +194,21 @@ def main():
                                    step_hook=ev.hook)
     elif w.cp_size > 1:
         bufs = bosf.RingBuffers.like(q, k, ids, w.cp_size)
+        # The ring schedule of this segment layout (visible pairs per rank and
+        # step), computed once outside the timed region like the layout itself;
+        # steps whose blocks hold no visible pair are then not launched.
+        plan = None
+        if not args.no_plan and not args.unfused:
+            plan = bosf.ring_plan(ids, pos, w.cp_size, w.reorder, w.stripe,
+                                  num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                                  head_dim=w.head_dim, dtype=q.dtype, causal=w.causal,
+                                  window=w.window)
+            log(f"ring plan (visible pairs per rank x step): {plan.tolist()}")
 
         def step():
             bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe, causal=w.causal,
                               window=w.window, bufs=bufs, step_hook=ev.hook,
-                              fused=not args.unfused)
+                              fused=not args.unfused, plan=plan)
     else:
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
@@ -244,7 +256,9 @@ def main():
         detail.update({
             "strategy": ("all-gather: each shard against the whole K/V, no merge" if allgather
                          else "ring: unfused, attn_merge per step" if args.unfused
-                         else "ring: merges fused into attn_fwd_accumulate epilogues"),
+                         else "ring: merges fused into attn_fwd_accumulate epilogues, "
+                              + ("every step launched" if args.no_plan
+                                 else "steps without visible pairs skipped")),
             "reorder_ms_per_step": reorder_ms,
             "reorder_GBs": fwd_bytes / (reorder_ms / 1000.0) / 1e9,
             "inverse_reorder_ms_per_step": inv_ms,
@@ -278,7 +292,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": (measured_traffic() if args.workload == 5 and not allgather
-                            and not args.unfused else None),
+                            and not args.unfused and not args.no_plan else None),
                 "kernel": "attn_fwd (tile classification + bf16 MFMA forward)",
                 "per_launch_flops": per_launch_flops}
 

@@ -26,4 +26,4 @@ from .ringattn import (  # noqa: F401
     version,
     workspace_size,
 )
-from .ring import RingBuffers, allgather_forward, ring_forward  # noqa: F401
+from .ring import RingBuffers, allgather_forward, ring_forward, ring_plan  # noqa: F401

@@ -72,7 +72,7 @@ def reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs: RingBuff
 
 
 def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, window=(-1, -1),
-               step_hook=None, fused=True):
+               step_hook=None, fused=True, steps=None):
     """Rank ``rank``'s R ring steps on the reordered buffers; the merged result
     lands in rank's shard of ``bufs.o`` / ``bufs.lse`` (reordered order).
 
@@ -81,7 +81,7 @@ def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, win
     the fp32 partial, the last step writing the final output); otherwise every
     step writes its own partial and ``attn_merge`` folds it in."""
     if fused:
-        return _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook)
+        return _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, steps)
     t = bufs.q.shape[1]
     n = t // cp_size
     rows = slice(rank * n, (rank + 1) * n)
@@ -114,22 +114,23 @@ def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, win
             step_hook("attn_merge", rank, s, False)
 
 
-def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook):
+def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, steps=None):
     t = bufs.q.shape[1]
     n = t // cp_size
     rows = slice(rank * n, (rank + 1) * n)
     q_r, id_r, pos_r = bufs.q[:, rows], bufs.ids[:, rows], bufs.pos[:, rows]
     o_r, lse_r = bufs.o[:, rows], bufs.lse[:, rows]
-    for s in range(cp_size):
+    steps = list(range(cp_size)) if steps is None else steps
+    for i, s in enumerate(steps):
         c = (rank - s) % cp_size
         cols = slice(c * n, (c + 1) * n)
         args = (q_r, bufs.k[:, cols], bufs.v[:, cols], id_r, pos_r, bufs.ids[:, cols],
                 bufs.pos[:, cols])
-        last = s == cp_size - 1
+        last = i == len(steps) - 1
         dst, dst_lse = (o_r, lse_r) if last else (bufs.acc, bufs.acc_lse)
         if step_hook:
             step_hook("attn_fwd", rank, s, True)
-        if s == 0:
+        if i == 0:
             ra.attn_fwd(*args, scale=scale, causal=causal, window=window, out_dtype=dst.dtype,
                         out=dst, lse=dst_lse, workspace=bufs.workspace)
         else:
@@ -139,15 +140,47 @@ def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook):
             step_hook("attn_fwd", rank, s, False)
 
 
+def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_heads, num_kv_heads,
+              head_dim=128, dtype=torch.bfloat16, causal=True, window=(-1, -1)):
+    """Visible pairs of every ring step on this segment layout, ``int64 [R, R]``
+    on the host (rank, step), from the library's tile classification.
+
+    The counts depend only on the segment ids and positions, so one plan
+    serves every forward on the same layout.  A block with no visible pair
+    contributes nothing to its rank's softmax ("Causal attention": such blocks
+    are skipped), so :func:`ring_forward` given the plan runs only the steps
+    with work and lets the last of them write the final output.
+    """
+    b, t = ids.shape
+    n = t // cp_size
+    ids_r = ra.reorder(ids, cp_size, kind, stripe_size)
+    pos_r = ra.reorder(pos, cp_size, kind, stripe_size)
+    plan = torch.zeros((cp_size, cp_size), dtype=torch.int64)
+    for r in range(cp_size):
+        rows = slice(r * n, (r + 1) * n)
+        for s in range(cp_size):
+            c = (r - s) % cp_size
+            cols = slice(c * n, (c + 1) * n)
+            _, pairs = ra.classify_tiles(ids_r[:, rows], pos_r[:, rows], ids_r[:, cols],
+                                         pos_r[:, cols], num_q_heads=num_q_heads,
+                                         num_kv_heads=num_kv_heads, head_dim=head_dim,
+                                         dtype=dtype, causal=causal, window=window)
+            plan[r, s] = int(pairs.sum().item())
+    return plan
+
+
 def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, scale=None,
                  causal=True, window=(-1, -1), ranks=None, bufs: RingBuffers | None = None,
-                 partial_dtype=torch.float32, out_dtype=None, step_hook=None, fused=True):
+                 partial_dtype=torch.float32, out_dtype=None, step_hook=None, fused=True,
+                 plan=None):
     """Ring-decomposed attention forward of self-attention inputs on one GPU.
 
     q ``[B,T,Hq,D]``, k/v ``[B,T,Hkv,D]``, ids/pos ``int32 [B,T]`` in the
     original token order.  Returns ``(o, lse)`` in the original order.  With
     ``ranks`` a subset of ranks, only those shards of the output are computed
-    (the others are left as they were in ``bufs``).
+    (the others are left as they were in ``bufs``).  With ``plan`` (from
+    :func:`ring_plan` on the same layout and mask) the fused path runs only
+    the steps whose blocks hold visible pairs.
     """
     if q.shape[1] != k.shape[1]:
         raise ValueError("the ring driver runs self-attention (Tq == Tk)")
@@ -166,8 +199,11 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     if step_hook:
         step_hook("reorder", -1, -1, False)
     for r in (range(cp_size) if ranks is None else ranks):
+        steps = None
+        if plan is not None and fused:
+            steps = [s for s in range(cp_size) if int(plan[r, s]) > 0] or [cp_size - 1]
         rank_steps(r, cp_size, bufs, scale=scale, causal=causal, window=window, step_hook=step_hook,
-                   fused=fused)
+                   fused=fused, steps=steps)
     if step_hook:
         step_hook("inverse_reorder", -1, -1, True)
     o = ra.inverse_reorder(bufs.o, cp_size, kind, stripe_size)

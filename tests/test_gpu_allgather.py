@@ -1,4 +1,4 @@
-"""GPU parity of the all-gather context-parallel forward against the fp64 oracle.
+"""GPU parity of the all-gather context-parallel forward and of the ring plan.
 
 Each rank's query shard of the striped reorder attends to the whole
 (reordered) K/V in one call; the result, permuted back, must equal plain
@@ -107,3 +107,57 @@ def test_allgather_full_size_zero_queries_every_row():
     err = (got - ref[:, :, None])[live[:, :, None].expand_as(got)].abs().max().item()
     assert err <= 1e-5, err
     assert (o[~live] == 0).all()
+
+
+def _plan(w, ids, pos):
+    return bosf.ring_plan(ids.to(DEV), pos.to(DEV), w.cp_size, w.reorder, w.stripe,
+                          num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                          head_dim=w.head_dim, causal=w.causal, window=w.window)
+
+
+def test_ring_plan_counts_match_oracle():
+    """Per (rank, step) visible pairs of the sharded packed workload's ring, from
+    the library's classification, equal the oracle's mask counts."""
+    w = get(3)
+    ids, pos = packed_metadata(w.batch, w.seq_len, w.slots, w.valid_per_slot)
+    plan = _plan(w, ids, pos)
+    m = oracle.reorder_map(w.seq_len, w.cp_size, w.reorder, w.stripe)
+    ids_r, pos_r = ids.numpy()[:, m], pos.numpy()[:, m]
+    n = w.seq_len // w.cp_size
+    for r in range(w.cp_size):
+        for s in range(w.cp_size):
+            c = (r - s) % w.cp_size
+            want = oracle.visible_pairs(ids_r[:, r * n:(r + 1) * n], pos_r[:, r * n:(r + 1) * n],
+                                        ids_r[:, c * n:(c + 1) * n], pos_r[:, c * n:(c + 1) * n],
+                                        causal=w.causal, window=w.window).sum()
+            assert int(plan[r, s]) == int(want), (r, s, int(plan[r, s]), int(want))
+    assert (plan == 0).any(), "the layout should have empty ring steps"
+
+
+def test_ring_plan_long_context_total():
+    """The long-context ring's plan sums to the step's visible pairs (closed
+    form, tests/golden/visible_pairs.txt) and is the same for ranks r and r+2
+    (the dual-chunk layout is periodic with period 2 in the rank here)."""
+    w = get(5)
+    ids, pos = packed_metadata(w.batch, w.seq_len, w.slots, w.valid_per_slot)
+    plan = _plan(w, ids, pos)
+    assert int(plan.sum()) == 536936448
+    assert torch.equal(plan[0], plan[2]) and torch.equal(plan[1], plan[3])
+    assert (plan == 0).sum() == 8
+
+
+def test_ring_with_plan_is_bit_identical():
+    """Skipping the steps without visible pairs changes nothing: the last
+    step that has work writes the same bf16 output the empty step would have."""
+    w = dataclasses.replace(get(5), batch=1, seq_len=16384, num_q_heads=16, slots=2,
+                            valid_per_slot=6000, window=(2048, 0))
+    q, k, v, ids, pos = device_inputs(w)
+    plan = bosf.ring_plan(ids, pos, w.cp_size, w.reorder, w.stripe, num_q_heads=w.num_q_heads,
+                          num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, causal=w.causal,
+                          window=w.window)
+    assert (plan == 0).any()
+    o1, l1 = bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe,
+                               causal=w.causal, window=w.window)
+    o2, l2 = bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe,
+                               causal=w.causal, window=w.window, plan=plan)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
