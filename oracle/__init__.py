@@ -25,6 +25,10 @@ What it computes, and where that is defined:
 * ``classify_tiles_exact``/``visible_pairs``: skip / full / partial blocks,
   "Context parallelism and ring attention", section "Causal attention".
 * ``ring_attention``: the per-device ring loop, section "Ring attention".
+* ``attention_backward`` (and per-row / per-key samples): dQ, dK, dV of the
+  attention above by the chain rule of its definition; the pages time the
+  forward together with its backward (tutorial section 5) but print no
+  backward formula.
 
 Every function is pinned by the ``-m "not gpu"`` tests against closed forms,
 invariants, a library routine (torch's scaled-dot-product attention on the
@@ -32,6 +36,7 @@ CPU in fp64) and scalar brute force; nothing is "parity unpinned".
 """
 
 from .attention import attention, attention_rows, visible
+from .backward import attention_backward, backward_key_rows, backward_query_rows
 from .merge import fold_mzu, merge, state_from_output, state_to_output
 from .reorder import apply_map, inverse_map, reorder_map
 from .ring import ring_attention
@@ -39,6 +44,7 @@ from .tiles import classify_tiles_exact, tile_class_counts, visible_pairs
 
 __all__ = [
     "attention", "attention_rows", "visible",
+    "attention_backward", "backward_query_rows", "backward_key_rows",
     "merge", "fold_mzu", "state_from_output", "state_to_output",
     "reorder_map", "inverse_map", "apply_map",
     "ring_attention",
