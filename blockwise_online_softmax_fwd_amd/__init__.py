@@ -1,4 +1,4 @@
-"""MI355X-native blockwise online-softmax attention forward.
+"""MI355X-native blockwise online-softmax attention forward (and its backward).
 
 The compute lives in ``libringattn.so`` (HIP kernels for gfx950 behind the C
 ABI of ``include/ringattn.h``); :mod:`.ringattn` is its ctypes binding and
@@ -12,9 +12,11 @@ from .ringattn import (  # noqa: F401
     TILE_PARTIAL,
     TILE_SKIP,
     RingAttnError,
+    attn_bwd,
     attn_fwd,
     attn_fwd_accumulate,
     attn_merge,
+    bwd_workspace_size,
     check_support,
     classify_tiles,
     inverse_reorder,

@@ -20,7 +20,13 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libringattn.so")
 
-SOURCES = ["api.cpp", "classify.hip", "attn_bf16.hip", "attn_f32.hip", "merge.hip", "reorder.hip"]
+SOURCES = ["api.cpp", "classify.hip", "attn_bf16.hip", "attn_f32.hip", "merge.hip", "reorder.hip",
+           "bwd.hip"]
+
+# Per-source code generation options.  The backward kernels keep their MFMA
+# accumulators in ordinary VGPRs: their scores feed VALU work every tile, and
+# the default accumulator-register form adds a copy per element and spills.
+EXTRA_FLAGS = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"
 
@@ -43,7 +49,7 @@ def common_flags():
 
 def _compile(src: str, verbose: bool) -> str:
     out = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", out] + common_flags()
+    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", out] + common_flags() + EXTRA_FLAGS.get(src, [])
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     if verbose:

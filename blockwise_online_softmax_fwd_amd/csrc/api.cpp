@@ -468,6 +468,209 @@ ra_status ra_attn_merge(const ra_merge_desc *d, const void *o_a, const float *ls
   return RA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The backward's tile shapes: the dq pass uses the forward's (bm = 32 nt
+// queries, bn = 64 keys); the dk/dv pass tiles keys by kBwdKvTile and queries
+// by kBwdQTile.
+struct BwdShape {
+  int32_t tnk, tnq;
+};
+
+ra_status check_bwd_desc(const ra_attn_desc *d, Resolved *r, BwdShape *bs) {
+  ra_status st = check_desc(d, r);
+  if (st != RA_OK) return st;
+  if (d->qkv_dtype != RA_BF16)
+    return fail(RA_ERR_UNSUPPORTED, "the backward needs bf16 q, k and v");
+  const int64_t tnk = ((int64_t)d->kv_len + ra::kBwdKvTile - 1) / ra::kBwdKvTile;
+  const int64_t tnq = ((int64_t)d->q_len + ra::kBwdQTile - 1) / ra::kBwdQTile;
+  if (tnq > kMaxKeyTiles)
+    return fail(RA_ERR_UNSUPPORTED, "q_len %d exceeds %lld query tiles of %d tokens", d->q_len,
+                (long long)kMaxKeyTiles, ra::kBwdQTile);
+  if ((int64_t)d->batch * d->num_kv_heads * tnk >= (int64_t)1 << 31)
+    return fail(RA_ERR_UNSUPPORTED, "too many key tiles for one launch");
+  bs->tnk = (int32_t)tnk;
+  bs->tnq = (int32_t)tnq;
+  return RA_OK;
+}
+
+ra::BwdLayout bwd_layout_of(const ra_attn_desc *d, const Resolved &r, const BwdShape &bs) {
+  return ra::bwd_workspace_layout(d->batch, d->q_len, d->num_q_heads, d->num_kv_heads,
+                                  d->head_dim, r.nqt, r.nkt, bs.tnq, bs.tnk);
+}
+
+// The mask with the roles of queries and keys swapped: with d = pos_q - pos_k
+// the pair is visible iff lo <= d <= hi; seen from the key, -d must lie in
+// [-hi, -lo], i.e. causal 0, left window -lo and right window hi.
+ra::MaskParams swapped_mask(const ra_attn_desc *d) {
+  ra::MaskParams m;
+  m.causal = 0;
+  m.wl = d->causal ? 0 : d->window_right;
+  m.wr = d->window_left;
+  return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status ra_attn_bwd_workspace_size(const ra_attn_desc *desc, size_t *bytes) {
+  Resolved r;
+  BwdShape bs;
+  const ra_status st = check_bwd_desc(desc, &r, &bs);
+  if (st != RA_OK) return st;
+  if (!bytes) return fail(RA_ERR_NULL, "bytes is NULL");
+  *bytes = bwd_layout_of(desc, r, bs).total;
+  return RA_OK;
+}
+
+ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const void *v,
+                      const int32_t *qid, const int32_t *qpos, const int32_t *kid,
+                      const int32_t *kpos, const void *o, const float *lse, const void *dout,
+                      int32_t grad_dtype, void *dq, void *dk, void *dv, void *workspace,
+                      size_t workspace_bytes, ra_stream_t stream) {
+  Resolved r;
+  BwdShape bs;
+  ra_status st = check_bwd_desc(d, &r, &bs);
+  if (st != RA_OK) return st;
+  if (!dtype_ok(grad_dtype)) return fail(RA_ERR_DTYPE, "unknown grad_dtype %d", grad_dtype);
+  const bool has_q = d->batch > 0 && d->q_len > 0;
+  const bool has_k = d->batch > 0 && d->kv_len > 0;
+  if (has_q && (!q || !o || !lse || !dout || !dq)) return fail(RA_ERR_NULL, "q, o, lse, dout or dq is NULL");
+  if (has_k && (!k || !v || !dk || !dv)) return fail(RA_ERR_NULL, "k, v, dk or dv is NULL");
+  st = check_meta(d, r, qid, qpos, kid, kpos);
+  if (st != RA_OK) return st;
+  const size_t os = dtype_size(d->out_dtype), gs = dtype_size(grad_dtype);
+  const void *p16[8] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void *ptr : p16)
+    if (!aligned(ptr, 16)) return fail(RA_ERR_ALIGN, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+  if ((r.q_bs * 2) % 16 || (r.kv_bs * 2) % 16 || (r.o_bs * os) % 16 || (r.o_bs * 2) % 16 ||
+      (r.q_bs * gs) % 16 || (r.kv_bs * gs) % 16)
+    return fail(RA_ERR_ALIGN, "batch strides must be multiples of 16 bytes for every tensor using them");
+  if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
+  const int64_t D = d->head_dim;
+  const int64_t qe = (int64_t)d->q_len * d->num_q_heads * D, ke = (int64_t)d->kv_len * d->num_kv_heads * D;
+  const size_t q_span = span_bytes(d->batch, r.q_bs, qe, 2);
+  const size_t kv_span = span_bytes(d->batch, r.kv_bs, ke, 2);
+  const size_t o_span = span_bytes(d->batch, r.o_bs, qe, os);
+  const size_t do_span = span_bytes(d->batch, r.o_bs, qe, 2);
+  const size_t l_span = span_bytes(d->batch, r.lse_bs, (int64_t)d->q_len * d->num_q_heads, 4);
+  const size_t dq_span = span_bytes(d->batch, r.q_bs, qe, gs);
+  const size_t dkv_span = span_bytes(d->batch, r.kv_bs, ke, gs);
+  const void *ins[6] = {q, k, v, o, lse, dout};
+  const size_t in_span[6] = {q_span, kv_span, kv_span, o_span, l_span, do_span};
+  const void *outs[3] = {dq, dk, dv};
+  const size_t out_span[3] = {dq_span, dkv_span, dkv_span};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_span[i], ins[j], in_span[j]))
+        return fail(RA_ERR_ALIAS, "a gradient buffer overlaps an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], out_span[i], outs[j], out_span[j]))
+        return fail(RA_ERR_ALIAS, "gradient buffers overlap each other");
+  }
+  if (!has_q && !has_k) return RA_OK;
+  const ra::BwdLayout L = bwd_layout_of(d, r, bs);
+  if (L.total > 0 && !workspace)
+    return fail(RA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+  if (!aligned(workspace, 256)) return fail(RA_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  ra::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.qid = qid;
+  p.qpos = qpos;
+  p.kid = kid;
+  p.kpos = kpos;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.lse2 = (float *)(ws + L.lse2);
+  p.dsum = (float *)(ws + L.dsum);
+  p.list = (const uint32_t *)(ws + L.list);
+  p.count = (const int32_t *)(ws + L.count);
+  p.tlist = (const uint32_t *)(ws + L.tlist);
+  p.tcount = (const int32_t *)(ws + L.tcount);
+  p.kvpack = ws + L.kvpack;
+  p.qpack = ws + L.qpack;
+  p.q_bs = r.q_bs;
+  p.kv_bs = r.kv_bs;
+  p.o_bs = r.o_bs;
+  p.do_bs = r.o_bs;
+  p.lse_bs = r.lse_bs;
+  p.qm_bs = r.qm_bs;
+  p.km_bs = r.km_bs;
+  p.dq_bs = r.q_bs;
+  p.dkv_bs = r.kv_bs;
+  p.batch = d->batch;
+  p.tq = d->q_len;
+  p.tk = d->kv_len;
+  p.hq = d->num_q_heads;
+  p.hkv = d->num_kv_heads;
+  p.group = d->num_q_heads / d->num_kv_heads;
+  p.nqt = r.nqt;
+  p.nkt = r.nkt;
+  p.tnk = bs.tnk;
+  p.tnq = bs.tnq;
+  p.scale = d->scale;
+  p.scale_log2 = d->scale * 1.4426950408889634f;
+  p.mask = mask_of(d);
+  const bool out_bf16 = grad_dtype == RA_BF16;
+
+  // Schedules: the forward's (query tiles x 64-key tiles) for dq, and the
+  // swapped one (128-key tiles x 32-query tiles) for dk/dv.
+  ra::Schedule fs;
+  fs.qsum = (ra::TileSum *)(ws + L.qsum);
+  fs.ksum = (ra::TileSum *)(ws + L.ksum);
+  fs.count = (int32_t *)(ws + L.count);
+  fs.pairs = (int64_t *)(ws + L.pairs);
+  fs.list = (uint32_t *)(ws + L.list);
+  ra::Schedule ts;
+  ts.qsum = (ra::TileSum *)(ws + L.tqsum);
+  ts.ksum = (ra::TileSum *)(ws + L.tksum);
+  ts.count = (int32_t *)(ws + L.tcount);
+  ts.pairs = (int64_t *)(ws + L.tpairs);
+  ts.list = (uint32_t *)(ws + L.tlist);
+  hipError_t e;
+  if (has_q) {
+    st = run_schedule(d, r, fs, qid, qpos, kid, kpos, nullptr, s);
+    if (st != RA_OK) return st;
+    e = ra::launch_bwd_prep(p, d->head_dim, d->out_dtype == RA_BF16, s);
+    if (e != hipSuccess) return hip_fail(e, "backward prep");
+  }
+  if (has_k) {
+    e = ra::launch_summaries(kid, kpos, r.km_bs, d->batch, d->kv_len, ra::kBwdKvTile, bs.tnk, ts.qsum, s);
+    if (e != hipSuccess) return hip_fail(e, "tile summaries (keys, swapped)");
+    e = ra::launch_summaries(qid, qpos, r.qm_bs, d->batch, d->q_len, ra::kBwdQTile, bs.tnq, ts.ksum, s);
+    if (e != hipSuccess) return hip_fail(e, "tile summaries (queries, swapped)");
+    e = ra::launch_classify(ts, kid, kpos, qid, qpos, r.km_bs, r.qm_bs, d->batch, d->kv_len,
+                            d->q_len, ra::kBwdKvTile, ra::kBwdQTile, bs.tnk, bs.tnq,
+                            swapped_mask(d), nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "tile classification (swapped)");
+  }
+  e = ra::launch_bwd_pack(p, d->head_dim, s);
+  if (e != hipSuccess) return hip_fail(e, "backward tile packing");
+  if (has_q) {
+    e = ra::launch_bwd_dq(p, d->head_dim, r.nt, out_bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "backward dq pass");
+  }
+  if (has_k) {
+    e = ra::launch_bwd_dkdv(p, d->head_dim, out_bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "backward dk/dv pass");
+  }
+  return RA_OK;
+}
+
 static ra_status check_reorder(int32_t batch, int32_t seq, int64_t row_bytes, int32_t cp,
                                int32_t kind, int32_t stripe) {
   if (batch < 0 || seq < 0) return fail(RA_ERR_SHAPE, "batch and seq_len must be >= 0");

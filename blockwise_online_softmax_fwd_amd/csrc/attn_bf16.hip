@@ -33,43 +33,20 @@
 #include <limits.h>
 #include <math.h>
 
+#include "bf16_tiles.h"
 #include "internal.h"
 #include "lse_merge.h"
 
 namespace ra {
 namespace {
 
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using namespace tiles;
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 constexpr int BN = kBnBf16;          // keys per tile
 constexpr float kNoMax = -1e30f;     // finite "nothing seen yet" running max
 constexpr float kRescaleLog2 = 8.0f; // raise the max only beyond 2^8
-
-// Key (0..15) stored at V^T column x (0..15) of a 16-key chunk: a lane of half
-// h reads the 8 columns 8h..8h+7, which must hold keys 4h..4h+3 and
-// 8+4h..8+4h+3 -- the accumulator rows that half of the wave holds.
-__device__ __forceinline__ int vt_key(int x) {
-  const int h = (x >> 3) & 1, e = x & 7;
-  return (x & ~15) + (e < 4 ? 4 * h + e : 8 + 4 * h + (e - 4));
-}
-
-// XOR swizzle of the 16-byte chunks of a packed row.  LDS serves a 16-byte
-// read for 16 lanes per cycle across 256 bytes of banks; the MFMA operand
-// reads have 16 lanes on 16 consecutive rows at the same logical chunk, so the
-// physical chunk is XORed with the row's index among the rows that share one
-// 256-byte bank line.  cpr = 16-byte chunks per row (8 or 16).
-template <int CPR>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  static_assert(CPR == 8 || CPR == 16, "rows of 128 or 256 bytes");
-  return CPR == 16 ? (chunk ^ (row & 15)) : (chunk ^ ((row >> 1) & 7));
-}
 
 // ----------------------------------------------------------------------------- packing
 

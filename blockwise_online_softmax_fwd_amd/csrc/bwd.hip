@@ -1,0 +1,785 @@
+// Attention backward for bf16 Q/K/V/dO on gfx950 matrix cores.
+//
+// Gradients of O = softmax(scale * Q K^T + M) V ("Context parallelism and ring
+// attention", "The attention problem"; the TransformerEngine JAX tutorial
+// times this backward together with the forward, section 5).  Per query head
+// h reading K/V head g, with P = exp(scale * Q K^T + M - LSE) recomputed from
+// the forward's LSE (no max, no sum):
+//   dV_g += P^T dO,   dP = dO V^T,   dS = P * (dP - D)  with D = rowsum(dO * O),
+//   dQ = scale * dS K,   dK_g += scale * dS^T Q.
+//
+// Kernels:
+//  * prep: D and LSE * log2(e) for every (b, t, h) row (+inf where the row saw
+//    no key, so its probabilities come out 0 without special cases).
+//  * pack: per 64-key tile of one K/V head, K and V as [key][d] and K^T as
+//    [d][key] (the dQ pass); per 32-query tile of one query head, Q and dO as
+//    [query][d], Q^T and dO^T as [d][query], LSE*log2(e), D, ids and positions
+//    (the dK/dV pass).  Every row is padded by 16 bytes: 16 lanes reading the
+//    same 16-byte column of 16 consecutive rows then hit distinct LDS banks,
+//    and each lane's operand addresses differ by constants only (one address
+//    register per block instead of one per swizzled chunk).  Transposed blocks
+//    use the forward's token order inside 16-token chunks (vt_key).
+//  * dQ pass: the forward's workgroup shape and work lists.  Per key tile a
+//    wave forms S^T = K Q^T and dP^T = V dO^T, then dS^T, and accumulates
+//    dQ^T += K^T dS^T; S and dP never leave registers.
+//  * dK/dV pass: 4 waves, one per SIMD, each owning 32 keys of one K/V head
+//    (their K and V are the B operands, held in registers).  The work list of
+//    the 128-key tile (from the same classification kernels run with keys and
+//    queries swapped) names the 32-query tiles that see it; every one of them
+//    is visited once per query head of the group, so the group's sum lands in
+//    registers and each key's gradients are written once, without atomics.
+//    Per visit: S = Q K^T and dP = dO V^T (lane = key, rows = queries), then
+//    dV^T += dO^T P and dK^T += Q^T dS.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
+#include <stddef.h>
+
+#include "bf16_tiles.h"
+#include "internal.h"
+
+namespace ra {
+namespace {
+
+using namespace tiles;
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+constexpr int BN = kBnBf16;      // keys per tile of the dQ pass
+constexpr int BQ = kBwdQTile;    // queries per tile of the dK/dV pass
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ----------------------------------------------------------------------------- prep
+
+template <int D, bool OBF>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  constexpr int TPR = D / 4;       // threads per row, 4 elements each
+  constexpr int RPB = 256 / TPR;   // rows per block and step
+  const int64_t rows = (int64_t)p.batch * p.tq * p.hq;
+  const int sub = threadIdx.x % TPR;
+  const int64_t per_b = (int64_t)p.tq * p.hq;
+  for (int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR; r < rows;
+       r += (int64_t)gridDim.x * RPB) {
+    const int64_t b = r / per_b, rr = r - b * per_b;   // rr = t * hq + h
+    const int64_t col = rr * D + sub * 4;
+    const bf16x4 dov = *(const bf16x4 *)((const bf16 *)p.dout + b * p.do_bs + col);
+    float dot = 0.0f;
+    if (OBF) {
+      const bf16x4 ov = *(const bf16x4 *)((const bf16 *)p.o + b * p.o_bs + col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot = fmaf((float)dov[e], (float)ov[e], dot);
+    } else {
+      const f32x4 ov = *(const f32x4 *)((const float *)p.o + b * p.o_bs + col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot = fmaf((float)dov[e], ov[e], dot);
+    }
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, TPR);
+    if (sub == 0) {
+      const float l = p.lse[b * p.lse_bs + rr];
+      p.dsum[r] = dot;
+      p.lse2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- packing
+
+// Row strides (elements) of the padded blocks.
+template <int D> constexpr int kRowN = D + 8;        // [token][d] rows
+constexpr int kRowTK = BN + 8;                       // K^T rows (64 keys)
+constexpr int kRowTQ = BQ + 8;                       // Q^T / dO^T rows (32 queries)
+
+template <int D>
+struct KvTile {                 // one packed tile of the dQ pass
+  bf16 k[BN * kRowN<D>];        // [key][d]
+  bf16 v[BN * kRowN<D>];        // [key][d]
+  bf16 kt[D * kRowTK];          // [d][key], token order vt_key
+  int32_t meta[2 * BN];         // ids, positions (0 past the end)
+};
+
+template <int D>
+struct QTile {                  // one packed tile of the dK/dV pass
+  bf16 qn[BQ * kRowN<D>];       // [query][d]
+  bf16 don[BQ * kRowN<D>];      // [query][d]
+  bf16 qt[D * kRowTQ];          // [d][query], token order vt_key
+  bf16 dot[D * kRowTQ];         // [d][query], token order vt_key
+  float lse2[BQ];               // LSE * log2(e); +inf past the end or for a row without keys
+  float dsum[BQ];               // rowsum(dO * O)
+  int32_t qid[BQ];
+  int32_t qpos[BQ];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pack_kv_kernel(BwdParams p) {
+  constexpr int DV = D / 8;              // 16-byte chunks of data per [key][d] row
+  constexpr int RN = kRowN<D> / 8;       // chunks per padded row
+  constexpr int RT = kRowTK / 8;
+  static_assert(sizeof(KvTile<D>) == bwd_kv_tile_bytes(D), "packed K/V tile size");
+  __shared__ __attribute__((aligned(16))) bf16 ks[BN][D + 8];
+  const int kt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int64_t tile = ((int64_t)b * p.hkv + g) * p.nkt + kt;
+  KvTile<D> *out = (KvTile<D> *)((char *)p.kvpack + tile * sizeof(KvTile<D>));
+  const bf16 *kb = (const bf16 *)p.k + b * p.kv_bs + (int64_t)g * D;
+  const bf16 *vb = (const bf16 *)p.v + b * p.kv_bs + (int64_t)g * D;
+  const int64_t tok = (int64_t)p.hkv * D;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int u = tid; u < BN * RN; u += 256) {
+    const int r = u / RN, c = u % RN;
+    const int key = kt * BN + r;
+    const bool in = key < p.tk && c < DV;
+    const u32x4 kv = in ? *(const u32x4 *)(kb + key * tok + c * 8) : zero;
+    *(u32x4 *)(out->k + u * 8) = kv;
+    *(u32x4 *)(out->v + u * 8) = in ? *(const u32x4 *)(vb + key * tok + c * 8) : zero;
+    if (c < DV) *(u32x4 *)&ks[r][c * 8] = kv;
+  }
+  if (tid < BN) {
+    const int key = kt * BN + tid;
+    out->meta[tid] = key < p.tk ? p.kid[b * p.km_bs + key] : 0;
+    out->meta[BN + tid] = key < p.tk ? p.kpos[b * p.km_bs + key] : 0;
+  }
+  __syncthreads();
+  const uint16_t *ksu = (const uint16_t *)&ks[0][0];
+  for (int u = tid; u < D * RT; u += 256) {
+    const int d = u / RT, c = u % RT;
+    u32x4 o = zero;
+    if (c < BN / 8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = ksu[vt_key(c * 8 + 2 * j) * (D + 8) + d];
+        const uint32_t hi = ksu[vt_key(c * 8 + 2 * j + 1) * (D + 8) + d];
+        o[j] = lo | (hi << 16);
+      }
+    }
+    *(u32x4 *)(out->kt + u * 8) = o;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pack_q_kernel(BwdParams p) {
+  constexpr int DV = D / 8;
+  constexpr int RN = kRowN<D> / 8;
+  constexpr int RT = kRowTQ / 8;
+  static_assert(sizeof(QTile<D>) == bwd_q_tile_bytes(D), "packed Q/dO tile size");
+  __shared__ __attribute__((aligned(16))) bf16 qs[BQ][D + 8];
+  __shared__ __attribute__((aligned(16))) bf16 gs[BQ][D + 8];
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int64_t tile = ((int64_t)b * p.hq + h) * p.tnq + qt;
+  QTile<D> *out = (QTile<D> *)((char *)p.qpack + tile * sizeof(QTile<D>));
+  const bf16 *qb = (const bf16 *)p.q + b * p.q_bs + (int64_t)h * D;
+  const bf16 *gb = (const bf16 *)p.dout + b * p.do_bs + (int64_t)h * D;
+  const int64_t tok = (int64_t)p.hq * D;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int u = tid; u < BQ * RN; u += 256) {
+    const int r = u / RN, c = u % RN;
+    const int t = qt * BQ + r;
+    const bool in = t < p.tq && c < DV;
+    const u32x4 qv = in ? *(const u32x4 *)(qb + t * tok + c * 8) : zero;
+    const u32x4 gv = in ? *(const u32x4 *)(gb + t * tok + c * 8) : zero;
+    *(u32x4 *)(out->qn + u * 8) = qv;
+    *(u32x4 *)(out->don + u * 8) = gv;
+    if (c < DV) {
+      *(u32x4 *)&qs[r][c * 8] = qv;
+      *(u32x4 *)&gs[r][c * 8] = gv;
+    }
+  }
+  if (tid < BQ) {
+    const int t = qt * BQ + tid;
+    const bool in = t < p.tq;
+    const int64_t r = ((int64_t)b * p.tq + t) * p.hq + h;
+    out->lse2[tid] = in ? p.lse2[r] : INFINITY;
+    out->dsum[tid] = in ? p.dsum[r] : 0.0f;
+    out->qid[tid] = in ? p.qid[b * p.qm_bs + t] : 0;
+    out->qpos[tid] = in ? p.qpos[b * p.qm_bs + t] : 0;
+  }
+  __syncthreads();
+  const uint16_t *qsu = (const uint16_t *)&qs[0][0];
+  const uint16_t *gsu = (const uint16_t *)&gs[0][0];
+  for (int u = tid; u < D * RT; u += 256) {
+    const int d = u / RT, c = u % RT;
+    u32x4 oq = zero, og = zero;
+    if (c < BQ / 8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t0 = vt_key(c * 8 + 2 * j), t1 = vt_key(c * 8 + 2 * j + 1);
+        oq[j] = (uint32_t)qsu[t0 * (D + 8) + d] | ((uint32_t)qsu[t1 * (D + 8) + d] << 16);
+        og[j] = (uint32_t)gsu[t0 * (D + 8) + d] | ((uint32_t)gsu[t1 * (D + 8) + d] << 16);
+      }
+    }
+    *(u32x4 *)(out->qt + u * 8) = oq;
+    *(u32x4 *)(out->dot + u * 8) = og;
+  }
+}
+
+// ----------------------------------------------------------------------------- masks
+
+// Visibility of one key against the lane's query (dQ pass): kid == qkey (-1
+// for a padding query) and lo <= qpos - kpos <= hi.
+struct LaneMask {
+  int qkey, qpos, lo, hi;
+  __device__ __forceinline__ bool operator()(int kid, int kpos) const {
+    const int d = qpos - kpos;
+    return (kid == qkey) & (d >= lo) & (d <= hi);
+  }
+};
+
+// Visibility of one query against the lane's key (dK/dV pass): qid == kkey (-1
+// for a padding or missing key) and lo <= qpos - kpos <= hi.
+struct KeyMask {
+  int kkey, kpos, lo, hi;
+  __device__ __forceinline__ bool operator()(int qid, int qpos) const {
+    const int d = qpos - kpos;
+    return (qid == kkey) & (d >= lo) & (d <= hi);
+  }
+};
+
+__device__ __forceinline__ void mask_bounds(const MaskParams &m, int &lo, int &hi) {
+  lo = m.causal ? 0 : INT_MIN;
+  if (m.wr >= 0) lo = max(lo, -m.wr);
+  hi = m.wl >= 0 ? m.wl : INT_MAX;
+}
+
+// ----------------------------------------------------------------------------- dQ pass
+
+template <int D, int NT, bool OUT_BF16>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+bwd_dq_kernel(BwdParams p) {
+  constexpr int NH = kWaves / NT;
+  constexpr int BM = 32 * NT;
+  constexpr int DC = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = (int)sizeof(KvTile<D>);
+  constexpr int BLK = (int)offsetof(KvTile<D>, meta);   // bytes of the three bf16 blocks
+  static_assert(BLK % 1024 == 0, "tile blocks are loaded 1 KB per wave instruction");
+  constexpr int CHUNKS = BLK / 1024;
+  constexpr int kStageBytes = kWaves * 32 * 68 * 4;
+  constexpr int kSmemBytes = 2 * TILE > kStageBytes ? 2 * TILE : kStageBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  KvTile<D> &t0 = *reinterpret_cast<KvTile<D> *>(smem);
+  KvTile<D> &t1 = *reinterpret_cast<KvTile<D> *>(smem + TILE);
+  float(*stage)[32][68] = reinterpret_cast<float(*)[32][68]>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar tile offsets
+  const int col = lane & 31, half = lane >> 5;
+  const int hcn = p.group / NH;
+  const int64_t nwork = (int64_t)p.batch * p.hkv * p.nqt * hcn;
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (item >= nwork) return;
+  int64_t w = item;
+  const int hc = (int)(w % hcn);
+  w /= hcn;
+  const int qt = (int)(w % p.nqt);
+  w /= p.nqt;
+  const int g = (int)(w % p.hkv);
+  const int b = (int)(w / p.hkv);
+  const int h = g * p.group + hc * NH + (wave % NH);
+  const int tq = qt * BM + (wave / NH) * 32 + col;
+  const bool qvalid = tq < p.tq;
+
+  const int64_t row = (int64_t)b * p.nqt + qt;
+  const int n = p.count[row];
+  typedef const __attribute__((address_space(4))) uint32_t *const_list_t;
+  const const_list_t lst = (const_list_t)(p.list + row * p.nkt);
+  const char *pack = (const char *)p.kvpack + ((int64_t)b * p.hkv + g) * p.nkt * TILE;
+
+  auto issue = [&](KvTile<D> &dst, int kt) __attribute__((always_inline)) {
+    const char *src = pack + (int64_t)kt * TILE;
+#pragma unroll
+    for (int i = 0; i < (CHUNKS + kWaves - 1) / kWaves; ++i) {
+      const int c = wave + i * kWaves;
+      if (CHUNKS % kWaves == 0 || c < CHUNKS)
+        __builtin_amdgcn_global_load_lds((const void *)(src + c * 1024 + lane * 16),
+                                         LDS_PTR((char *)&dst + c * 1024), 16, 0, 0);
+    }
+    if (wave < 2) {
+      const int off = BLK + wave * (BN * 4);
+      __builtin_amdgcn_global_load_lds((const void *)(src + off + lane * 4),
+                                       LDS_PTR((char *)&dst + off), 4, 0, 0);
+    }
+  };
+
+  // B operands: Q (for S^T = K Q^T) and dO (for dP^T = V dO^T), 8 head_dim
+  // values per step.
+  bf16x8 qf[DC], gf[DC];
+  {
+    const int64_t rel = (int64_t)tq * p.hq * D + (int64_t)h * D + 8 * half;
+    const bf16 *qrow = (const bf16 *)p.q + b * p.q_bs + rel;
+    const bf16 *grow = (const bf16 *)p.dout + b * p.do_bs + rel;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const bool ld = qvalid && n > 0;
+      qf[c] = ld ? *(const bf16x8 *)(qrow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      gf[c] = ld ? *(const bf16x8 *)(grow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+  const int64_t rowidx = ((int64_t)b * p.tq + tq) * p.hq + h;
+  const float l2 = qvalid ? p.lse2[rowidx] : INFINITY;
+  const float dl = qvalid ? p.dsum[rowidx] : 0.0f;
+  LaneMask lm;
+  {
+    const int my_qid = qvalid ? p.qid[b * p.qm_bs + tq] : 0;
+    lm.qkey = my_qid != 0 ? my_qid : -1;
+    lm.qpos = qvalid ? p.qpos[b * p.qm_bs + tq] : 0;
+    mask_bounds(p.mask, lm.lo, lm.hi);
+  }
+  const bool ragged = (p.tk % BN) != 0;
+  auto entry_tile = [&](int it) { return (int)(lst[it] & 0x7fffffffu); };
+  auto entry_masked = [&](int it) {
+    const uint32_t e = lst[it];
+    return (e >> 31) != 0 || (ragged && (int)(e & 0x7fffffffu) == p.nkt - 1);
+  };
+  const float c2 = p.scale_log2;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+
+  // One 32-key block of S^T (or dP^T): A operand rows kb*32 + col of an
+  // [key][d] block, B operand the lane's query row.
+  auto scores = [&](f32x16 &s, const bf16 *blk, const bf16x8 (&bop)[DC])
+      __attribute__((always_inline)) {
+    const bf16 *arow = blk + col * kRowN<D> + 8 * half;
+    const f32x16 zero16 = {};
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)arow, bop[0], zero16, 0, 0, 0);
+#pragma unroll
+    for (int c = 1; c < DC; ++c)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(arow + 16 * c), bop[c], s, 0,
+                                                  0, 0);
+  };
+
+  // One tile, one 32-key block at a time: S^T and dP^T, the mask (boundary
+  // tiles only), dS^T = P^T (dP^T - D) with P^T = 2^(s c2 - LSE log2 e) packed
+  // to bf16 B operands, then dQ^T += K^T dS^T over the block's two 16-key chunks.
+  auto compute = [&](const KvTile<D> &tl, bool masked) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
+      scores(s, tl.k + kb * 32 * kRowN<D>, qf);
+      scores(dp, tl.v + kb * 32 * kRowN<D>, gf);
+      if (masked) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int kk = kb * 32 + 8 * r4 + 4 * half;
+          const int4 ids = *(const int4 *)&tl.meta[kk];
+          const int4 pss = *(const int4 *)&tl.meta[BN + kk];
+          s[4 * r4 + 0] = lm(ids.x, pss.x) ? s[4 * r4 + 0] : -INFINITY;
+          s[4 * r4 + 1] = lm(ids.y, pss.y) ? s[4 * r4 + 1] : -INFINITY;
+          s[4 * r4 + 2] = lm(ids.z, pss.z) ? s[4 * r4 + 2] : -INFINITY;
+          s[4 * r4 + 3] = lm(ids.w, pss.w) ? s[4 * r4 + 3] : -INFINITY;
+        }
+      }
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2));
+        dsf[r >> 3][r & 7] = (bf16)(pv * (dp[r] - dl));
+      }
+#pragma unroll
+      for (int c2i = 0; c2i < 2; ++c2i) {
+        const int ch = 2 * kb + c2i;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = *(const bf16x8 *)(tl.kt + (db * 32 + col) * kRowTK + 16 * ch + 8 * half);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[c2i], acc[db], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (n > 0) {
+    issue(t0, entry_tile(0));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  for (int it = 0; it < n;) {
+    if (it + 1 < n) issue(t1, entry_tile(it + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t0, entry_masked(it));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (++it >= n) break;
+    if (it + 1 < n) issue(t0, entry_tile(it + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t1, entry_masked(it));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    ++it;
+  }
+
+  // dQ = scale * (dQ^T)^T, through LDS in 64-column halves: 16-byte stores.
+  const int tq0 = qt * BM + (wave / NH) * 32;
+  const int rsub = lane >> 4, c4 = (lane & 15) * 4;
+#pragma unroll
+  for (int hd = 0; hd < DB / 2; ++hd) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = acc[2 * hd + j][4 * r4 + e] * p.scale;
+        *(f32x4 *)&stage[wave][col][32 * j + 8 * r4 + 4 * half] = val;
+      }
+#pragma unroll
+    for (int pass = 0; pass < 8; ++pass) {
+      const int qrow = 4 * pass + rsub;
+      const int t = tq0 + qrow;
+      const f32x4 val = *(const f32x4 *)&stage[wave][qrow][c4];
+      if (t < p.tq) {
+        const int64_t rel = (int64_t)t * p.hq * D + (int64_t)h * D + 64 * hd + c4;
+        if (OUT_BF16) {
+          bf16x4 hv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = (bf16)val[e];
+          *(bf16x4 *)((bf16 *)p.dq + b * p.dq_bs + rel) = hv;
+        } else {
+          *(f32x4 *)((float *)p.dq + b * p.dq_bs + rel) = val;
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- dK/dV pass
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(64 * kBwdKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+bwd_dkdv_kernel(BwdParams p) {
+  constexpr int W = kBwdKvWaves;
+  constexpr int DC = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = (int)sizeof(QTile<D>);
+  constexpr int BLK = (int)offsetof(QTile<D>, lse2);    // bytes of the four bf16 blocks
+  static_assert(BLK % 1024 == 0, "tile blocks are loaded 1 KB per wave instruction");
+  constexpr int CHUNKS = BLK / 1024;
+  constexpr int SROW = D + 4;     // staging row of one key, fp32
+  constexpr int kStageBytes = W * 32 * SROW * 4;
+  constexpr int kSmemBytes = 2 * TILE > kStageBytes ? 2 * TILE : kStageBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  QTile<D> &t0 = *reinterpret_cast<QTile<D> *>(smem);
+  QTile<D> &t1 = *reinterpret_cast<QTile<D> *>(smem + TILE);
+  float(*stage)[32][SROW] = reinterpret_cast<float(*)[32][SROW]>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar tile offsets
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t nwork = (int64_t)p.batch * p.hkv * p.tnk;
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (item >= nwork) return;
+  const int kt = (int)(item % p.tnk);
+  const int g = (int)((item / p.tnk) % p.hkv);
+  const int b = (int)(item / ((int64_t)p.tnk * p.hkv));
+  const int key = kt * kBwdKvTile + wave * 32 + col;
+  const bool kvalid = key < p.tk;
+
+  const int64_t row = (int64_t)b * p.tnk + kt;
+  const int nq = p.tcount[row];
+  const int n = nq * p.group;         // visits: (query tile, head of the group)
+  typedef const __attribute__((address_space(4))) uint32_t *const_list_t;
+  const const_list_t lst = (const_list_t)(p.tlist + row * p.tnq);
+
+  auto visit_tile = [&](int it) {
+    const int qtile = (int)(lst[it / p.group] & 0x7fffffffu);
+    const int h = g * p.group + it % p.group;
+    return ((int64_t)b * p.hq + h) * p.tnq + qtile;
+  };
+  const bool ragged_q = (p.tq % BQ) != 0;
+  auto visit_masked = [&](int it) {
+    const uint32_t e = lst[it / p.group];
+    return (e >> 31) != 0 || (ragged_q && (int)(e & 0x7fffffffu) == p.tnq - 1) || !kvalid;
+  };
+  auto issue = [&](QTile<D> &dst, int64_t tile) __attribute__((always_inline)) {
+    const char *src = (const char *)p.qpack + tile * TILE;
+#pragma unroll
+    for (int i = 0; i < (CHUNKS + W - 1) / W; ++i) {
+      const int c = wave + i * W;
+      if (CHUNKS % W == 0 || c < CHUNKS)
+        __builtin_amdgcn_global_load_lds((const void *)(src + c * 1024 + lane * 16),
+                                         LDS_PTR((char *)&dst + c * 1024), 16, 0, 0);
+    }
+    if (wave < 2) {
+      const int off = BLK + wave * 256;
+      __builtin_amdgcn_global_load_lds((const void *)(src + off + lane * 4),
+                                       LDS_PTR((char *)&dst + off), 4, 0, 0);
+    }
+  };
+
+  // B operands: the lane's key row of K and of V, 8 head_dim values per step.
+  bf16x8 kf[DC], vf[DC];
+  {
+    const int64_t rel = (int64_t)key * p.hkv * D + (int64_t)g * D + 8 * half;
+    const bf16 *krow = (const bf16 *)p.k + b * p.kv_bs + rel;
+    const bf16 *vrow = (const bf16 *)p.v + b * p.kv_bs + rel;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const bool ld = kvalid && n > 0;
+      kf[c] = ld ? *(const bf16x8 *)(krow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      vf[c] = ld ? *(const bf16x8 *)(vrow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+  KeyMask km;
+  {
+    const int my_kid = kvalid ? p.kid[b * p.km_bs + key] : 0;
+    km.kkey = my_kid != 0 ? my_kid : -1;
+    km.kpos = kvalid ? p.kpos[b * p.km_bs + key] : 0;
+    mask_bounds(p.mask, km.lo, km.hi);
+  }
+  const float c2 = p.scale_log2;
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[db][r] = 0.0f;
+      dv[db][r] = 0.0f;
+    }
+
+  auto compute = [&](const QTile<D> &tl, bool masked) __attribute__((always_inline)) {
+    // S = Q K^T and dP = dO V^T for the 32 queries of the tile: lane = key,
+    // element r of the accumulator = query row 8(r/4) + 4 half + r%4.
+    f32x16 s, dp;
+    {
+      bf16x8 aq[DC], ag[DC];
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        aq[c] = *(const bf16x8 *)(tl.qn + col * kRowN<D> + 16 * c + 8 * half);
+        ag[c] = *(const bf16x8 *)(tl.don + col * kRowN<D> + 16 * c + 8 * half);
+      }
+      const f32x16 zero16 = {};
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0], kf[0], zero16, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[0], vf[0], zero16, 0, 0, 0);
+#pragma unroll
+      for (int c = 1; c < DC; ++c) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[c], kf[c], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[c], vf[c], dp, 0, 0, 0);
+      }
+    }
+    if (masked) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int qq = 8 * r4 + 4 * half;
+        const int4 ids = *(const int4 *)&tl.qid[qq];
+        const int4 pss = *(const int4 *)&tl.qpos[qq];
+        s[4 * r4 + 0] = km(ids.x, pss.x) ? s[4 * r4 + 0] : -INFINITY;
+        s[4 * r4 + 1] = km(ids.y, pss.y) ? s[4 * r4 + 1] : -INFINITY;
+        s[4 * r4 + 2] = km(ids.z, pss.z) ? s[4 * r4 + 2] : -INFINITY;
+        s[4 * r4 + 3] = km(ids.w, pss.w) ? s[4 * r4 + 3] : -INFINITY;
+      }
+    }
+    // P = 2^(s c2 - LSE log2 e), dS = P (dP - D), per query row; packed to
+    // bf16 as the B operands of the two accumulations.
+    bf16x8 pf[2], df[2];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int qq = 8 * r4 + 4 * half;
+      const f32x4 l4 = *(const f32x4 *)&tl.lse2[qq];
+      const f32x4 d4 = *(const f32x4 *)&tl.dsum[qq];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * r4 + e;
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[e]));
+        pf[r >> 3][r & 7] = (bf16)pv;
+        df[r >> 3][r & 7] = (bf16)(pv * (dp[r] - d4[e]));
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end).
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int off = (db * 32 + col) * kRowTQ + 16 * ch + 8 * half;
+        const bf16x8 ag = *(const bf16x8 *)(tl.dot + off);
+        const bf16x8 aq = *(const bf16x8 *)(tl.qt + off);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[ch], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, df[ch], dk[db], 0, 0, 0);
+      }
+  };
+
+  if (n > 0) {
+    issue(t0, visit_tile(0));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  for (int it = 0; it < n;) {
+    if (it + 1 < n) issue(t1, visit_tile(it + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t0, visit_masked(it));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (++it >= n) break;
+    if (it + 1 < n) issue(t0, visit_tile(it + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(t1, visit_masked(it));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    ++it;
+  }
+
+  // dK = scale * (dK^T)^T and dV = (dV^T)^T through LDS: each wave stages its
+  // 32 keys x D, then writes whole rows, 16 bytes per lane.
+  const int key0 = kt * kBwdKvTile + wave * 32;
+  auto store = [&](const f32x16 (&acc)[DB], float mul, void *dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = acc[db][4 * r4 + e] * mul;
+        *(f32x4 *)&stage[wave][col][db * 32 + 8 * r4 + 4 * half] = val;
+      }
+    constexpr int LPR = D / 4;            // lanes per key row
+    constexpr int RPP = 64 / LPR;         // rows per pass
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPP; ++pass) {
+      const int kr = pass * RPP + lane / LPR;
+      const int c = (lane % LPR) * 4;
+      const int t = key0 + kr;
+      const f32x4 val = *(const f32x4 *)&stage[wave][kr][c];
+      if (t < p.tk) {
+        const int64_t rel = (int64_t)t * p.hkv * D + (int64_t)g * D + c;
+        if (OUT_BF16) {
+          bf16x4 hv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = (bf16)val[e];
+          *(bf16x4 *)((bf16 *)dst + b * p.dkv_bs + rel) = hv;
+        } else {
+          *(f32x4 *)((float *)dst + b * p.dkv_bs + rel) = val;
+        }
+      }
+    }
+  };
+  __syncthreads();  // the staging reuses the tile buffers
+  store(dk, p.scale, p.dk);
+  store(dv, 1.0f, p.dv);
+}
+
+// ----------------------------------------------------------------------------- launchers
+
+template <int D, int NT>
+hipError_t launch_dq_nt(const BwdParams &p, bool out_bf16, hipStream_t stream) {
+  constexpr int NH = kWaves / NT;
+  const int64_t nwork = (int64_t)p.batch * p.hkv * p.nqt * (p.group / NH);
+  if (nwork == 0) return hipSuccess;
+  const int64_t grid = (nwork + 7) / 8 * 8;
+  if (out_bf16)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NT, true>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NT, false>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_d(const BwdParams &p, int32_t nt, bool out_bf16, hipStream_t stream) {
+  switch (nt) {
+    case 1: return launch_dq_nt<D, 1>(p, out_bf16, stream);
+    case 2: return launch_dq_nt<D, 2>(p, out_bf16, stream);
+    case 4: return launch_dq_nt<D, 4>(p, out_bf16, stream);
+    case 8: return launch_dq_nt<D, 8>(p, out_bf16, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_dkdv_d(const BwdParams &p, bool out_bf16, hipStream_t stream) {
+  const int64_t nwork = (int64_t)p.batch * p.hkv * p.tnk;
+  if (nwork == 0) return hipSuccess;
+  const int64_t grid = (nwork + 7) / 8 * 8;
+  if (out_bf16)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)grid), dim3(64 * kBwdKvWaves), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)grid), dim3(64 * kBwdKvWaves), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+BwdLayout bwd_workspace_layout(int32_t batch, int32_t tq, int32_t hq, int32_t hkv, int32_t d,
+                               int32_t nqt, int32_t nkt, int32_t tnq, int32_t tnk) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  BwdLayout w;
+  size_t off = 0;
+  const size_t B = (size_t)batch;
+  w.qsum = off;   off = up(off + B * nqt * sizeof(TileSum));
+  w.ksum = off;   off = up(off + B * nkt * sizeof(TileSum));
+  w.count = off;  off = up(off + B * nqt * sizeof(int32_t));
+  w.pairs = off;  off = up(off + B * nqt * sizeof(int64_t));
+  w.list = off;   off = up(off + B * nqt * nkt * sizeof(uint32_t));
+  w.tqsum = off;  off = up(off + B * tnk * sizeof(TileSum));
+  w.tksum = off;  off = up(off + B * tnq * sizeof(TileSum));
+  w.tcount = off; off = up(off + B * tnk * sizeof(int32_t));
+  w.tpairs = off; off = up(off + B * tnk * sizeof(int64_t));
+  w.tlist = off;  off = up(off + B * tnk * tnq * sizeof(uint32_t));
+  w.lse2 = off;   off = up(off + B * tq * hq * sizeof(float));
+  w.dsum = off;   off = up(off + B * tq * hq * sizeof(float));
+  w.kvpack = off; off = up(off + B * hkv * nkt * bwd_kv_tile_bytes(d));
+  w.qpack = off;  off = up(off + B * hq * tnq * bwd_q_tile_bytes(d));
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_bwd_prep(const BwdParams &p, int32_t head_dim, bool o_bf16, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.batch * p.tq * p.hq;
+  if (rows == 0) return hipSuccess;
+  const int64_t rpb = 256 / (head_dim / 4);
+  int64_t blocks = (rows + rpb - 1) / rpb;
+  if (blocks > 16384) blocks = 16384;
+  const dim3 grid((unsigned)blocks);
+  if (head_dim == 128) {
+    if (o_bf16) hipLaunchKernelGGL((bwd_prep_kernel<128, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((bwd_prep_kernel<128, false>), grid, dim3(256), 0, stream, p);
+  } else if (head_dim == 64) {
+    if (o_bf16) hipLaunchKernelGGL((bwd_prep_kernel<64, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((bwd_prep_kernel<64, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pack(const BwdParams &p, int32_t head_dim, hipStream_t stream) {
+  if (p.batch == 0) return hipSuccess;
+  if (head_dim != 128 && head_dim != 64) return hipErrorInvalidValue;
+  if (p.nkt > 0) {
+    const dim3 grid(p.nkt, p.hkv, p.batch);
+    if (head_dim == 128) hipLaunchKernelGGL(bwd_pack_kv_kernel<128>, grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(bwd_pack_kv_kernel<64>, grid, dim3(256), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.tnq > 0) {
+    const dim3 grid(p.tnq, p.hq, p.batch);
+    if (head_dim == 128) hipLaunchKernelGGL(bwd_pack_q_kernel<128>, grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(bwd_pack_q_kernel<64>, grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdParams &p, int32_t head_dim, int32_t nt, bool out_bf16,
+                         hipStream_t stream) {
+  if (head_dim == 128) return launch_dq_d<128>(p, nt, out_bf16, stream);
+  if (head_dim == 64) return launch_dq_d<64>(p, nt, out_bf16, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dkdv(const BwdParams &p, int32_t head_dim, bool out_bf16,
+                           hipStream_t stream) {
+  if (head_dim == 128) return launch_dkdv_d<128>(p, out_bf16, stream);
+  if (head_dim == 64) return launch_dkdv_d<64>(p, out_bf16, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ra

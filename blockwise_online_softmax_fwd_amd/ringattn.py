@@ -28,7 +28,7 @@ STATUS = {0: "RA_OK", 1: "RA_ERR_NULL", 2: "RA_ERR_SHAPE", 3: "RA_ERR_DTYPE", 4:
 EXPORTS = ["ra_version", "ra_status_string", "ra_last_error", "ra_check_support", "ra_tile_shape",
            "ra_attn_fwd_workspace_size", "ra_attn_fwd", "ra_attn_fwd_accumulate",
            "ra_classify_tiles", "ra_attn_merge", "ra_reorder", "ra_inverse_reorder",
-           "ra_reorder_index"]
+           "ra_reorder_index", "ra_attn_bwd_workspace_size", "ra_attn_bwd"]
 
 
 class RingAttnError(RuntimeError):
@@ -89,6 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ra_reorder": ([P, P, I32, I32, I64, I32, I32, I32, P], I32),
         "ra_inverse_reorder": ([P, P, I32, I32, I64, I32, I32, I32, P], I32),
         "ra_reorder_index": ([I32, I32, I32, I32, I32, P], I32),
+        "ra_attn_bwd_workspace_size": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)], I32),
+        "ra_attn_bwd": ([ctypes.POINTER(AttnDesc)] + [P] * 10 + [I32] + [P] * 3 + [P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -272,6 +274,67 @@ def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, k
         _ptr(kv_segment_ids), _ptr(kv_segment_pos), ctypes.byref(part), _ptr(out), _ptr(lse),
         _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(q)))
     return out, lse
+
+
+def bwd_workspace_size(desc: AttnDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().ra_attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, o, lse, dout,
+             *, scale=None, causal=True, window=(-1, -1), grad_dtype=torch.float32, dq=None,
+             dk=None, dv=None, workspace=None):
+    """Gradients ``(dq, dk, dv)`` of the masked GQA attention forward.
+
+    q ``[B,Tq,Hq,D]``, k/v ``[B,Tk,Hkv,D]`` bf16; ``o``/``lse`` the forward's
+    outputs for the same inputs and mask (o bf16 or fp32); ``dout`` bf16 with
+    o's shape and batch stride.  Gradients are ``grad_dtype`` (float32 or
+    bfloat16) with the shapes and batch strides of q and k; given buffers are
+    overwritten.
+    """
+    _require_gpu(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, o, lse, dout)
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("the backward needs bfloat16 q, k and v")
+    if dout.dtype != torch.bfloat16:
+        raise TypeError("dout must be bfloat16")
+    if k.shape != v.shape or _batch_stride(v, 3) != _batch_stride(k, 3):
+        raise ValueError("k and v must have the same shape and batch stride")
+    if o.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("o and dout must have q's shape, lse [B,Tq,Hq]")
+    if _batch_stride(dout, 3) != _batch_stride(o, 3):
+        raise ValueError("dout must have o's batch stride")
+    for t in (q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos):
+        if t.dtype != torch.int32:
+            raise TypeError("segment ids and positions must be int32")
+    gc = _dtype_code(grad_dtype)
+    gdt = _torch_dtype(gc)
+
+    def like(t):
+        # the library writes a gradient with its input's batch stride
+        bs = _batch_stride(t, 3) or t.shape[1] * t.shape[2] * t.shape[3]
+        return torch.empty_strided(t.shape, (bs, t.shape[2] * t.shape[3], t.shape[3], 1),
+                                   dtype=gdt, device=t.device)
+
+    if dq is None:
+        dq = like(q)
+    if dk is None:
+        dk = like(k)
+    if dv is None:
+        dv = like(k)
+    for t, like in ((dq, q), (dk, k), (dv, k)):
+        if t.dtype != gdt or t.shape != like.shape or _batch_stride(t, 3) != _batch_stride(like, 3):
+            raise ValueError("gradient buffers must have grad_dtype and their input's shape and batch stride")
+    desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window,
+                      _dtype_code(o.dtype), o, lse)
+    ws_bytes = bwd_workspace_size(desc)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _check(load_library().ra_attn_bwd(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_segment_ids), _ptr(q_segment_pos),
+        _ptr(kv_segment_ids), _ptr(kv_segment_pos), _ptr(o), _ptr(lse), _ptr(dout), gc, _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(q)))
+    return dq, dk, dv
 
 
 def classify_tiles(q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, *, num_q_heads,

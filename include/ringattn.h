@@ -213,6 +213,49 @@ ra_status ra_attn_merge(const ra_merge_desc *desc, const void *o_a, const float 
                         ra_stream_t stream);
 
 /*
+ * Attention backward: the gradients of ra_attn_fwd's o with respect to q, k and
+ * v, given the output gradient dout ([RA] "The attention problem" for the
+ * function differentiated; [TUT] s5 times the forward together with this
+ * backward, and [CPP] lists the backward primitives beside the forward ones).
+ * Per query head h reading K/V head g = h / (Hq/Hkv), with the forward's lse:
+ *   P  = exp(scale * q_h k_g^T + M - lse)        (0 where M masks; rows without
+ *                                                  a visible key are all 0)
+ *   dS = P * (dout_h v_g^T - rowsum(dout_h * o_h))
+ *   dq_h = scale * dS k_g,   dk_g = scale * sum_h dS^T q_h,   dv_g = sum_h P^T dout_h
+ * The mask M and every other rule of desc are ra_attn_fwd's; o and lse must be
+ * that forward's outputs for the same inputs (P is rebuilt from lse; no max or
+ * sum is recomputed).  Key tiles with no visible pair are skipped and only
+ * boundary tiles are masked, in both passes: dq over the forward's tile lists,
+ * dk/dv over lists built with the roles of keys and queries swapped.
+ *
+ * Inputs:  q, k, v bf16 (qkv_dtype must be RA_BF16); o [B,Tq,Hq,D] out_dtype
+ *          with o_batch_stride; lse [B,Tq,Hq] fp32 with lse_batch_stride;
+ *          dout [B,Tq,Hq,D] bf16 with o_batch_stride (in its own elements).
+ * Outputs: dq like q (q_batch_stride), dk and dv like k (kv_batch_stride), all
+ *          of dtype grad_dtype (RA_BF16 or RA_F32), fully overwritten: rows no
+ *          visible pair reaches (padding, masked keys) get 0.  Each key's
+ *          dk/dv is accumulated in registers over its whole query-head group
+ *          and written once: no atomics, and the result does not depend on
+ *          scheduling.
+ * q, k, v, o, dout, dq, dk, dv: 16-byte aligned, batch strides multiples of 16
+ * bytes; lse and metadata 4-byte aligned.  dq, dk and dv must not overlap each
+ * other or any input (RA_ERR_ALIAS).  workspace: device memory of at least
+ * ra_attn_bwd_workspace_size() bytes, 256-byte aligned, owned by the caller,
+ * overwritten (both passes' tile lists, rowsum(dout*o), and packed copies of
+ * q/dout and k/v tiles in the layouts the kernels read); calls that share a
+ * workspace must be ordered on one stream.  Supported: D in {64, 128}, any
+ * GQA group, Tq up to 2^20 and Tk up to 2^21 tokens per call.
+ */
+ra_status ra_attn_bwd_workspace_size(const ra_attn_desc *desc, size_t *bytes);
+
+ra_status ra_attn_bwd(const ra_attn_desc *desc, const void *q, const void *k, const void *v,
+                      const int32_t *q_segment_ids, const int32_t *q_segment_pos,
+                      const int32_t *kv_segment_ids, const int32_t *kv_segment_pos,
+                      const void *o, const float *lse, const void *dout, int32_t grad_dtype,
+                      void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                      ra_stream_t stream);
+
+/*
  * Causal load-balancing permutation of the sequence axis of a dense
  * [batch, seq_len, row_bytes] tensor (any of q, k, v, segment ids/positions, o,
  * lse) -- [TUT] s4 reorder_causal_load_balancing with seq_dim 1:

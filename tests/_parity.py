@@ -39,3 +39,43 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype="bf16", what=""):
     assert o_err <= o_tol, f"{what}: max |dO| = {o_err:.3e} > {o_tol}"
     assert l_err <= l_tol, f"{what}: max |dLSE| = {l_err:.3e} > {l_tol}"
     return o_err, l_err
+
+
+# Gradient bar (bf16 inputs).  The backward rounds P and dS to bf16 (unit
+# roundoff u = 2^-8) before the three gradient products and accumulates in
+# fp32; a gradient element is a sum of such products, so its error is a sum of
+# independent roundings of relative size <= u (RMS u/sqrt(3) ~ 2.3e-3 of the
+# element's magnitude), plus the same again when the gradient itself is stored
+# in bf16 and when O arrives in bf16 (through D = rowsum(dO * O)).  The bar is
+# about 3x that estimate on the relative Frobenius error and 2e-2 of the
+# tensor's largest magnitude element-wise.  Entries whose exact gradient is 0
+# because no visible pair reaches them must come out exactly 0.  A gradient
+# that is 0 only by cancellation (a row with a single visible key has
+# dP = D) keeps the fp32 residue of dP - D, two differently ordered sums of
+# the same products: ~1e-7 relative to |dP| ~ sqrt(D), so 1e-4 absolute.
+GRAD_FRO = 1e-2
+GRAD_MAX = 2e-2
+GRAD_CANCEL_ATOL = 1e-4
+
+
+def compare_grads(got, ref, what="", fro_tol=GRAD_FRO, max_tol=GRAD_MAX, exact_zero=None):
+    """Assert the gradient bar; return (relative Frobenius error, max error / max |ref|)."""
+    g = to64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert g.shape == ref.shape, f"{what}: shape {g.shape} vs {ref.shape}"
+    assert np.isfinite(g).all(), f"{what}: NaN or Inf"
+    if exact_zero is not None and exact_zero.any():
+        bad = g[exact_zero] != 0
+        assert not bad.any(), f"{what}: {int(bad.sum())} entries that no pair reaches are not 0"
+    nref = float(np.linalg.norm(ref))
+    mref = float(np.abs(ref).max()) if ref.size else 0.0
+    err = g - ref
+    if nref == 0.0:
+        mx = float(np.abs(err).max()) if err.size else 0.0
+        assert mx <= GRAD_CANCEL_ATOL, f"{what}: exact gradient is 0, got max |g| = {mx:.3e}"
+        return 0.0, mx
+    fro = float(np.linalg.norm(err)) / nref
+    mx = float(np.abs(err).max()) / mref
+    assert fro <= fro_tol, f"{what}: relative Frobenius error {fro:.3e} > {fro_tol}"
+    assert mx <= max_tol, f"{what}: max error {mx:.3e} of max |ref| > {max_tol}"
+    return fro, mx

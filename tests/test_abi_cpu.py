@@ -252,3 +252,52 @@ def test_reorder_index_matches_oracle(t, r, kind, s):
     assert np.array_equal(m, ref)
     inv = ra.reorder_index(t, r, kind, s, inverse=True)
     assert np.array_equal(inv, oracle.inverse_map(ref))
+
+
+def _bwd(lib, d, ws_bytes=1 << 34, grad=ra.RA_F32, **over):
+    args = dict(q=_p(0), k=_p(1 << 32), v=_p(2 << 32), qid=_p(3 << 32), qpos=_p(4 << 32),
+                kid=_p(5 << 32), kpos=_p(6 << 32), o=_p(7 << 32), lse=_p(8 << 32),
+                dout=_p(10 << 32), dq=_p(11 << 32), dk=_p(12 << 32), dv=_p(13 << 32),
+                ws=_p(16 << 32))
+    args.update(over)
+    return lib.ra_attn_bwd(ctypes.byref(d), args["q"], args["k"], args["v"], args["qid"],
+                           args["qpos"], args["kid"], args["kpos"], args["o"], args["lse"],
+                           args["dout"], grad, args["dq"], args["dk"], args["dv"], args["ws"],
+                           ctypes.c_size_t(ws_bytes), None)
+
+
+def test_bwd_workspace_size():
+    d = _desc(q_len=4096, kv_len=4096)
+    n = ra.bwd_workspace_size(d)
+    # packed Q/dO tiles (both layouts) alone: 2 x 2 x Tq*Hq*D bf16 per batch row, plus padding
+    assert n > 2 * 2 * 2 * 4096 * 16 * 128 * 2
+    assert ra.bwd_workspace_size(_desc(q_len=64, kv_len=64)) < n
+    d32 = _desc(qkv_dtype=ra.RA_F32, head_dim=64)
+    with pytest.raises(ra.RingAttnError, match="RA_ERR_UNSUPPORTED"):
+        ra.bwd_workspace_size(d32)
+    with pytest.raises(ra.RingAttnError, match="RA_ERR_UNSUPPORTED"):
+        ra.bwd_workspace_size(_desc(q_len=32 * 32768 + 1))
+
+
+def test_bwd_validation(lib):
+    d = _desc()
+    assert lib.ra_attn_bwd(None, *([None] * 10), 0, *([None] * 4), 0, None) == NULL
+    for name in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "qid", "kpos"):
+        assert _bwd(lib, d, **{name: None}) == NULL, name
+    assert _bwd(lib, d, ws=None) == WS
+    assert _bwd(lib, d, ws_bytes=ra.bwd_workspace_size(d) - 1) == WS
+    assert _bwd(lib, d, grad=5) == DTYPE
+    for name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv"):
+        assert _bwd(lib, d, **{name: _p((14 << 32) + 8)}) == ALIGN, name
+    assert _bwd(lib, d, lse=_p((8 << 32) + 2)) == ALIGN
+    assert _bwd(lib, d, ws=_p((16 << 32) + 64)) == ALIGN
+    assert _bwd(lib, _desc(qkv_dtype=ra.RA_F32)) == UNSUP
+    assert _bwd(lib, _desc(head_dim=80)) == UNSUP
+    # gradients overlapping an input or each other
+    assert _bwd(lib, d, dq=_p(0)) == ALIAS
+    assert _bwd(lib, d, dk=_p((2 << 32) + 4096)) == ALIAS
+    assert _bwd(lib, d, dv=_p(12 << 32)) == ALIAS
+    assert _bwd(lib, d, dq=_p((10 << 32) + 16)) == ALIAS
+    # empty problems launch nothing and succeed
+    assert _bwd(lib, _desc(batch=0)) == OK
+    assert _bwd(lib, _desc(q_len=0, kv_len=0), ws=None, ws_bytes=0) == OK
