@@ -149,6 +149,11 @@ def main():
                          "partials, or each shard against the whole gathered K/V (striped)")
     ap.add_argument("--stripe", type=int, default=512,
                     help="stripe size of the all-gather strategy's striped reorder")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the attention backward (attn_bwd) instead of the forward: every "
+                         "shard of the all-gather strategy against the whole K/V, o and lse from "
+                         "the forward computed once outside the timed region")
+    ap.add_argument("--grad-dtype", choices=("f32", "bf16"), default="f32")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy this many MiB with a plain device copy kernel "
                          "(a known-size reference for hardware byte counters)")
@@ -166,6 +171,8 @@ def main():
     if allgather:
         w = dataclasses.replace(w, reorder="striped", stripe=args.stripe)
     bosf.load_library()
+    if args.backward:
+        return bench_backward(args, w, dev)
     desc = w.describe()
     if allgather:
         desc = desc.replace(f"{w.cp_size} shards x {w.cp_size} ring steps",
@@ -334,6 +341,114 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+BWD_METRIC = "attention bwd TFLOP/s (visible pairs, 10*D*Hq per pair) + % of bf16 MFMA peak, 1 MI355X"
+
+
+def bench_backward(args, w, dev):
+    """attn_bwd over every shard of the all-gather strategy: shard r's queries
+    (striped reorder) against the whole gathered K/V, with dout ~ N(0, 1).
+    One step computes dq of every query and each shard's dk/dv contribution
+    (what a reduce-scatter would sum across devices).  FLOPs count only visible
+    pairs, 10 * head_dim * Hq per pair (the five products S, dP, dV, dK, dQ)."""
+    if w.cp_size > 1:
+        w = dataclasses.replace(w, reorder="striped", stripe=args.stripe)
+    desc = w.describe()
+    if w.cp_size > 1:
+        desc = desc.replace(f"{w.cp_size} shards x {w.cp_size} ring steps",
+                            f"{w.cp_size} shards (stripe {w.stripe}), each against the whole "
+                            "gathered K/V in one call")
+    log(f"backward, workload {w.cfg} {w.name}: {desc}")
+    q, k, v, ids, pos = make_inputs(w, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 17)
+    do = torch.randn(q.shape, generator=g, device=dev).to(torch.bfloat16)
+    cp = max(1, w.cp_size)
+    if cp > 1:
+        q, k, v, ids, pos, do = (bosf.reorder(t, cp, w.reorder, w.stripe) for t in (q, k, v, ids, pos, do))
+    n = w.seq_len // cp
+    gdt = torch.float32 if args.grad_dtype == "f32" else torch.bfloat16
+    shards = []
+    for r in range(cp):
+        sl = slice(r * n, (r + 1) * n)
+        qs, ds = q[:, sl].contiguous(), do[:, sl].contiguous()
+        iq, pq = ids[:, sl], pos[:, sl]
+        o, lse = bosf.attn_fwd(qs, k, v, iq, pq, ids, pos, causal=w.causal, window=w.window)
+        dk = torch.empty(k.shape, dtype=gdt, device=dev)
+        dv = torch.empty(k.shape, dtype=gdt, device=dev)
+        dq = torch.empty(qs.shape, dtype=gdt, device=dev)
+        shards.append((qs, ds, iq, pq, o, lse, dq, dk, dv))
+    del q, do
+    bdesc = bosf.make_desc(w.batch, n, w.seq_len, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                           strides={"q_meta_batch_stride": ids.stride(0)})
+    wsp = torch.empty(bosf.bwd_workspace_size(bdesc), dtype=torch.uint8, device=dev)
+    log(f"backward workspace {wsp.numel() / 2**30:.2f} GiB")
+    _, pairs = bosf.classify_tiles(ids, pos, ids, pos, num_q_heads=w.num_q_heads,
+                                   num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                                   dtype=k.dtype, causal=w.causal, window=w.window)
+    visible = int(pairs.sum().item())
+    flops = 10.0 * w.head_dim * w.num_q_heads * visible
+    log(f"visible pairs {visible}, {flops / 1e12:.3f} TFLOP per backward step")
+    stream = torch.cuda.current_stream(dev)
+    evs = []
+
+    def step(record):
+        for (qs, ds, iq, pq, o, lse, dq, dk, dv) in shards:
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            bosf.attn_bwd(qs, k, v, iq, pq, ids, pos, o, lse, ds, causal=w.causal,
+                          window=w.window, grad_dtype=gdt, dq=dq, dk=dk, dv=dv, workspace=wsp)
+            if record:
+                e1 = torch.cuda.Event(enable_timing=True)
+                e1.record(stream)
+                evs.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1000.0 / args.steps
+    value = flops / (ms_step / 1000.0) / 1e12
+    calls = [a.elapsed_time(b) for a, b in evs]
+    call_ms = float(np.mean(calls))
+    achieved = flops / cp / (call_ms / 1000.0) / 1e12
+    log(f"{ms_step:.3f} ms/step, {value:.1f} TFLOP/s; attn_bwd {call_ms:.3f} ms per call")
+    line = {
+        "metric": BWD_METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "config": {"workload": f"{w.name} backward{' all-gather' if cp > 1 else ''}: {desc}",
+                   "batch": w.batch, "seq_len": w.seq_len, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "window": list(w.window), "cp_shards": cp, "reorder": w.reorder,
+                   "stripe": w.stripe, "grad_dtype": args.grad_dtype},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "attn_bwd call (prep, both classifications, packing, dq and "
+                               "dk/dv passes)",
+                     "per_launch_flops": flops / cp},
+        "cpu_baseline": None,
+        "detail": {"attn_bwd_calls_per_step": cp, "attn_bwd_avg_ms_per_call": call_ms,
+                   "visible_pairs_per_step": visible,
+                   "workspace_bytes": int(wsp.numel())},
     }
     print(json.dumps(line), flush=True)
 

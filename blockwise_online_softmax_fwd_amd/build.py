@@ -23,10 +23,8 @@ LIB = os.path.join(HERE, "libringattn.so")
 SOURCES = ["api.cpp", "classify.hip", "attn_bf16.hip", "attn_f32.hip", "merge.hip", "reorder.hip",
            "bwd.hip"]
 
-# Per-source code generation options.  The backward kernels keep their MFMA
-# accumulators in ordinary VGPRs: their scores feed VALU work every tile, and
-# the default accumulator-register form adds a copy per element and spills.
-EXTRA_FLAGS = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source code generation options (none at present).
+EXTRA_FLAGS: dict = {}
 
 ARCH = "gfx950"
 

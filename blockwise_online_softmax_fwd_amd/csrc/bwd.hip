@@ -22,9 +22,9 @@
 //  * dQ pass: the forward's workgroup shape and work lists.  Per key tile a
 //    wave forms S^T = K Q^T and dP^T = V dO^T, then dS^T, and accumulates
 //    dQ^T += K^T dS^T; S and dP never leave registers.
-//  * dK/dV pass: 4 waves, one per SIMD, each owning 32 keys of one K/V head
+//  * dK/dV pass: 8 waves, two per SIMD, each owning 32 keys of one K/V head
 //    (their K and V are the B operands, held in registers).  The work list of
-//    the 128-key tile (from the same classification kernels run with keys and
+//    the 256-key tile (from the same classification kernels run with keys and
 //    queries swapped) names the 32-query tiles that see it; every one of them
 //    is visited once per query head of the group, so the group's sum lands in
 //    registers and each key's gradients are written once, without atomics.
@@ -258,7 +258,6 @@ bwd_dq_kernel(BwdParams p) {
   constexpr int kSmemBytes = 2 * TILE > kStageBytes ? 2 * TILE : kStageBytes;
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   KvTile<D> &t0 = *reinterpret_cast<KvTile<D> *>(smem);
-  KvTile<D> &t1 = *reinterpret_cast<KvTile<D> *>(smem + TILE);
   float(*stage)[32][68] = reinterpret_cast<float(*)[32][68]>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -393,24 +392,23 @@ bwd_dq_kernel(BwdParams p) {
     }
   };
 
+  // Double-buffered loop with one body: tile it computes from buffer it & 1
+  // while tile it + 1 streams into the other.
+  auto buffer = [&](int i) -> KvTile<D> & {
+    return *reinterpret_cast<KvTile<D> *>(smem + i * TILE);
+  };
   if (n > 0) {
     issue(t0, entry_tile(0));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
-  for (int it = 0; it < n;) {
-    if (it + 1 < n) issue(t1, entry_tile(it + 1));
+  for (int it = 0; it < n; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < n) issue(buffer(cur ^ 1), entry_tile(it + 1));
     __builtin_amdgcn_sched_barrier(0);
-    compute(t0, entry_masked(it));
+    compute(buffer(cur), entry_masked(it));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (++it >= n) break;
-    if (it + 1 < n) issue(t0, entry_tile(it + 1));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(t1, entry_masked(it));
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    ++it;
   }
 
   // dQ = scale * (dQ^T)^T, through LDS in 64-column halves: 16-byte stores.
@@ -450,7 +448,7 @@ bwd_dq_kernel(BwdParams p) {
 // ----------------------------------------------------------------------------- dK/dV pass
 
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(64 * kBwdKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+__global__ __launch_bounds__(64 * kBwdKvWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dkdv_kernel(BwdParams p) {
   constexpr int W = kBwdKvWaves;
   constexpr int DC = D / 16;
@@ -459,13 +457,14 @@ bwd_dkdv_kernel(BwdParams p) {
   constexpr int BLK = (int)offsetof(QTile<D>, lse2);    // bytes of the four bf16 blocks
   static_assert(BLK % 1024 == 0, "tile blocks are loaded 1 KB per wave instruction");
   constexpr int CHUNKS = BLK / 1024;
-  constexpr int SROW = D + 4;     // staging row of one key, fp32
+  constexpr int SROW = 68;        // staging row: 64 fp32 columns of one key, padded
   constexpr int kStageBytes = W * 32 * SROW * 4;
-  constexpr int kSmemBytes = 2 * TILE > kStageBytes ? 2 * TILE : kStageBytes;
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  constexpr int kTileBytes = 2 * TILE > kStageBytes ? 2 * TILE : kStageBytes;
+  constexpr int kVBytes = W * 32 * kRowN<D> * 2;   // the workgroup's V rows, [key][d] padded
+  __shared__ __attribute__((aligned(16))) char smem[kTileBytes + kVBytes];
   QTile<D> &t0 = *reinterpret_cast<QTile<D> *>(smem);
-  QTile<D> &t1 = *reinterpret_cast<QTile<D> *>(smem + TILE);
   float(*stage)[32][SROW] = reinterpret_cast<float(*)[32][SROW]>(smem);
+  bf16 *vrows = reinterpret_cast<bf16 *>(smem + kTileBytes);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar tile offsets
@@ -512,17 +511,22 @@ bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // B operands: the lane's key row of K and of V, 8 head_dim values per step.
-  bf16x8 kf[DC], vf[DC];
+  // B operands: the lane's key row of K in registers, 8 head_dim values per
+  // step; the wave's V rows go to LDS (row wave*32 + col, same 8-value pieces)
+  // and are read back per visit, which keeps the persistent register state at
+  // K plus the two accumulators.
+  bf16x8 kf[DC];
+  bf16 *const vmine = vrows + (wave * 32 + col) * kRowN<D> + 8 * half;
   {
     const int64_t rel = (int64_t)key * p.hkv * D + (int64_t)g * D + 8 * half;
     const bf16 *krow = (const bf16 *)p.k + b * p.kv_bs + rel;
     const bf16 *vrow = (const bf16 *)p.v + b * p.kv_bs + rel;
+    const bool ld = kvalid && n > 0;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      const bool ld = kvalid && n > 0;
       kf[c] = ld ? *(const bf16x8 *)(krow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      vf[c] = ld ? *(const bf16x8 *)(vrow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      *(bf16x8 *)(vmine + 16 * c) =
+          ld ? *(const bf16x8 *)(vrow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
   }
   KeyMask km;
@@ -546,23 +550,24 @@ bwd_dkdv_kernel(BwdParams p) {
   auto compute = [&](const QTile<D> &tl, bool masked) __attribute__((always_inline)) {
     // S = Q K^T and dP = dO V^T for the 32 queries of the tile: lane = key,
     // element r of the accumulator = query row 8(r/4) + 4 half + r%4.
-    f32x16 s, dp;
+    f32x16 s = {}, dp = {};
     {
-      bf16x8 aq[DC], ag[DC];
+      const bf16 *qa = tl.qn + col * kRowN<D> + 8 * half;
+      const bf16 *ga = tl.don + col * kRowN<D> + 8 * half;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        aq[c] = *(const bf16x8 *)(tl.qn + col * kRowN<D> + 16 * c + 8 * half);
-        ag[c] = *(const bf16x8 *)(tl.don + col * kRowN<D> + 16 * c + 8 * half);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(qa + 16 * c), kf[c], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(ga + 16 * c),
+                                                     *(const bf16x8 *)(vmine + 16 * c), dp, 0, 0, 0);
       }
-      const f32x16 zero16 = {};
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0], kf[0], zero16, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[0], vf[0], zero16, 0, 0, 0);
+      // operand reads three at a time, each group followed by its two products
 #pragma unroll
-      for (int c = 1; c < DC; ++c) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[c], kf[c], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[c], vf[c], dp, 0, 0, 0);
+      for (int c = 0; c < DC; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (masked) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -591,6 +596,7 @@ bwd_dkdv_kernel(BwdParams p) {
         df[r >> 3][r & 7] = (bf16)(pv * (dp[r] - d4[e]));
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end).
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch)
@@ -602,58 +608,66 @@ bwd_dkdv_kernel(BwdParams p) {
         dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[ch], dv[db], 0, 0, 0);
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, df[ch], dk[db], 0, 0, 0);
       }
+#pragma unroll
+    for (int i = 0; i < 2 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Double-buffered loop with one body: visit it computes from buffer it & 1
+  // while visit it + 1 streams into the other (a single copy of the body keeps
+  // the accumulators in one set of registers).
+  auto buffer = [&](int i) -> QTile<D> & {
+    return *reinterpret_cast<QTile<D> *>(smem + i * TILE);
+  };
   if (n > 0) {
     issue(t0, visit_tile(0));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
-  for (int it = 0; it < n;) {
-    if (it + 1 < n) issue(t1, visit_tile(it + 1));
+  for (int it = 0; it < n; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < n) issue(buffer(cur ^ 1), visit_tile(it + 1));
     __builtin_amdgcn_sched_barrier(0);
-    compute(t0, visit_masked(it));
+    compute(buffer(cur), visit_masked(it));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (++it >= n) break;
-    if (it + 1 < n) issue(t0, visit_tile(it + 1));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(t1, visit_masked(it));
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    ++it;
   }
 
   // dK = scale * (dK^T)^T and dV = (dV^T)^T through LDS: each wave stages its
-  // 32 keys x D, then writes whole rows, 16 bytes per lane.
+  // 32 keys x 64 columns at a time, then writes 4 whole 256-byte row pieces
+  // per pass, 16 bytes per lane.
   const int key0 = kt * kBwdKvTile + wave * 32;
+  const int rsub = lane >> 4, c4 = (lane & 15) * 4;
   auto store = [&](const f32x16 (&acc)[DB], float mul, void *dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int hd = 0; hd < DB / 2; ++hd) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 val;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = acc[db][4 * r4 + e] * mul;
-        *(f32x4 *)&stage[wave][col][db * 32 + 8 * r4 + 4 * half] = val;
-      }
-    constexpr int LPR = D / 4;            // lanes per key row
-    constexpr int RPP = 64 / LPR;         // rows per pass
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 val;
 #pragma unroll
-    for (int pass = 0; pass < 32 / RPP; ++pass) {
-      const int kr = pass * RPP + lane / LPR;
-      const int c = (lane % LPR) * 4;
-      const int t = key0 + kr;
-      const f32x4 val = *(const f32x4 *)&stage[wave][kr][c];
-      if (t < p.tk) {
-        const int64_t rel = (int64_t)t * p.hkv * D + (int64_t)g * D + c;
-        if (OUT_BF16) {
-          bf16x4 hv;
+          for (int e = 0; e < 4; ++e) val[e] = acc[2 * hd + j][4 * r4 + e] * mul;
+          *(f32x4 *)&stage[wave][col][32 * j + 8 * r4 + 4 * half] = val;
+        }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) hv[e] = (bf16)val[e];
-          *(bf16x4 *)((bf16 *)dst + b * p.dkv_bs + rel) = hv;
-        } else {
-          *(f32x4 *)((float *)dst + b * p.dkv_bs + rel) = val;
+      for (int pass = 0; pass < 8; ++pass) {
+        const int kr = 4 * pass + rsub;
+        const int t = key0 + kr;
+        const f32x4 val = *(const f32x4 *)&stage[wave][kr][c4];
+        if (t < p.tk) {
+          const int64_t rel = (int64_t)t * p.hkv * D + (int64_t)g * D + 64 * hd + c4;
+          if (OUT_BF16) {
+            bf16x4 hv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hv[e] = (bf16)val[e];
+            *(bf16x4 *)((bf16 *)dst + b * p.dkv_bs + rel) = hv;
+          } else {
+            *(f32x4 *)((float *)dst + b * p.dkv_bs + rel) = val;
+          }
         }
       }
     }

@@ -117,7 +117,7 @@ hipError_t launch_reorder(const void *src, void *dst, int32_t batch, int32_t seq
 // ----------------------------------------------------------------------------- backward
 
 constexpr int kBwdQTile = 32;    // queries per packed tile of the dK/dV pass
-constexpr int kBwdKvWaves = 4;   // dK/dV workgroup: 4 waves of 32 keys
+constexpr int kBwdKvWaves = 8;   // dK/dV workgroup: 8 waves of 32 keys
 constexpr int kBwdKvTile = 32 * kBwdKvWaves;
 
 // Bytes of one packed K/V tile of the dQ pass (K, V and K^T blocks, ids and
