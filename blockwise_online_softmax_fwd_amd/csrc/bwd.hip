@@ -26,8 +26,9 @@
 //    (their K and V are the B operands, held in registers).  The work list of
 //    the 256-key tile (from the same classification kernels run with keys and
 //    queries swapped) names the 32-query tiles that see it; every one of them
-//    is visited once per query head of the group, so the group's sum lands in
-//    registers and each key's gradients are written once, without atomics.
+//    is visited once per query head of the group (head by head), so the
+//    group's sum lands in registers and each key's gradients are written once,
+//    without atomics.
 //    Per visit: S = Q K^T and dP = dO V^T (lane = key, rows = queries), then
 //    dV^T += dO^T P and dK^T += Q^T dS.
 #include <hip/hip_runtime.h>
@@ -485,14 +486,18 @@ bwd_dkdv_kernel(BwdParams p) {
   typedef const __attribute__((address_space(4))) uint32_t *const_list_t;
   const const_list_t lst = (const_list_t)(p.tlist + row * p.tnq);
 
+  // Visit it = (head it / nq of the group, query tile it % nq of the list):
+  // head by head, so workgroups of neighbouring key tiles (dealt to the same
+  // XCD) read the same Q tiles within a few visits of each other.
   auto visit_tile = [&](int it) {
-    const int qtile = (int)(lst[it / p.group] & 0x7fffffffu);
-    const int h = g * p.group + it % p.group;
+    const int hi = it / nq;
+    const int qtile = (int)(lst[it - hi * nq] & 0x7fffffffu);
+    const int h = g * p.group + hi;
     return ((int64_t)b * p.hq + h) * p.tnq + qtile;
   };
   const bool ragged_q = (p.tq % BQ) != 0;
   auto visit_masked = [&](int it) {
-    const uint32_t e = lst[it / p.group];
+    const uint32_t e = lst[it % nq];
     return (e >> 31) != 0 || (ragged_q && (int)(e & 0x7fffffffu) == p.tnq - 1) || !kvalid;
   };
   auto issue = [&](QTile<D> &dst, int64_t tile) __attribute__((always_inline)) {
