@@ -37,10 +37,22 @@ constexpr int64_t kMaxKeyTiles = 32768;  // class bytes of one query tile fit in
 
 struct Resolved {
   int64_t q_bs, kv_bs, o_bs, lse_bs, qm_bs, km_bs;
+  int64_t q_ts, kv_ts, o_ts;  // token strides (elements)
   int32_t bm, bn, nqt, nkt, nt;
 };
 
 int64_t pick(int64_t given, int64_t dense) { return given == 0 ? dense : given; }
+
+// True if B x T rows of L elements at batch stride bs and token stride ts never
+// overlap, with one stride nesting the other (the layouts the header lists).
+bool nested(int64_t B, int64_t T, int64_t L, int64_t bs, int64_t ts) {
+  if (B <= 0 || T <= 0 || L <= 0) return true;
+  if (B == 1 && T == 1) return true;
+  if (B == 1) return ts >= L;
+  if (T == 1) return bs >= L;
+  if (bs >= ts) return ts >= L && bs >= (T - 1) * ts + L;
+  return bs >= L && ts >= (B - 1) * bs + L;
+}
 
 ra_status check_desc(const ra_attn_desc *d, Resolved *r) {
   if (!d) return fail(RA_ERR_NULL, "desc is NULL");
@@ -66,21 +78,25 @@ ra_status check_desc(const ra_attn_desc *d, Resolved *r) {
                 d->window_right);
   const int64_t B = d->batch, Tq = d->q_len, Tk = d->kv_len, Hq = d->num_q_heads,
                 Hkv = d->num_kv_heads, D = d->head_dim;
-  const int64_t strides[6] = {d->q_batch_stride,   d->kv_batch_stride,     d->o_batch_stride,
-                              d->lse_batch_stride, d->q_meta_batch_stride, d->kv_meta_batch_stride};
-  for (int i = 0; i < 6; ++i)
-    if (strides[i] < 0) return fail(RA_ERR_SHAPE, "batch strides must be >= 0");
-  r->q_bs = pick(d->q_batch_stride, Tq * Hq * D);
-  r->kv_bs = pick(d->kv_batch_stride, Tk * Hkv * D);
-  r->o_bs = pick(d->o_batch_stride, Tq * Hq * D);
+  const int64_t strides[9] = {d->q_batch_stride,   d->kv_batch_stride,     d->o_batch_stride,
+                              d->lse_batch_stride, d->q_meta_batch_stride, d->kv_meta_batch_stride,
+                              d->q_token_stride,   d->kv_token_stride,     d->o_token_stride};
+  for (int i = 0; i < 9; ++i)
+    if (strides[i] < 0) return fail(RA_ERR_SHAPE, "batch and token strides must be >= 0");
+  r->q_ts = pick(d->q_token_stride, Hq * D);
+  r->kv_ts = pick(d->kv_token_stride, Hkv * D);
+  r->o_ts = pick(d->o_token_stride, Hq * D);
+  r->q_bs = pick(d->q_batch_stride, Tq * r->q_ts);
+  r->kv_bs = pick(d->kv_batch_stride, Tk * r->kv_ts);
+  r->o_bs = pick(d->o_batch_stride, Tq * r->o_ts);
   r->lse_bs = pick(d->lse_batch_stride, Tq * Hq);
   r->qm_bs = pick(d->q_meta_batch_stride, Tq);
   r->km_bs = pick(d->kv_meta_batch_stride, Tk);
-  if (B > 1) {
-    if (r->q_bs < Tq * Hq * D || r->o_bs < Tq * Hq * D || r->kv_bs < Tk * Hkv * D ||
-        r->lse_bs < Tq * Hq || r->qm_bs < Tq || r->km_bs < Tk)
-      return fail(RA_ERR_SHAPE, "a batch stride is smaller than one batch row");
-  }
+  if (!nested(B, Tq, Hq * D, r->q_bs, r->q_ts) || !nested(B, Tq, Hq * D, r->o_bs, r->o_ts) ||
+      !nested(B, Tk, Hkv * D, r->kv_bs, r->kv_ts))
+    return fail(RA_ERR_SHAPE, "q, k/v or o strides let two (batch, token) rows overlap");
+  if (B > 1 && (r->lse_bs < Tq * Hq || r->qm_bs < Tq || r->km_bs < Tk))
+    return fail(RA_ERR_SHAPE, "a batch stride is smaller than one batch row");
   if (d->qkv_dtype == RA_BF16) {
     r->nt = ra::bf16_token_subtiles(d->num_q_heads / d->num_kv_heads);
     r->bm = 32 * r->nt;
@@ -110,6 +126,35 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
 size_t span_bytes(int64_t batch, int64_t bs, int64_t row_elems, size_t es) {
   if (batch <= 0 || row_elems <= 0) return 0;
   return (size_t)((batch - 1) * bs + row_elems) * es;
+}
+
+// Bytes from the first to one past the last element of a [B, T, L] tensor at
+// batch stride bs and token stride ts (elements of size es).
+size_t span_bytes2(int64_t batch, int64_t tokens, int64_t L, int64_t bs, int64_t ts, size_t es) {
+  if (batch <= 0 || tokens <= 0 || L <= 0) return 0;
+  return (size_t)((batch - 1) * bs + (tokens - 1) * ts + L) * es;
+}
+
+// Overlap of two [B, T, L] tensors that share their batch and token strides
+// (bytes: sb, st; rows of la and lb bytes, Ta and Tb tokens), as when rows of
+// several tensors sit side by side in one packed buffer.  Exact when the outer
+// stride is a multiple of the inner one; otherwise the spans are compared.
+bool rows_overlap(const void *a, int64_t Ta, int64_t la, const void *b, int64_t Tb, int64_t lb,
+                  int64_t batch, int64_t sb, int64_t st) {
+  if (!a || !b || batch <= 0 || Ta <= 0 || Tb <= 0 || la <= 0 || lb <= 0) return false;
+  if ((uintptr_t)a > (uintptr_t)b) {
+    const void *tp = a; a = b; b = tp;
+    int64_t t = Ta; Ta = Tb; Tb = t;
+    t = la; la = lb; lb = t;
+  }
+  const int64_t d = (int64_t)((uintptr_t)b - (uintptr_t)a);
+  if (d >= (batch - 1) * sb + (Ta - 1) * st + la) return false;
+  const int64_t T = Ta > Tb ? Ta : Tb;
+  const int64_t inner = batch > 1 && T > 1 ? (sb < st ? sb : st) : (T > 1 ? st : sb);
+  const int64_t outer = sb < st ? st : sb;
+  if (inner <= 0 || (batch > 1 && T > 1 && outer % inner)) return true;
+  const int64_t r = d % inner;
+  return !(r >= la && r + lb <= inner);
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -240,13 +285,16 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
   const size_t es = dtype_size(d->qkv_dtype), os = dtype_size(d->out_dtype);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return fail(RA_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
-  if ((r.q_bs * es) % 16 || (r.kv_bs * es) % 16 || (r.o_bs * os) % 16)
-    return fail(RA_ERR_ALIGN, "batch strides of q, k, v and o must be multiples of 16 bytes");
+  if ((r.q_bs * es) % 16 || (r.kv_bs * es) % 16 || (r.o_bs * os) % 16 || (r.q_ts * es) % 16 ||
+      (r.kv_ts * es) % 16 || (r.o_ts * os) % 16)
+    return fail(RA_ERR_ALIGN, "batch and token strides of q, k, v and o must be multiples of 16 bytes");
   if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
   const int64_t D = d->head_dim;
-  const size_t q_span = span_bytes(d->batch, r.q_bs, (int64_t)d->q_len * d->num_q_heads * D, es);
-  const size_t kv_span = span_bytes(d->batch, r.kv_bs, (int64_t)d->kv_len * d->num_kv_heads * D, es);
-  const size_t o_span = span_bytes(d->batch, r.o_bs, (int64_t)d->q_len * d->num_q_heads * D, os);
+  const int64_t B = d->batch, Tq = d->q_len, Tk = d->kv_len;
+  const int64_t Lq = (int64_t)d->num_q_heads * D, Lk = (int64_t)d->num_kv_heads * D;
+  const size_t q_span = span_bytes2(B, Tq, Lq, r.q_bs, r.q_ts, es);
+  const size_t kv_span = span_bytes2(B, Tk, Lk, r.kv_bs, r.kv_ts, es);
+  const size_t o_span = span_bytes2(B, Tq, Lq, r.o_bs, r.o_ts, os);
   const size_t l_span = span_bytes(d->batch, r.lse_bs, (int64_t)d->q_len * d->num_q_heads, 4);
   if (overlaps(o, o_span, q, q_span) || overlaps(o, o_span, k, kv_span) ||
       overlaps(o, o_span, v, kv_span) || overlaps(lse, l_span, o, o_span) ||
@@ -260,15 +308,15 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
     if (acc->o_batch_stride < 0 || acc->lse_batch_stride < 0)
       return fail(RA_ERR_SHAPE, "partial batch strides must be >= 0");
     const int64_t rows = (int64_t)d->q_len * d->num_q_heads;
-    acc_o_bs = pick(acc->o_batch_stride, rows * D);
+    acc_o_bs = pick(acc->o_batch_stride, Tq * r.o_ts);
     acc_lse_bs = pick(acc->lse_batch_stride, rows);
-    if (d->batch > 1 && (acc_o_bs < rows * D || acc_lse_bs < rows))
+    if (!nested(B, Tq, Lq, acc_o_bs, r.o_ts) || (d->batch > 1 && acc_lse_bs < rows))
       return fail(RA_ERR_SHAPE, "a partial batch stride is smaller than one batch row");
     if (has_q && (!acc->o || !acc->lse)) return fail(RA_ERR_NULL, "partial o or lse is NULL");
     const size_t as = dtype_size(acc->dtype);
     if (!aligned(acc->o, 16) || (acc_o_bs * as) % 16 || !aligned(acc->lse, 4))
       return fail(RA_ERR_ALIGN, "partial o must be 16-byte aligned (lse 4-byte)");
-    const size_t a_span = span_bytes(d->batch, acc_o_bs, rows * D, as);
+    const size_t a_span = span_bytes2(B, Tq, Lq, acc_o_bs, r.o_ts, as);
     const size_t al_span = span_bytes(d->batch, acc_lse_bs, rows, 4);
     const bool same_o = acc->o == o && acc->dtype == d->out_dtype && acc_o_bs == r.o_bs;
     const bool same_l = acc->lse == lse && acc_lse_bs == r.lse_bs;
@@ -303,6 +351,9 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
   p.kv_bs = r.kv_bs;
   p.o_bs = r.o_bs;
   p.lse_bs = r.lse_bs;
+  p.q_ts = r.q_ts;
+  p.kv_ts = r.kv_ts;
+  p.o_ts = r.o_ts;
   p.qm_bs = r.qm_bs;
   p.km_bs = r.km_bs;
   p.batch = d->batch;
@@ -335,6 +386,7 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
     pk.vpack = (char *)workspace + L.vpack;
     pk.mpack = (int32_t *)((char *)workspace + L.mpack);
     pk.kv_bs = r.kv_bs;
+    pk.kv_ts = r.kv_ts;
     pk.km_bs = r.km_bs;
     pk.batch = d->batch;
     pk.tk = d->kv_len;
@@ -546,31 +598,41 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   const void *p16[8] = {q, k, v, o, dout, dq, dk, dv};
   for (const void *ptr : p16)
     if (!aligned(ptr, 16)) return fail(RA_ERR_ALIGN, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
-  if ((r.q_bs * 2) % 16 || (r.kv_bs * 2) % 16 || (r.o_bs * os) % 16 || (r.o_bs * 2) % 16 ||
-      (r.q_bs * gs) % 16 || (r.kv_bs * gs) % 16)
-    return fail(RA_ERR_ALIGN, "batch strides must be multiples of 16 bytes for every tensor using them");
+  const int64_t sts[5] = {r.q_bs, r.kv_bs, r.q_ts, r.kv_ts, 0};
+  for (int i = 0; i < 4; ++i)
+    if ((sts[i] * 2) % 16 || (sts[i] * (int64_t)gs) % 16)
+      return fail(RA_ERR_ALIGN, "batch and token strides must be multiples of 16 bytes for every tensor using them");
+  if ((r.o_bs * os) % 16 || (r.o_bs * 2) % 16 || (r.o_ts * os) % 16 || (r.o_ts * 2) % 16)
+    return fail(RA_ERR_ALIGN, "batch and token strides must be multiples of 16 bytes for every tensor using them");
   if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
   const int64_t D = d->head_dim;
-  const int64_t qe = (int64_t)d->q_len * d->num_q_heads * D, ke = (int64_t)d->kv_len * d->num_kv_heads * D;
-  const size_t q_span = span_bytes(d->batch, r.q_bs, qe, 2);
-  const size_t kv_span = span_bytes(d->batch, r.kv_bs, ke, 2);
-  const size_t o_span = span_bytes(d->batch, r.o_bs, qe, os);
-  const size_t do_span = span_bytes(d->batch, r.o_bs, qe, 2);
-  const size_t l_span = span_bytes(d->batch, r.lse_bs, (int64_t)d->q_len * d->num_q_heads, 4);
-  const size_t dq_span = span_bytes(d->batch, r.q_bs, qe, gs);
-  const size_t dkv_span = span_bytes(d->batch, r.kv_bs, ke, gs);
+  const int64_t B = d->batch, Tq = d->q_len, Tk = d->kv_len;
+  const int64_t Lq = (int64_t)d->num_q_heads * D, Lk = (int64_t)d->num_kv_heads * D;
+  const size_t q_span = span_bytes2(B, Tq, Lq, r.q_bs, r.q_ts, 2);
+  const size_t kv_span = span_bytes2(B, Tk, Lk, r.kv_bs, r.kv_ts, 2);
+  const size_t o_span = span_bytes2(B, Tq, Lq, r.o_bs, r.o_ts, os);
+  const size_t do_span = span_bytes2(B, Tq, Lq, r.o_bs, r.o_ts, 2);
+  const size_t l_span = span_bytes(B, r.lse_bs, Tq * d->num_q_heads, 4);
+  const size_t dq_span = span_bytes2(B, Tq, Lq, r.q_bs, r.q_ts, gs);
+  const size_t dkv_span = span_bytes2(B, Tk, Lk, r.kv_bs, r.kv_ts, gs);
   const void *ins[6] = {q, k, v, o, lse, dout};
   const size_t in_span[6] = {q_span, kv_span, kv_span, o_span, l_span, do_span};
   const void *outs[3] = {dq, dk, dv};
   const size_t out_span[3] = {dq_span, dkv_span, dkv_span};
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < 3; ++i)
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], out_span[i], ins[j], in_span[j]))
         return fail(RA_ERR_ALIAS, "a gradient buffer overlaps an input");
-    for (int j = i + 1; j < 3; ++j)
-      if (overlaps(outs[i], out_span[i], outs[j], out_span[j]))
-        return fail(RA_ERR_ALIAS, "gradient buffers overlap each other");
-  }
+  // The gradients may share one packed buffer (rows side by side at equal
+  // strides, e.g. dk/dv of a packed K/V layout); otherwise their spans must not meet.
+  const int64_t g = (int64_t)gs;
+  if (rows_overlap(dk, Tk, Lk * g, dv, Tk, Lk * g, B, r.kv_bs * g, r.kv_ts * g))
+    return fail(RA_ERR_ALIAS, "dk and dv overlap");
+  const bool same = r.q_bs == r.kv_bs && r.q_ts == r.kv_ts;
+  for (void *kg : {dk, dv})
+    if (same ? rows_overlap(dq, Tq, Lq * g, kg, Tk, Lk * g, B, r.q_bs * g, r.q_ts * g)
+             : overlaps(dq, dq_span, kg, dkv_span))
+      return fail(RA_ERR_ALIAS, "dq overlaps dk or dv");
   if (!has_q && !has_k) return RA_OK;
   const ra::BwdLayout L = bwd_layout_of(d, r, bs);
   if (L.total > 0 && !workspace)
@@ -612,6 +674,9 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   p.km_bs = r.km_bs;
   p.dq_bs = r.q_bs;
   p.dkv_bs = r.kv_bs;
+  p.q_ts = r.q_ts;
+  p.kv_ts = r.kv_ts;
+  p.o_ts = r.o_ts;
   p.batch = d->batch;
   p.tq = d->q_len;
   p.tk = d->kv_len;

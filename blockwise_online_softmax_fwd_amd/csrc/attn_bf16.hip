@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(PackParams p) {
   const int64_t tile = ((int64_t)b * p.hkv + g) * p.nkt + kt;
   const bf16 *kb = (const bf16 *)p.k + b * p.kv_bs + (int64_t)g * D;
   const bf16 *vb = (const bf16 *)p.v + b * p.kv_bs + (int64_t)g * D;
-  const int64_t tok = (int64_t)p.hkv * D;
+  const int64_t tok = p.kv_ts;
   bf16 *kout = (bf16 *)p.kpack + tile * (BN * D);
   bf16 *vout = (bf16 *)p.vpack + tile * (BN * D);
   const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -216,7 +216,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
   // Q fragment (B operand of S^T = K Q^T): 8 consecutive head_dim values per step.
   bf16x8 qf[DC];
   {
-    const bf16 *qrow = (const bf16 *)p.q + b * p.q_bs + (int64_t)tq * p.hq * D + (int64_t)h * D +
+    const bf16 *qrow = (const bf16 *)p.q + b * p.q_bs + (int64_t)tq * p.q_ts + (int64_t)h * D +
                        8 * half;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
@@ -412,7 +412,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
       const int t = tq0 + qrow;
       f32x4 val = *(const f32x4 *)&stage[wave][qrow][c4];
       if (t < p.tq) {
-        const int64_t rel = (int64_t)t * p.hq * D + (int64_t)h * D + 64 * hd + c4;
+        const int64_t rel = (int64_t)t * p.o_ts + (int64_t)h * D + 64 * hd + c4;
         const float wa = stage_w[wave][qrow];
         if (wa != 0.0f) {
           f32x4 a;

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
   const bool qvalid = tq < p.tq;
 
   float q[DH], o[DH];
-  const float *qrow = (const float *)p.q + b * p.q_bs + (int64_t)tq * p.hq * D + (int64_t)h * D +
+  const float *qrow = (const float *)p.q + b * p.q_bs + (int64_t)tq * p.q_ts + (int64_t)h * D +
                       half * DH;
   for (int d = 0; d < DH; ++d) {
     q[d] = qvalid ? qrow[d] : 0.0f;
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
   const uint32_t *lst = p.list + row * p.nkt;
   const float *kb = (const float *)p.k + b * p.kv_bs + (int64_t)g * D;
   const float *vb = (const float *)p.v + b * p.kv_bs + (int64_t)g * D;
-  const int64_t kv_tok = (int64_t)p.hkv * D;
+  const int64_t kv_tok = p.kv_ts;
   const bool ragged = (p.tk % BN) != 0;
 
   float m = -INFINITY, z = 0.0f;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
   const float l_own = live ? m + logf(z) : -INFINITY;
   float w_own = live ? 1.0f / z : 0.0f;
   float w_acc = 0.0f, l_out = l_own;
-  const int64_t rel = (int64_t)tq * p.hq * D + (int64_t)h * D + half * DH;
+  const int64_t rel = (int64_t)tq * p.o_ts + (int64_t)h * D + half * DH;
   if (p.acc_mode) {
     const float la = p.acc_lse[b * p.acc_lse_bs + (int64_t)tq * p.hq + h];
     l_out = lse_add(l_own, la);

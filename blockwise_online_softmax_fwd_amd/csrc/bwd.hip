@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   for (int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR; r < rows;
        r += (int64_t)gridDim.x * RPB) {
     const int64_t b = r / per_b, rr = r - b * per_b;   // rr = t * hq + h
-    const int64_t col = rr * D + sub * 4;
+    const int64_t t = rr / p.hq, h = rr - t * p.hq;
+    const int64_t col = t * p.o_ts + h * D + sub * 4;
     const bf16x4 dov = *(const bf16x4 *)((const bf16 *)p.dout + b * p.do_bs + col);
     float dot = 0.0f;
     if (OBF) {
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void bwd_pack_kv_kernel(BwdParams p) {
   KvTile<D> *out = (KvTile<D> *)((char *)p.kvpack + tile * sizeof(KvTile<D>));
   const bf16 *kb = (const bf16 *)p.k + b * p.kv_bs + (int64_t)g * D;
   const bf16 *vb = (const bf16 *)p.v + b * p.kv_bs + (int64_t)g * D;
-  const int64_t tok = (int64_t)p.hkv * D;
+  const int64_t tok = p.kv_ts;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int u = tid; u < BN * RN; u += 256) {
     const int r = u / RN, c = u % RN;
@@ -171,14 +172,13 @@ __global__ __launch_bounds__(256) void bwd_pack_q_kernel(BwdParams p) {
   QTile<D> *out = (QTile<D> *)((char *)p.qpack + tile * sizeof(QTile<D>));
   const bf16 *qb = (const bf16 *)p.q + b * p.q_bs + (int64_t)h * D;
   const bf16 *gb = (const bf16 *)p.dout + b * p.do_bs + (int64_t)h * D;
-  const int64_t tok = (int64_t)p.hq * D;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int u = tid; u < BQ * RN; u += 256) {
     const int r = u / RN, c = u % RN;
     const int t = qt * BQ + r;
     const bool in = t < p.tq && c < DV;
-    const u32x4 qv = in ? *(const u32x4 *)(qb + t * tok + c * 8) : zero;
-    const u32x4 gv = in ? *(const u32x4 *)(gb + t * tok + c * 8) : zero;
+    const u32x4 qv = in ? *(const u32x4 *)(qb + t * p.q_ts + c * 8) : zero;
+    const u32x4 gv = in ? *(const u32x4 *)(gb + t * p.o_ts + c * 8) : zero;
     *(u32x4 *)(out->qn + u * 8) = qv;
     *(u32x4 *)(out->don + u * 8) = gv;
     if (c < DV) {
@@ -306,9 +306,9 @@ bwd_dq_kernel(BwdParams p) {
   // values per step.
   bf16x8 qf[DC], gf[DC];
   {
-    const int64_t rel = (int64_t)tq * p.hq * D + (int64_t)h * D + 8 * half;
-    const bf16 *qrow = (const bf16 *)p.q + b * p.q_bs + rel;
-    const bf16 *grow = (const bf16 *)p.dout + b * p.do_bs + rel;
+    const bf16 *qrow = (const bf16 *)p.q + b * p.q_bs + (int64_t)tq * p.q_ts + (int64_t)h * D + 8 * half;
+    const bf16 *grow = (const bf16 *)p.dout + b * p.do_bs + (int64_t)tq * p.o_ts + (int64_t)h * D +
+                       8 * half;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       const bool ld = qvalid && n > 0;
@@ -432,7 +432,7 @@ bwd_dq_kernel(BwdParams p) {
       const int t = tq0 + qrow;
       const f32x4 val = *(const f32x4 *)&stage[wave][qrow][c4];
       if (t < p.tq) {
-        const int64_t rel = (int64_t)t * p.hq * D + (int64_t)h * D + 64 * hd + c4;
+        const int64_t rel = (int64_t)t * p.q_ts + (int64_t)h * D + 64 * hd + c4;
         if (OUT_BF16) {
           bf16x4 hv;
 #pragma unroll
@@ -523,7 +523,7 @@ bwd_dkdv_kernel(BwdParams p) {
   bf16x8 kf[DC];
   bf16 *const vmine = vrows + (wave * 32 + col) * kRowN<D> + 8 * half;
   {
-    const int64_t rel = (int64_t)key * p.hkv * D + (int64_t)g * D + 8 * half;
+    const int64_t rel = (int64_t)key * p.kv_ts + (int64_t)g * D + 8 * half;
     const bf16 *krow = (const bf16 *)p.k + b * p.kv_bs + rel;
     const bf16 *vrow = (const bf16 *)p.v + b * p.kv_bs + rel;
     const bool ld = kvalid && n > 0;
@@ -664,7 +664,7 @@ bwd_dkdv_kernel(BwdParams p) {
         const int t = key0 + kr;
         const f32x4 val = *(const f32x4 *)&stage[wave][kr][c4];
         if (t < p.tk) {
-          const int64_t rel = (int64_t)t * p.hkv * D + (int64_t)g * D + 64 * hd + c4;
+          const int64_t rel = (int64_t)t * p.kv_ts + (int64_t)g * D + 64 * hd + c4;
           if (OUT_BF16) {
             bf16x4 hv;
 #pragma unroll

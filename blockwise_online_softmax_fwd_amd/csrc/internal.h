@@ -55,6 +55,7 @@ struct PackParams {
   void *kpack, *vpack;
   int32_t *mpack;
   int64_t kv_bs, km_bs;
+  int64_t kv_ts;             // token stride of K and V (elements)
   int32_t batch, tk, hkv, nkt;
 };
 hipError_t launch_pack_kv(const PackParams &p, int32_t head_dim, hipStream_t stream);
@@ -69,6 +70,7 @@ struct AttnParams {
   const void *kpack, *vpack;   // bf16 path: packed tiles written by pack_kv
   const int32_t *mpack;
   int64_t q_bs, kv_bs, o_bs, lse_bs, qm_bs, km_bs;  // batch strides (elements)
+  int64_t q_ts, kv_ts, o_ts;  // token strides (elements); the running partial has o's
   int32_t batch, tq, tk, hq, hkv, group;
   int32_t nqt, nkt;
   float scale;       // score scale
@@ -151,6 +153,7 @@ struct BwdParams {
   const int32_t *tcount;
   void *kvpack, *qpack;
   int64_t q_bs, kv_bs, o_bs, do_bs, lse_bs, qm_bs, km_bs, dq_bs, dkv_bs;
+  int64_t q_ts, kv_ts, o_ts;           // token strides: dq like q, dk/dv like k, dO like o
   int32_t batch, tq, tk, hq, hkv, group;
   int32_t nqt, nkt;                    // dQ schedule tiles
   int32_t tnk, tnq;                    // dK/dV schedule: key tiles (128), query tiles (32)

@@ -44,7 +44,8 @@ class AttnDesc(ctypes.Structure):
         (n, ctypes.c_int32) for n in ("causal", "window_left", "window_right")] + [
         (n, ctypes.c_int64) for n in (
             "q_batch_stride", "kv_batch_stride", "o_batch_stride", "lse_batch_stride",
-            "q_meta_batch_stride", "kv_meta_batch_stride")]
+            "q_meta_batch_stride", "kv_meta_batch_stride", "q_token_stride", "kv_token_stride",
+            "o_token_stride")]
 
 
 class Partial(ctypes.Structure):
@@ -137,6 +138,20 @@ def _batch_stride(t, inner_dims: int) -> int:
     return t.stride(0) if t.size(0) > 1 else 0
 
 
+def _bt_strides(t):
+    """(batch stride, token stride) of a [B, T, H, D] tensor whose H and D dims are
+    dense (the layouts of the library: BSHD, SBHD, and views into packed K/V or
+    Q/K/V buffers).  Size-1 dims report the dense value."""
+    if t.dim() != 4:
+        raise ValueError("expected a [B, T, H, D] tensor")
+    b, n, h, d = t.shape
+    if (d > 1 and t.stride(3) != 1) or (h > 1 and t.stride(2) != d):
+        raise ValueError(f"tensor of shape {tuple(t.shape)} must have dense heads and head_dim")
+    ts = t.stride(1) if n > 1 else h * d
+    bs = t.stride(0) if b > 1 else n * ts
+    return bs, ts
+
+
 def _require_gpu(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
@@ -183,14 +198,15 @@ def workspace_size(desc: AttnDesc) -> int:
 def _attn_desc(q, k, q_ids, kv_ids, scale, causal, window, out_dtype, o, lse):
     b, tq, hq, d = q.shape
     tk, hkv = k.shape[1], k.shape[2]
+    (qbs, qts), (kbs, kts) = _bt_strides(q), _bt_strides(k)
     strides = {
-        "q_batch_stride": _batch_stride(q, 3),
-        "kv_batch_stride": _batch_stride(k, 3),
+        "q_batch_stride": qbs, "q_token_stride": qts,
+        "kv_batch_stride": kbs, "kv_token_stride": kts,
         "q_meta_batch_stride": _batch_stride(q_ids, 1),
         "kv_meta_batch_stride": _batch_stride(kv_ids, 1),
     }
     if o is not None:
-        strides["o_batch_stride"] = _batch_stride(o, 3)
+        strides["o_batch_stride"], strides["o_token_stride"] = _bt_strides(o)
     if lse is not None:
         strides["lse_batch_stride"] = _batch_stride(lse, 2)
     return make_desc(b, tq, tk, hq, hkv, d, _dtype_code(q.dtype), out_dtype, scale, causal,
@@ -210,8 +226,8 @@ def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
         raise TypeError("q, k and v must share one dtype")
     if k.shape != v.shape:
         raise ValueError("k and v must have the same shape")
-    if _batch_stride(v, 3) != _batch_stride(k, 3):
-        raise ValueError("k and v must have the same batch stride")
+    if _bt_strides(v) != _bt_strides(k):
+        raise ValueError("k and v must have the same batch and token strides")
     for t in (q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos):
         if t.dtype != torch.int32:
             raise TypeError("segment ids and positions must be int32")
@@ -246,8 +262,8 @@ def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, k
     _require_gpu(q, k, v, partial_o, partial_lse)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
-    if k.shape != v.shape or _batch_stride(v, 3) != _batch_stride(k, 3):
-        raise ValueError("k and v must have the same shape and batch stride")
+    if k.shape != v.shape or _bt_strides(v) != _bt_strides(k):
+        raise ValueError("k and v must have the same shape and strides")
     b, tq, hq, d = q.shape
     if tuple(partial_o.shape) != (b, tq, hq, d) or tuple(partial_lse.shape) != (b, tq, hq):
         raise ValueError("the partial must have o's and lse's shapes")
@@ -264,7 +280,10 @@ def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, k
     part = Partial()
     part.o, part.lse = partial_o.data_ptr(), partial_lse.data_ptr()
     part.dtype = _dtype_code(partial_o.dtype)
-    part.o_batch_stride = _batch_stride(partial_o, 3)
+    pbs, pts = _bt_strides(partial_o)
+    if pts != _bt_strides(out)[1]:
+        raise ValueError("the partial must have out's token stride")
+    part.o_batch_stride = pbs
     part.lse_batch_stride = _batch_stride(partial_lse, 2)
     ws_bytes = workspace_size(desc)
     if workspace is None or workspace.numel() < ws_bytes:
@@ -289,8 +308,8 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
 
     q ``[B,Tq,Hq,D]``, k/v ``[B,Tk,Hkv,D]`` bf16; ``o``/``lse`` the forward's
     outputs for the same inputs and mask (o bf16 or fp32); ``dout`` bf16 with
-    o's shape and batch stride.  Gradients are ``grad_dtype`` (float32 or
-    bfloat16) with the shapes and batch strides of q and k; given buffers are
+    o's shape and strides.  Gradients are ``grad_dtype`` (float32 or
+    bfloat16) with the shapes and strides of q and k; given buffers are
     overwritten.
     """
     _require_gpu(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, o, lse, dout)
@@ -298,12 +317,12 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
         raise TypeError("the backward needs bfloat16 q, k and v")
     if dout.dtype != torch.bfloat16:
         raise TypeError("dout must be bfloat16")
-    if k.shape != v.shape or _batch_stride(v, 3) != _batch_stride(k, 3):
-        raise ValueError("k and v must have the same shape and batch stride")
+    if k.shape != v.shape or _bt_strides(v) != _bt_strides(k):
+        raise ValueError("k and v must have the same shape and strides")
     if o.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != tuple(q.shape[:3]):
         raise ValueError("o and dout must have q's shape, lse [B,Tq,Hq]")
-    if _batch_stride(dout, 3) != _batch_stride(o, 3):
-        raise ValueError("dout must have o's batch stride")
+    if _bt_strides(dout) != _bt_strides(o):
+        raise ValueError("dout must have o's batch and token strides")
     for t in (q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos):
         if t.dtype != torch.int32:
             raise TypeError("segment ids and positions must be int32")
@@ -311,10 +330,9 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
     gdt = _torch_dtype(gc)
 
     def like(t):
-        # the library writes a gradient with its input's batch stride
-        bs = _batch_stride(t, 3) or t.shape[1] * t.shape[2] * t.shape[3]
-        return torch.empty_strided(t.shape, (bs, t.shape[2] * t.shape[3], t.shape[3], 1),
-                                   dtype=gdt, device=t.device)
+        # the library writes a gradient with its input's batch and token strides
+        bs, ts = _bt_strides(t)
+        return torch.empty_strided(t.shape, (bs, ts, t.shape[3], 1), dtype=gdt, device=t.device)
 
     if dq is None:
         dq = like(q)
@@ -323,8 +341,8 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
     if dv is None:
         dv = like(k)
     for t, like in ((dq, q), (dk, k), (dv, k)):
-        if t.dtype != gdt or t.shape != like.shape or _batch_stride(t, 3) != _batch_stride(like, 3):
-            raise ValueError("gradient buffers must have grad_dtype and their input's shape and batch stride")
+        if t.dtype != gdt or t.shape != like.shape or _bt_strides(t) != _bt_strides(like):
+            raise ValueError("gradient buffers must have grad_dtype and their input's shape and strides")
     desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window,
                       _dtype_code(o.dtype), o, lse)
     ws_bytes = bwd_workspace_size(desc)

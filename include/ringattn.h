@@ -73,8 +73,22 @@ enum { RA_TILE_SKIP = 0, RA_TILE_PARTIAL = 1, RA_TILE_FULL = 2 };
  *        && (window_right < 0 || pos_kv[j] - pos_q[i] <= window_right).
  * Query head h reads K/V head h / (Hq / Hkv).
  * Batch strides are in elements of the tensor they describe; 0 selects the dense
- * value (Tq*Hq*D for q and o, Tk*Hkv*D for k and v, Tq*Hq for lse, Tq / Tk for
- * the int32 metadata).
+ * value (Tq * q token stride for q, and likewise for o, k and v; Tq*Hq for lse,
+ * Tq / Tk for the int32 metadata).
+ *
+ * Layouts ([TUT] s1: separate-tensor THD and packed K/V THD_T2HD, BSHD; [CPP] the
+ * qkv_layout field of the fused attention configuration): inside a
+ * token the Hx*D values of q, k, v and o are contiguous (head, then head_dim),
+ * but consecutive tokens may sit token_stride elements apart, so q, k, v may be
+ * views into one packed tensor and the sequence may be the outer dimension:
+ *   BSHD / THD with segment ids   token stride H*D, batch stride T*H*D (default)
+ *   THD_T2HD (K/V packed)         k = kv, v = kv + Hkv*D, kv token stride 2*Hkv*D
+ *   THD_T3HD (Q/K/V packed)       q = qkv, k = qkv + Hq*D, v = k + Hkv*D, all token
+ *                                 strides (Hq + 2*Hkv)*D
+ *   SBHD (sequence outermost)     token stride B*H*D, batch stride H*D
+ * The (batch, token) rows of each tensor must nest without overlap: with
+ * L = H*D, either token stride >= L and batch stride >= (T-1)*token stride + L,
+ * or batch stride >= L and token stride >= (B-1)*batch stride + L.
  */
 typedef struct ra_attn_desc {
   int32_t batch;          /* B  >= 0                                           */
@@ -95,6 +109,9 @@ typedef struct ra_attn_desc {
   int64_t lse_batch_stride;
   int64_t q_meta_batch_stride;
   int64_t kv_meta_batch_stride;
+  int64_t q_token_stride;   /* elements between consecutive tokens of q; 0 = Hq*D          */
+  int64_t kv_token_stride;  /* the same for k and v (one value for both); 0 = Hkv*D         */
+  int64_t o_token_stride;   /* the same for o (and a running partial, dout); 0 = Hq*D      */
 } ra_attn_desc;
 
 /* Library identification and diagnostics.  The returned strings are static

@@ -301,3 +301,40 @@ def test_bwd_validation(lib):
     # empty problems launch nothing and succeed
     assert _bwd(lib, _desc(batch=0)) == OK
     assert _bwd(lib, _desc(q_len=0, kv_len=0), ws=None, ws_bytes=0) == OK
+
+
+def test_layout_strides_validation(lib):
+    hd_q, hd_k = 16 * 128, 2 * 128          # Hq*D, Hkv*D of _desc()
+    # packed K/V (T2HD): token stride 2*Hkv*D, v half a row after k
+    d = _desc(kv_token_stride=2 * hd_k)
+    assert ra.check_support(d) == OK
+    # sequence-major (SBHD): batch stride H*D, token stride B*H*D
+    d = _desc(q_token_stride=2 * hd_q, q_batch_stride=hd_q, o_token_stride=2 * hd_q,
+              o_batch_stride=hd_q)
+    assert ra.check_support(d) == OK
+    # rows that would overlap
+    assert ra.check_support(_desc(q_token_stride=hd_q - 8)) == SHAPE
+    assert ra.check_support(_desc(q_token_stride=2 * hd_q, q_batch_stride=hd_q + 8)) == SHAPE
+    assert ra.check_support(_desc(kv_token_stride=-8)) == SHAPE
+    # token strides must keep 16-byte alignment
+    assert _fwd(lib, _desc(q_token_stride=hd_q + 4)) == ALIGN
+    assert _bwd(lib, _desc(kv_token_stride=2 * hd_k + 4)) == ALIGN
+
+
+def test_bwd_packed_gradients_are_not_aliases(lib):
+    hd_k = 2 * 128
+    d = _desc(kv_token_stride=2 * hd_k, kv_batch_stride=300 * 2 * hd_k)
+    base = 12 << 32
+    # dk and dv side by side in one packed buffer pass the alias checks (the call
+    # then stops at the missing workspace, before any HIP call)
+    assert _bwd(lib, d, ws=None, dk=_p(base), dv=_p(base + hd_k * 4)) == WS
+    # shifted by less than a row: overlap
+    assert _bwd(lib, d, ws=None, dk=_p(base), dv=_p(base + 16)) == ALIAS
+    # dq rows side by side with dk, dv at equal strides (packed Q/K/V gradients)
+    dq3 = _desc(q_len=300, num_q_heads=2, num_kv_heads=2, q_token_stride=6 * 128,
+                kv_token_stride=6 * 128, q_batch_stride=300 * 6 * 128,
+                kv_batch_stride=300 * 6 * 128)
+    assert _bwd(lib, dq3, ws=None, dq=_p(base), dk=_p(base + 256 * 4),
+                dv=_p(base + 512 * 4)) == WS
+    assert _bwd(lib, dq3, ws=None, dq=_p(base), dk=_p(base + 128 * 4),
+                dv=_p(base + 512 * 4)) == ALIAS
