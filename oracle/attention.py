@@ -55,12 +55,13 @@ def visible(qid, qpos, kid, kpos, causal=True, window=(-1, -1)):
 def _softmax_rows(qh, kc, vc, vis, scale):
     """One plain softmax per row.
 
-    qh ``[n, G, D]`` (n query tokens of one head group), kc/vc ``[m, D]`` (the
-    group's K/V head at m candidate keys), vis ``[n, m]``.  Returns O
-    ``[n, G, D]`` and LSE ``[n, G]``.
+    qh ``[n, G, D]`` (n query tokens of one head group), kc ``[m, D]`` and vc
+    ``[m, Dv]`` (the group's K/V head at m candidate keys), vis ``[n, m]``.
+    Returns O ``[n, G, Dv]`` and LSE ``[n, G]``.
     """
     n, g, d = qh.shape
-    o = np.zeros((n, g, d))
+    dv = vc.shape[1]
+    o = np.zeros((n, g, dv))
     lse = np.full((n, g), -np.inf)
     if kc.shape[0] == 0:
         return o, lse
@@ -71,7 +72,7 @@ def _softmax_rows(qh, kc, vc, vis, scale):
     m_safe = np.where(live, m, 0.0)
     e = np.exp(s - m_safe[:, :, None])           # masked entries give exp(-inf) = 0
     z = e.sum(axis=2)
-    u = (e.reshape(n * g, -1) @ vc).reshape(n, g, d)
+    u = (e.reshape(n * g, -1) @ vc).reshape(n, g, dv)
     o = np.where(live[:, :, None], u / np.where(live, z, 1.0)[:, :, None], 0.0)
     lse = np.where(live, m_safe + np.log(np.where(live, z, 1.0)), -np.inf)
     return o, lse
@@ -85,8 +86,10 @@ def attention(q, k, v, qid, qpos, kid, kpos, scale=None, causal=True, window=(-1
               q_block=128, workers=None):
     """Exact attention over whole tensors.
 
-    q ``[B, Tq, Hq, D]``, k/v ``[B, Tk, Hkv, D]``, metadata ``[B, T]``.
-    Returns fp64 ``O [B, Tq, Hq, D]`` and ``LSE [B, Tq, Hq]``.
+    q ``[B, Tq, Hq, D]``, k ``[B, Tk, Hkv, D]``, v ``[B, Tk, Hkv, Dv]``, metadata
+    ``[B, T]``.  Returns fp64 ``O [B, Tq, Hq, Dv]`` and ``LSE [B, Tq, Hq]``.  V's
+    head dim may differ from Q's and K's (the tutorial's single-GPU list names
+    DeepSeek-style MLA head dimensions); the default scale is D**-0.5 of Q/K.
     Work is spread over host threads by (batch row, query block); numpy
     releases the GIL inside its kernels.
     """
@@ -99,7 +102,7 @@ def attention(q, k, v, qid, qpos, kid, kpos, scale=None, causal=True, window=(-1
     grp = hq // hkv
     if scale is None:
         scale = d ** -0.5
-    o = np.zeros((b_, tq, hq, d))
+    o = np.zeros((b_, tq, hq, v.shape[3]))
     lse = np.full((b_, tq, hq), -np.inf)
 
     def one(job):
@@ -161,7 +164,7 @@ def attention_rows(q, k, v, qid, qpos, kid, kpos, rows, scale=None, causal=True,
         scale = d ** -0.5
     kid_all, kpos_all = i64(kid), i64(kpos)
     qid_all, qpos_all = i64(qid), i64(qpos)
-    o = np.zeros((len(rows), hq, d))
+    o = np.zeros((len(rows), hq, v.shape[3]))
     lse = np.full((len(rows), hq), -np.inf)
     for n, (b, i) in enumerate(rows):
         vis = visible(qid_all[b, i:i + 1], qpos_all[b, i:i + 1], kid_all[b], kpos_all[b],

@@ -158,3 +158,24 @@ def test_sampled_rows_and_keys_equal_full():
     gk, gv = oracle.backward_key_rows(q, k, v, do, qi, qp, ki, kp, rows, **kw)
     np.testing.assert_allclose(gk, np.stack([dk[b, t] for b, t in rows]), atol=1e-12, rtol=0)
     np.testing.assert_allclose(gv, np.stack([dv[b, t] for b, t in rows]), atol=1e-12, rtol=0)
+
+
+def test_backward_value_head_dim_differs_torch_autograd():
+    """V (and dO) with their own head dim, as with MLA head dimensions."""
+    rng = np.random.default_rng(61)
+    b, t, hq, hkv, d, dv = 2, 31, 4, 2, 12, 20
+    qi, qp = random_layout(rng, b, t, max_segments=3, pad_prob=0.2)
+    q = rng.standard_normal((b, t, hq, d))
+    k = rng.standard_normal((b, t, hkv, d))
+    v = rng.standard_normal((b, t, hkv, dv))
+    do = rng.standard_normal((b, t, hq, dv))
+    scale = d ** -0.5
+    tq_, tk_, tv_ = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    vis = _vis(qi, qp, qi, qp, True, (7, 0))
+    o = _torch_forward(tq_, tk_, tv_, vis, scale)
+    o.backward(torch.tensor(do))
+    dq, dk, dv_ = oracle.attention_backward(q, k, v, do, qi, qp, qi, qp, window=(7, 0))
+    assert dv_.shape == v.shape
+    np.testing.assert_allclose(dq, tq_.grad.numpy(), atol=1e-11, rtol=0)
+    np.testing.assert_allclose(dk, tk_.grad.numpy(), atol=1e-11, rtol=0)
+    np.testing.assert_allclose(dv_, tv_.grad.numpy(), atol=1e-11, rtol=0)

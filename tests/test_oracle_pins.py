@@ -70,6 +70,26 @@ def test_sdpa_scale_is_head_dim_rsqrt():
     assert np.abs(o2 - ref2).max() < 1e-12
 
 
+@pytest.mark.parametrize("d,dv,causal", [(24, 16, True), (12, 20, False)])
+def test_value_head_dim_differs_torch_sdpa(d, dv, causal):
+    """V's head dim differing from Q/K's (MLA head dimensions, tutorial's
+    single-GPU list): torch's SDPA in fp64 takes the same shapes; scale D**-0.5."""
+    b, t, hq, hkv = 2, 29, 4, 2
+    q, k, _ = random_qkv(b, t, t, hq, hkv, d, "f32", seed=21)
+    v = random_qkv(b, t, t, hq, hkv, dv, "f32", seed=22)[2]
+    ids, pos = _contig_meta(b, t)
+    o, lse = oracle.attention(q, k, v, ids, pos, ids, pos, causal=causal)
+    assert o.shape == (b, t, hq, dv)
+    ref = F.scaled_dot_product_attention(
+        q.double().transpose(1, 2), k.double().transpose(1, 2), v.double().transpose(1, 2),
+        is_causal=causal, enable_gqa=True).transpose(1, 2).numpy()
+    assert np.abs(o - ref).max() < 1e-12
+    rows = [(0, 0), (1, 17), (1, 28)]
+    o2, l2 = oracle.attention_rows(q, k, v, ids, pos, ids, pos, rows, causal=causal)
+    for n, (bb, i) in enumerate(rows):
+        assert np.abs(o2[n] - o[bb, i]).max() < 1e-13 and np.abs(l2[n] - lse[bb, i]).max() < 1e-13
+
+
 # --------------------------------------------------------------------------- exact special cases
 
 def _layouts():
@@ -271,7 +291,8 @@ def _brute(q, k, v, ids, pos, causal, window, scale):
     b, t, hq, d = q.shape
     tk, hkv = k.shape[1], k.shape[2]
     grp = hq // hkv
-    o = np.zeros((b, t, hq, d))
+    dv = v.shape[3]
+    o = np.zeros((b, t, hq, dv))
     lse = np.full((b, t, hq), -np.inf)
     for bb in range(b):
         for i in range(t):
@@ -296,7 +317,7 @@ def _brute(q, k, v, ids, pos, causal, window, scale):
                 mx = max(scores.values())
                 w = {j: math.exp(s - mx) for j, s in scores.items()}
                 z = math.fsum(w.values())
-                for x in range(d):
+                for x in range(dv):
                     o[bb, i, h, x] = math.fsum(w[j] * float(v[bb, j, g, x]) for j in w) / z
                 lse[bb, i, h] = mx + math.log(z)
     return o, lse
@@ -314,6 +335,8 @@ def test_brute_force_tiny(seed):
     window = (int(rng.integers(-1, 8)), int(rng.integers(-1, 5)))
     ids, pos = random_layout(rng, 2, t, max_segments=3, pad_prob=0.3, pos_offset_max=4)
     q, k, v = random_qkv(2, t, t, hq := hkv * grp, hkv, d, "bf16", seed=seed)
+    if seed % 2:      # V with its own head dim
+        v = random_qkv(2, t, t, hq, hkv, d + 4, "bf16", seed=seed + 50)[2]
     scale = float(rng.uniform(0.2, 1.0))
     o, lse = oracle.attention(q, k, v, ids, pos, ids, pos, scale=scale, causal=causal,
                               window=window)
