@@ -17,8 +17,9 @@ What it computes, and where that is defined:
   (fused attention call); segment ids / positions from its section 1; the
   (output, softmax_aux) pair from "Implementation: NVIDIA TransformerEngine JAX
   Cpp Attention", I/O contract, outputs.  V may carry its own head dim (the
-  tutorial's single-GPU list names DeepSeek-style MLA head dimensions); O then
-  has V's head dim and the default scale stays Q/K's head_dim**-0.5.
+  tutorial's "Next steps" section points to single-GPU attention with
+  DeepSeek-style MLA head dimensions); O then has V's head dim and the default
+  scale stays Q/K's head_dim**-0.5.
 * ``merge``/``fold_mzu``: combining partial results over disjoint key blocks,
   "Context parallelism and ring attention", section "Online softmax".
 * ``reorder_map``: causal load-balancing permutations (tutorial section 4,

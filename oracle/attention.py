@@ -88,8 +88,8 @@ def attention(q, k, v, qid, qpos, kid, kpos, scale=None, causal=True, window=(-1
 
     q ``[B, Tq, Hq, D]``, k ``[B, Tk, Hkv, D]``, v ``[B, Tk, Hkv, Dv]``, metadata
     ``[B, T]``.  Returns fp64 ``O [B, Tq, Hq, Dv]`` and ``LSE [B, Tq, Hq]``.  V's
-    head dim may differ from Q's and K's (the tutorial's single-GPU list names
-    DeepSeek-style MLA head dimensions); the default scale is D**-0.5 of Q/K.
+    head dim may differ from Q's and K's (the tutorial's "Next steps" section
+    names DeepSeek-style MLA head dimensions); the default scale is D**-0.5 of Q/K.
     Work is spread over host threads by (batch row, query block); numpy
     releases the GIL inside its kernels.
     """

@@ -73,7 +73,7 @@ def test_sdpa_scale_is_head_dim_rsqrt():
 @pytest.mark.parametrize("d,dv,causal", [(24, 16, True), (12, 20, False)])
 def test_value_head_dim_differs_torch_sdpa(d, dv, causal):
     """V's head dim differing from Q/K's (MLA head dimensions, tutorial's
-    single-GPU list): torch's SDPA in fp64 takes the same shapes; scale D**-0.5."""
+    "Next steps"): torch's SDPA in fp64 takes the same shapes; scale D**-0.5."""
     b, t, hq, hkv = 2, 29, 4, 2
     q, k, _ = random_qkv(b, t, t, hq, hkv, d, "f32", seed=21)
     v = random_qkv(b, t, t, hq, hkv, dv, "f32", seed=22)[2]
