@@ -53,7 +53,7 @@ def make_inputs(w, dev):
     shp_kv = (w.batch, w.seq_len, w.num_kv_heads, w.head_dim)
     q = torch.randn(shp_q, generator=g, device=dev).to(dt)
     k = torch.randn(shp_kv, generator=g, device=dev).to(dt)
-    v = torch.randn(shp_kv, generator=g, device=dev).to(dt)
+    v = torch.randn(shp_kv[:3] + (w.dv,), generator=g, device=dev).to(dt)
     ids, pos = packed_metadata(w.batch, w.seq_len, w.slots, w.valid_per_slot)
     return q, k, v, ids.to(dev), pos.to(dev)
 
@@ -126,7 +126,7 @@ def cpu_baseline(w, q, k, v, ids, pos, budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.head_dim * w.num_q_heads * pairs
+    flops = 2.0 * (w.head_dim + w.dv) * w.num_q_heads * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(rows)} random valid query rows x all {w.num_q_heads} heads "
                       f"({pairs} visible pairs, {flops / 1e9:.1f} GFLOP fp64) in {dt:.1f} s"}
@@ -186,9 +186,11 @@ def main():
     # visible pair exactly once).
     _, pairs = bosf.classify_tiles(ids, pos, ids, pos, num_q_heads=w.num_q_heads,
                                    num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
-                                   dtype=q.dtype, causal=w.causal, window=w.window)
+                                   v_head_dim=w.dv, dtype=q.dtype, causal=w.causal,
+                                   window=w.window)
     visible = int(pairs.sum().item())
-    flops = 4.0 * w.head_dim * w.num_q_heads * visible
+    # 2*D flops for Q K^T and 2*Dv for P V per visible pair and query head
+    flops = 2.0 * (w.head_dim + w.dv) * w.num_q_heads * visible
     log(f"visible pairs {visible}, {flops / 1e12:.3f} TFLOP per step")
 
     ev = EventLog()
@@ -217,10 +219,11 @@ def main():
                               window=w.window, bufs=bufs, step_hook=ev.hook,
                               fused=not args.unfused, plan=plan)
     else:
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape[:3] + (w.dv,), dtype=q.dtype, device=dev)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         desc = bosf.make_desc(w.batch, w.seq_len, w.seq_len, w.num_q_heads, w.num_kv_heads,
-                              w.head_dim, 0 if w.dtype == "bf16" else 1)
+                              w.head_dim, 0 if w.dtype == "bf16" else 1,
+                              strides={"v_head_dim": w.dv})
         wsp = torch.empty(bosf.workspace_size(desc), dtype=torch.uint8, device=dev)
 
         def step():
@@ -335,7 +338,7 @@ def main():
         "config": {"workload": f"{w.name}{' all-gather' if allgather else ''}: {desc}",
                    "batch": w.batch,
                    "seq_len": w.seq_len, "num_q_heads": w.num_q_heads,
-                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "v_head_dim": w.dv,
                    "window": list(w.window), "cp_shards": w.cp_size, "reorder": w.reorder,
                    "stripe": w.stripe, "strategy": "allgather" if allgather else "ring"},
         "roofline": roofline,

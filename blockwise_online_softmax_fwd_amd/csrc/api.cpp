@@ -38,6 +38,8 @@ constexpr int64_t kMaxKeyTiles = 32768;  // class bytes of one query tile fit in
 struct Resolved {
   int64_t q_bs, kv_bs, o_bs, lse_bs, qm_bs, km_bs;
   int64_t q_ts, kv_ts, o_ts;  // token strides (elements)
+  int64_t v_bs, v_ts;         // V's strides
+  int32_t dv;                 // head dim of V and O
   int32_t bm, bn, nqt, nkt, nt;
 };
 
@@ -68,8 +70,17 @@ ra_status check_desc(const ra_attn_desc *d, Resolved *r) {
   if (d->head_dim <= 0) return fail(RA_ERR_SHAPE, "head_dim must be > 0 (got %d)", d->head_dim);
   if (!dtype_ok(d->qkv_dtype)) return fail(RA_ERR_DTYPE, "unknown qkv_dtype %d", d->qkv_dtype);
   if (!dtype_ok(d->out_dtype)) return fail(RA_ERR_DTYPE, "unknown out_dtype %d", d->out_dtype);
-  if (d->head_dim != 64 && d->head_dim != 128)
-    return fail(RA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->v_head_dim < 0) return fail(RA_ERR_SHAPE, "v_head_dim must be >= 0");
+  if (d->reserved != 0) return fail(RA_ERR_SHAPE, "reserved must be 0");
+  r->dv = d->v_head_dim ? d->v_head_dim : d->head_dim;
+  {
+    const bool same = r->dv == d->head_dim && (d->head_dim == 64 || d->head_dim == 128);
+    const bool mla = d->head_dim == 192 && r->dv == 128 && d->qkv_dtype == RA_BF16;
+    if (!same && !mla)
+      return fail(RA_ERR_UNSUPPORTED,
+                  "head dims (%d, %d) not supported: (64, 64), (128, 128) or bf16 (192, 128)",
+                  d->head_dim, r->dv);
+  }
   if (!(d->scale > 0.0f) || !isfinite(d->scale))
     return fail(RA_ERR_SHAPE, "scale must be finite and > 0");
   if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_SHAPE, "causal must be 0 or 1");
@@ -78,23 +89,28 @@ ra_status check_desc(const ra_attn_desc *d, Resolved *r) {
                 d->window_right);
   const int64_t B = d->batch, Tq = d->q_len, Tk = d->kv_len, Hq = d->num_q_heads,
                 Hkv = d->num_kv_heads, D = d->head_dim;
-  const int64_t strides[9] = {d->q_batch_stride,   d->kv_batch_stride,     d->o_batch_stride,
-                              d->lse_batch_stride, d->q_meta_batch_stride, d->kv_meta_batch_stride,
-                              d->q_token_stride,   d->kv_token_stride,     d->o_token_stride};
-  for (int i = 0; i < 9; ++i)
+  const int64_t DV = r->dv;
+  const int64_t strides[11] = {d->q_batch_stride,   d->kv_batch_stride,     d->o_batch_stride,
+                               d->lse_batch_stride, d->q_meta_batch_stride, d->kv_meta_batch_stride,
+                               d->q_token_stride,   d->kv_token_stride,     d->o_token_stride,
+                               d->v_batch_stride,   d->v_token_stride};
+  for (int i = 0; i < 11; ++i)
     if (strides[i] < 0) return fail(RA_ERR_SHAPE, "batch and token strides must be >= 0");
   r->q_ts = pick(d->q_token_stride, Hq * D);
   r->kv_ts = pick(d->kv_token_stride, Hkv * D);
-  r->o_ts = pick(d->o_token_stride, Hq * D);
+  r->o_ts = pick(d->o_token_stride, Hq * DV);
   r->q_bs = pick(d->q_batch_stride, Tq * r->q_ts);
   r->kv_bs = pick(d->kv_batch_stride, Tk * r->kv_ts);
   r->o_bs = pick(d->o_batch_stride, Tq * r->o_ts);
+  // V follows K's strides unless its head dim differs or its own are given.
+  r->v_ts = pick(d->v_token_stride, DV == D ? r->kv_ts : Hkv * DV);
+  r->v_bs = pick(d->v_batch_stride, DV == D && d->v_token_stride == 0 ? r->kv_bs : Tk * r->v_ts);
   r->lse_bs = pick(d->lse_batch_stride, Tq * Hq);
   r->qm_bs = pick(d->q_meta_batch_stride, Tq);
   r->km_bs = pick(d->kv_meta_batch_stride, Tk);
-  if (!nested(B, Tq, Hq * D, r->q_bs, r->q_ts) || !nested(B, Tq, Hq * D, r->o_bs, r->o_ts) ||
-      !nested(B, Tk, Hkv * D, r->kv_bs, r->kv_ts))
-    return fail(RA_ERR_SHAPE, "q, k/v or o strides let two (batch, token) rows overlap");
+  if (!nested(B, Tq, Hq * D, r->q_bs, r->q_ts) || !nested(B, Tq, Hq * DV, r->o_bs, r->o_ts) ||
+      !nested(B, Tk, Hkv * D, r->kv_bs, r->kv_ts) || !nested(B, Tk, Hkv * DV, r->v_bs, r->v_ts))
+    return fail(RA_ERR_SHAPE, "q, k, v or o strides let two (batch, token) rows overlap");
   if (B > 1 && (r->lse_bs < Tq * Hq || r->qm_bs < Tq || r->km_bs < Tk))
     return fail(RA_ERR_SHAPE, "a batch stride is smaller than one batch row");
   if (d->qkv_dtype == RA_BF16) {
@@ -173,7 +189,7 @@ ra_status check_meta(const ra_attn_desc *d, const Resolved &r, const int32_t *qi
 
 ra::WorkspaceLayout layout_of(const ra_attn_desc *d, const Resolved &r) {
   const int32_t pd = d->qkv_dtype == RA_BF16 ? d->head_dim : 0;
-  return ra::workspace_layout(d->batch, r.nqt, r.nkt, d->num_kv_heads, pd);
+  return ra::workspace_layout(d->batch, r.nqt, r.nkt, d->num_kv_heads, pd, pd ? r.dv : 0);
 }
 
 ra_status check_workspace(const ra_attn_desc *d, const Resolved &r, const void *ws,
@@ -286,20 +302,22 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return fail(RA_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
   if ((r.q_bs * es) % 16 || (r.kv_bs * es) % 16 || (r.o_bs * os) % 16 || (r.q_ts * es) % 16 ||
-      (r.kv_ts * es) % 16 || (r.o_ts * os) % 16)
+      (r.kv_ts * es) % 16 || (r.o_ts * os) % 16 || (r.v_bs * es) % 16 || (r.v_ts * es) % 16)
     return fail(RA_ERR_ALIGN, "batch and token strides of q, k, v and o must be multiples of 16 bytes");
   if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
   const int64_t D = d->head_dim;
   const int64_t B = d->batch, Tq = d->q_len, Tk = d->kv_len;
   const int64_t Lq = (int64_t)d->num_q_heads * D, Lk = (int64_t)d->num_kv_heads * D;
+  const int64_t Lo = (int64_t)d->num_q_heads * r.dv, Lv = (int64_t)d->num_kv_heads * r.dv;
   const size_t q_span = span_bytes2(B, Tq, Lq, r.q_bs, r.q_ts, es);
   const size_t kv_span = span_bytes2(B, Tk, Lk, r.kv_bs, r.kv_ts, es);
-  const size_t o_span = span_bytes2(B, Tq, Lq, r.o_bs, r.o_ts, os);
+  const size_t v_span = span_bytes2(B, Tk, Lv, r.v_bs, r.v_ts, es);
+  const size_t o_span = span_bytes2(B, Tq, Lo, r.o_bs, r.o_ts, os);
   const size_t l_span = span_bytes(d->batch, r.lse_bs, (int64_t)d->q_len * d->num_q_heads, 4);
   if (overlaps(o, o_span, q, q_span) || overlaps(o, o_span, k, kv_span) ||
-      overlaps(o, o_span, v, kv_span) || overlaps(lse, l_span, o, o_span) ||
+      overlaps(o, o_span, v, v_span) || overlaps(lse, l_span, o, o_span) ||
       overlaps(lse, l_span, q, q_span) || overlaps(lse, l_span, k, kv_span) ||
-      overlaps(lse, l_span, v, kv_span))
+      overlaps(lse, l_span, v, v_span))
     return fail(RA_ERR_ALIAS, "o / lse overlap an input or each other");
   int64_t acc_o_bs = 0, acc_lse_bs = 0;
   bool in_place = false;
@@ -310,13 +328,13 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
     const int64_t rows = (int64_t)d->q_len * d->num_q_heads;
     acc_o_bs = pick(acc->o_batch_stride, Tq * r.o_ts);
     acc_lse_bs = pick(acc->lse_batch_stride, rows);
-    if (!nested(B, Tq, Lq, acc_o_bs, r.o_ts) || (d->batch > 1 && acc_lse_bs < rows))
+    if (!nested(B, Tq, Lo, acc_o_bs, r.o_ts) || (d->batch > 1 && acc_lse_bs < rows))
       return fail(RA_ERR_SHAPE, "a partial batch stride is smaller than one batch row");
     if (has_q && (!acc->o || !acc->lse)) return fail(RA_ERR_NULL, "partial o or lse is NULL");
     const size_t as = dtype_size(acc->dtype);
     if (!aligned(acc->o, 16) || (acc_o_bs * as) % 16 || !aligned(acc->lse, 4))
       return fail(RA_ERR_ALIGN, "partial o must be 16-byte aligned (lse 4-byte)");
-    const size_t a_span = span_bytes2(B, Tq, Lq, acc_o_bs, r.o_ts, as);
+    const size_t a_span = span_bytes2(B, Tq, Lo, acc_o_bs, r.o_ts, as);
     const size_t al_span = span_bytes(d->batch, acc_lse_bs, rows, 4);
     const bool same_o = acc->o == o && acc->dtype == d->out_dtype && acc_o_bs == r.o_bs;
     const bool same_l = acc->lse == lse && acc_lse_bs == r.lse_bs;
@@ -354,6 +372,8 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
   p.q_ts = r.q_ts;
   p.kv_ts = r.kv_ts;
   p.o_ts = r.o_ts;
+  p.v_bs = r.v_bs;
+  p.v_ts = r.v_ts;
   p.qm_bs = r.qm_bs;
   p.km_bs = r.km_bs;
   p.batch = d->batch;
@@ -387,17 +407,19 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
     pk.mpack = (int32_t *)((char *)workspace + L.mpack);
     pk.kv_bs = r.kv_bs;
     pk.kv_ts = r.kv_ts;
+    pk.v_bs = r.v_bs;
+    pk.v_ts = r.v_ts;
     pk.km_bs = r.km_bs;
     pk.batch = d->batch;
     pk.tk = d->kv_len;
     pk.hkv = d->num_kv_heads;
     pk.nkt = r.nkt;
-    const hipError_t pe = ra::launch_pack_kv(pk, d->head_dim, s);
+    const hipError_t pe = ra::launch_pack_kv(pk, d->head_dim, r.dv, s);
     if (pe != hipSuccess) return hip_fail(pe, "K/V tile packing");
   }
   const bool out_bf16 = d->out_dtype == RA_BF16;
   const hipError_t e = d->qkv_dtype == RA_BF16
-                           ? ra::launch_attn_bf16(p, d->head_dim, r.nt, out_bf16, s)
+                           ? ra::launch_attn_bf16(p, d->head_dim, r.dv, r.nt, out_bf16, s)
                            : ra::launch_attn_f32(p, d->head_dim, out_bf16, s);
   if (e != hipSuccess) return hip_fail(e, "attention forward");
   return RA_OK;
@@ -536,6 +558,8 @@ ra_status check_bwd_desc(const ra_attn_desc *d, Resolved *r, BwdShape *bs) {
   if (st != RA_OK) return st;
   if (d->qkv_dtype != RA_BF16)
     return fail(RA_ERR_UNSUPPORTED, "the backward needs bf16 q, k and v");
+  if (r->dv != d->head_dim)
+    return fail(RA_ERR_UNSUPPORTED, "the backward needs v_head_dim == head_dim");
   const int64_t tnk = ((int64_t)d->kv_len + ra::kBwdKvTile - 1) / ra::kBwdKvTile;
   const int64_t tnq = ((int64_t)d->q_len + ra::kBwdQTile - 1) / ra::kBwdQTile;
   if (tnq > kMaxKeyTiles)
@@ -598,8 +622,8 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   const void *p16[8] = {q, k, v, o, dout, dq, dk, dv};
   for (const void *ptr : p16)
     if (!aligned(ptr, 16)) return fail(RA_ERR_ALIGN, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
-  const int64_t sts[5] = {r.q_bs, r.kv_bs, r.q_ts, r.kv_ts, 0};
-  for (int i = 0; i < 4; ++i)
+  const int64_t sts[6] = {r.q_bs, r.kv_bs, r.q_ts, r.kv_ts, r.v_bs, r.v_ts};
+  for (int i = 0; i < 6; ++i)
     if ((sts[i] * 2) % 16 || (sts[i] * (int64_t)gs) % 16)
       return fail(RA_ERR_ALIGN, "batch and token strides must be multiples of 16 bytes for every tensor using them");
   if ((r.o_bs * os) % 16 || (r.o_bs * 2) % 16 || (r.o_ts * os) % 16 || (r.o_ts * 2) % 16)
@@ -610,15 +634,17 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   const int64_t Lq = (int64_t)d->num_q_heads * D, Lk = (int64_t)d->num_kv_heads * D;
   const size_t q_span = span_bytes2(B, Tq, Lq, r.q_bs, r.q_ts, 2);
   const size_t kv_span = span_bytes2(B, Tk, Lk, r.kv_bs, r.kv_ts, 2);
+  const size_t v_span = span_bytes2(B, Tk, Lk, r.v_bs, r.v_ts, 2);
   const size_t o_span = span_bytes2(B, Tq, Lq, r.o_bs, r.o_ts, os);
   const size_t do_span = span_bytes2(B, Tq, Lq, r.o_bs, r.o_ts, 2);
   const size_t l_span = span_bytes(B, r.lse_bs, Tq * d->num_q_heads, 4);
   const size_t dq_span = span_bytes2(B, Tq, Lq, r.q_bs, r.q_ts, gs);
   const size_t dkv_span = span_bytes2(B, Tk, Lk, r.kv_bs, r.kv_ts, gs);
+  const size_t dvv_span = span_bytes2(B, Tk, Lk, r.v_bs, r.v_ts, gs);
   const void *ins[6] = {q, k, v, o, lse, dout};
-  const size_t in_span[6] = {q_span, kv_span, kv_span, o_span, l_span, do_span};
+  const size_t in_span[6] = {q_span, kv_span, v_span, o_span, l_span, do_span};
   const void *outs[3] = {dq, dk, dv};
-  const size_t out_span[3] = {dq_span, dkv_span, dkv_span};
+  const size_t out_span[3] = {dq_span, dkv_span, dvv_span};
   for (int i = 0; i < 3; ++i)
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], out_span[i], ins[j], in_span[j]))
@@ -626,13 +652,18 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   // The gradients may share one packed buffer (rows side by side at equal
   // strides, e.g. dk/dv of a packed K/V layout); otherwise their spans must not meet.
   const int64_t g = (int64_t)gs;
-  if (rows_overlap(dk, Tk, Lk * g, dv, Tk, Lk * g, B, r.kv_bs * g, r.kv_ts * g))
+  const bool kv_same = r.kv_bs == r.v_bs && r.kv_ts == r.v_ts;
+  if (kv_same ? rows_overlap(dk, Tk, Lk * g, dv, Tk, Lk * g, B, r.kv_bs * g, r.kv_ts * g)
+              : overlaps(dk, dkv_span, dv, dvv_span))
     return fail(RA_ERR_ALIAS, "dk and dv overlap");
-  const bool same = r.q_bs == r.kv_bs && r.q_ts == r.kv_ts;
-  for (void *kg : {dk, dv})
-    if (same ? rows_overlap(dq, Tq, Lq * g, kg, Tk, Lk * g, B, r.q_bs * g, r.q_ts * g)
-             : overlaps(dq, dq_span, kg, dkv_span))
-      return fail(RA_ERR_ALIAS, "dq overlaps dk or dv");
+  const bool qk_same = r.q_bs == r.kv_bs && r.q_ts == r.kv_ts;
+  const bool qv_same = r.q_bs == r.v_bs && r.q_ts == r.v_ts;
+  if (qk_same ? rows_overlap(dq, Tq, Lq * g, dk, Tk, Lk * g, B, r.q_bs * g, r.q_ts * g)
+              : overlaps(dq, dq_span, dk, dkv_span))
+    return fail(RA_ERR_ALIAS, "dq overlaps dk");
+  if (qv_same ? rows_overlap(dq, Tq, Lq * g, dv, Tk, Lk * g, B, r.q_bs * g, r.q_ts * g)
+              : overlaps(dq, dq_span, dv, dvv_span))
+    return fail(RA_ERR_ALIAS, "dq overlaps dv");
   if (!has_q && !has_k) return RA_OK;
   const ra::BwdLayout L = bwd_layout_of(d, r, bs);
   if (L.total > 0 && !workspace)
@@ -677,6 +708,8 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   p.q_ts = r.q_ts;
   p.kv_ts = r.kv_ts;
   p.o_ts = r.o_ts;
+  p.v_bs = r.v_bs;
+  p.v_ts = r.v_ts;
   p.batch = d->batch;
   p.tq = d->q_len;
   p.tk = d->kv_len;

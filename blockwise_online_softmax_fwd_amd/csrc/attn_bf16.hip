@@ -50,30 +50,53 @@ constexpr float kRescaleLog2 = 8.0f; // raise the max only beyond 2^8
 
 // ----------------------------------------------------------------------------- packing
 
+// Packed K rows: 64- and 128-wide rows are XOR-swizzled in place (16-byte
+// chunk c of row r stored at chunk swz(r, c)); 192-wide rows (the query/key
+// head dim of MLA) are padded to 200 elements instead, which spreads the 16
+// rows an operand read touches over distinct banks with plain offsets.
 template <int D>
+struct KRow {
+  static constexpr int chunks = D == 192 ? 25 : D / 8;   // 16-byte chunks per stored row
+  // logical chunk held at stored chunk ph of row r (>= D/8: padding)
+  __device__ static int logical(int r, int ph) {
+    if constexpr (D == 192) return ph;
+    else return swz<D / 8>(r, ph);
+  }
+  // element offset of logical chunk c within the stored row r
+  __device__ static int offset(int r, int c) {
+    if constexpr (D == 192) return 8 * c;
+    else return 8 * swz<D / 8>(r, c);
+  }
+};
+
+template <int D, int DVH>
 __global__ __launch_bounds__(256) void pack_kv_kernel(PackParams p) {
-  constexpr int DV = D / 8;          // 16-byte chunks per K row
-  constexpr int KCH = BN * DV;       // 16-byte chunks per block
-  __shared__ __attribute__((aligned(16))) bf16 vs[BN][D + 8];
+  constexpr int KR = KRow<D>::chunks;      // 16-byte chunks per packed K row
+  constexpr int DQC = D / 8;               // chunks of K data per row
+  constexpr int VC = DVH / 8;              // chunks of V data per row
+  __shared__ __attribute__((aligned(16))) bf16 vs[BN][DVH + 8];
   const int kt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t tile = ((int64_t)b * p.hkv + g) * p.nkt + kt;
   const bf16 *kb = (const bf16 *)p.k + b * p.kv_bs + (int64_t)g * D;
-  const bf16 *vb = (const bf16 *)p.v + b * p.kv_bs + (int64_t)g * D;
-  const int64_t tok = p.kv_ts;
-  bf16 *kout = (bf16 *)p.kpack + tile * (BN * D);
-  bf16 *vout = (bf16 *)p.vpack + tile * (BN * D);
+  const bf16 *vb = (const bf16 *)p.v + b * p.v_bs + (int64_t)g * DVH;
+  bf16 *kout = (bf16 *)p.kpack + tile * (BN * KR * 8);
+  bf16 *vout = (bf16 *)p.vpack + tile * (BN * DVH);
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  for (int u = tid; u < KCH; u += 256) {
-    const int r = u / DV, ph = u % DV;
+  for (int u = tid; u < BN * KR; u += 256) {
+    const int r = u / KR, ph = u % KR;
     const int key = kt * BN + r;
-    const int lc = swz<DV>(r, ph);
+    const int lc = KRow<D>::logical(r, ph);
     u32x4 val = zero;
-    if (key < p.tk) val = *(const u32x4 *)(kb + key * tok + lc * 8);
+    if (key < p.tk && lc < DQC) val = *(const u32x4 *)(kb + key * p.kv_ts + lc * 8);
     *(u32x4 *)(kout + (int64_t)u * 8) = val;
+  }
+  for (int u = tid; u < BN * VC; u += 256) {
+    const int r = u / VC, ph = u % VC;
+    const int key = kt * BN + r;
     u32x4 vv = zero;
-    if (key < p.tk) vv = *(const u32x4 *)(vb + key * tok + ph * 8);
+    if (key < p.tk) vv = *(const u32x4 *)(vb + key * p.v_ts + ph * 8);
     *(u32x4 *)&vs[r][ph * 8] = vv;
   }
   if (tid < BN) {
@@ -83,16 +106,16 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(PackParams p) {
     meta[BN + tid] = key < p.tk ? p.kpos[b * p.km_bs + key] : 0;
   }
   __syncthreads();
-  // V^T: D rows of BN keys, 8 chunks of 8 keys per row, swizzled by row.
+  // V^T: DVH rows of BN keys, 8 chunks of 8 keys per row, swizzled by row.
   const uint16_t *vsu = (const uint16_t *)&vs[0][0];
-  for (int u = tid; u < D * (BN / 8); u += 256) {
+  for (int u = tid; u < DVH * (BN / 8); u += 256) {
     const int d = u / (BN / 8), ph = u % (BN / 8);
     const int lc = swz<BN / 8>(d, ph);
     u32x4 out;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = vsu[vt_key(lc * 8 + 2 * j) * (D + 8) + d];
-      const uint32_t hi = vsu[vt_key(lc * 8 + 2 * j + 1) * (D + 8) + d];
+      const uint32_t lo = vsu[vt_key(lc * 8 + 2 * j) * (DVH + 8) + d];
+      const uint32_t hi = vsu[vt_key(lc * 8 + 2 * j + 1) * (DVH + 8) + d];
       out[j] = lo | (hi << 16);
     }
     *(u32x4 *)(vout + (int64_t)u * 8) = out;
@@ -127,26 +150,29 @@ struct LaneMask {
   }
 };
 
-template <int D>
+template <int D, int DVH>
 struct Tile {
-  bf16 k[BN * D];
-  bf16 vt[D * BN];
+  bf16 k[BN * KRow<D>::chunks * 8];
+  bf16 vt[DVH * BN];
   int32_t meta[2 * BN];
 };
 
-template <int D, int NT, bool OUT_BF16>
+// D: head dim of Q and K; DVH: head dim of V and O.
+template <int D, int DVH, int NT, bool OUT_BF16>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_fwd_bf16_kernel(AttnParams p) {
   constexpr int NH = kWaves / NT;
   constexpr int BM = 32 * NT;
   constexpr int DC = D / 16;               // MFMA steps over head_dim for S^T
-  constexpr int DB = D / 32;               // 32-row blocks of O^T
-  constexpr int BLK = BN * D * 2;          // bytes of one packed K (or V^T) block
-  constexpr int WPW = BLK / 1024 / kWaves; // 1 KB direct loads per wave per block
-  static_assert(WPW >= 1, "block too small for the wave count");
+  constexpr int DB = DVH / 32;             // 32-row blocks of O^T
+  constexpr int KROW = KRow<D>::chunks * 8;
+  constexpr int BLKK = BN * KROW * 2;      // bytes of one packed K block
+  constexpr int BLKV = BN * DVH * 2;       // bytes of one packed V^T block
+  static_assert(BLKK % 1024 == 0 && BLKV % 1024 == 0, "1 KB direct loads");
+  constexpr int CK = BLKK / 1024, CV = BLKV / 1024;
 
-  __shared__ __attribute__((aligned(16))) Tile<D> t0;
-  __shared__ __attribute__((aligned(16))) Tile<D> t1;
+  __shared__ __attribute__((aligned(16))) Tile<D, DVH> t0;
+  __shared__ __attribute__((aligned(16))) Tile<D, DVH> t1;
   // Epilogue staging: each wave's 32 x 64 slice of O (fp32, rows padded to
   // 68 floats so the column-wise writes spread over the banks) and the per-row
   // weight of the running partial.
@@ -194,17 +220,34 @@ attn_fwd_bf16_kernel(AttnParams p) {
   const char *mpack = (const char *)p.mpack;
 
   // Direct HBM -> LDS loads of one packed tile (1 KB per wave instruction).
-  auto issue = [&](Tile<D> &dst, int kt) {
+  auto issue = [&](Tile<D, DVH> &dst, int kt) {
     const int64_t t = tile0 + kt;
-    const char *ks = kpack + t * BLK;
-    const char *vs = vpack + t * BLK;
+    const char *ks = kpack + t * BLKK;
+    const char *vs = vpack + t * BLKV;
+    if constexpr (CK % kWaves == 0 && CK == CV) {
 #pragma unroll
-    for (int i = 0; i < WPW; ++i) {
-      const int c = wave * WPW + i;
-      __builtin_amdgcn_global_load_lds((const void *)(ks + c * 1024 + lane * 16),
-                                       LDS_PTR((char *)dst.k + c * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(vs + c * 1024 + lane * 16),
-                                       LDS_PTR((char *)dst.vt + c * 1024), 16, 0, 0);
+      for (int i = 0; i < CK / kWaves; ++i) {
+        const int c = wave * (CK / kWaves) + i;
+        __builtin_amdgcn_global_load_lds((const void *)(ks + c * 1024 + lane * 16),
+                                         LDS_PTR((char *)dst.k + c * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(vs + c * 1024 + lane * 16),
+                                         LDS_PTR((char *)dst.vt + c * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < (CK + kWaves - 1) / kWaves; ++i) {
+        const int c = wave + i * kWaves;
+        if (c < CK)
+          __builtin_amdgcn_global_load_lds((const void *)(ks + c * 1024 + lane * 16),
+                                           LDS_PTR((char *)dst.k + c * 1024), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < (CV + kWaves - 1) / kWaves; ++i) {
+        const int c = wave + i * kWaves;
+        if (c < CV)
+          __builtin_amdgcn_global_load_lds((const void *)(vs + c * 1024 + lane * 16),
+                                           LDS_PTR((char *)dst.vt + c * 1024), 16, 0, 0);
+      }
     }
     if (wave < 2) {
       const char *ms = mpack + t * (2 * BN * 4) + wave * (BN * 4);
@@ -253,15 +296,15 @@ attn_fwd_bf16_kernel(AttnParams p) {
   const float c2 = p.scale_log2;
 
   // One tile: S^T = K Q^T, mask (boundary tiles only), online softmax, O^T += V^T P^T.
-  auto compute = [&](const Tile<D> &tl, bool masked) {
+  auto compute = [&](const Tile<D, DVH> &tl, bool masked) {
     f32x16 s[2];
     {
       bf16x8 ka0[DC], ka1[DC];
-      const bf16 *krow0 = tl.k + col * D, *krow1 = tl.k + (32 + col) * D;
+      const bf16 *krow0 = tl.k + col * KROW, *krow1 = tl.k + (32 + col) * KROW;
 #pragma unroll
-      for (int c = 0; c < DC; ++c) ka0[c] = *(const bf16x8 *)(krow0 + 8 * swz<D / 8>(col, 2 * c + half));
+      for (int c = 0; c < DC; ++c) ka0[c] = *(const bf16x8 *)(krow0 + KRow<D>::offset(col, 2 * c + half));
 #pragma unroll
-      for (int c = 0; c < DC; ++c) ka1[c] = *(const bf16x8 *)(krow1 + 8 * swz<D / 8>(col, 2 * c + half));
+      for (int c = 0; c < DC; ++c) ka1[c] = *(const bf16x8 *)(krow1 + KRow<D>::offset(col, 2 * c + half));
       const f32x16 zero16 = {};
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[0], qf[0], zero16, 0, 0, 0);
 #pragma unroll
@@ -412,7 +455,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
       const int t = tq0 + qrow;
       f32x4 val = *(const f32x4 *)&stage[wave][qrow][c4];
       if (t < p.tq) {
-        const int64_t rel = (int64_t)t * p.o_ts + (int64_t)h * D + 64 * hd + c4;
+        const int64_t rel = (int64_t)t * p.o_ts + (int64_t)h * DVH + 64 * hd + c4;
         const float wa = stage_w[wave][qrow];
         if (wa != 0.0f) {
           f32x4 a;
@@ -442,54 +485,58 @@ attn_fwd_bf16_kernel(AttnParams p) {
   }
 }
 
-template <int D, int NT>
+template <int D, int DVH, int NT>
 hipError_t launch_nt(const AttnParams &p, bool out_bf16, hipStream_t stream) {
   constexpr int NH = kWaves / NT;
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.nqt * (p.group / NH);
   if (nwork == 0) return hipSuccess;
   const int64_t grid = (nwork + 7) / 8 * 8;
   if (out_bf16)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NT, true>), dim3((unsigned)grid), dim3(512), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, DVH, NT, true>), dim3((unsigned)grid), dim3(512),
+                       0, stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NT, false>), dim3((unsigned)grid), dim3(512), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, DVH, NT, false>), dim3((unsigned)grid), dim3(512),
+                       0, stream, p);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int DVH>
 hipError_t launch_d(const AttnParams &p, int32_t nt, bool out_bf16, hipStream_t stream) {
   switch (nt) {
-    case 1: return launch_nt<D, 1>(p, out_bf16, stream);
-    case 2: return launch_nt<D, 2>(p, out_bf16, stream);
-    case 4: return launch_nt<D, 4>(p, out_bf16, stream);
-    case 8: return launch_nt<D, 8>(p, out_bf16, stream);
+    case 1: return launch_nt<D, DVH, 1>(p, out_bf16, stream);
+    case 2: return launch_nt<D, DVH, 2>(p, out_bf16, stream);
+    case 4: return launch_nt<D, DVH, 4>(p, out_bf16, stream);
+    case 8: return launch_nt<D, DVH, 8>(p, out_bf16, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-size_t packed_kv_bytes(int32_t batch, int32_t hkv, int32_t nkt, int32_t head_dim) {
-  return (size_t)batch * hkv * nkt * (2 * (size_t)BN * head_dim * 2 + 2 * BN * 4);
+size_t packed_k_block_bytes(int32_t head_dim) {
+  return (size_t)BN * (head_dim == 192 ? 200 : head_dim) * 2;
 }
 
-hipError_t launch_pack_kv(const PackParams &p, int32_t head_dim, hipStream_t stream) {
+hipError_t launch_pack_kv(const PackParams &p, int32_t head_dim, int32_t v_head_dim,
+                          hipStream_t stream) {
   if (p.batch == 0 || p.nkt == 0) return hipSuccess;
   dim3 grid(p.nkt, p.hkv, p.batch);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(pack_kv_kernel<128>, grid, dim3(256), 0, stream, p);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL(pack_kv_kernel<64>, grid, dim3(256), 0, stream, p);
+  if (head_dim == 128 && v_head_dim == 128)
+    hipLaunchKernelGGL((pack_kv_kernel<128, 128>), grid, dim3(256), 0, stream, p);
+  else if (head_dim == 64 && v_head_dim == 64)
+    hipLaunchKernelGGL((pack_kv_kernel<64, 64>), grid, dim3(256), 0, stream, p);
+  else if (head_dim == 192 && v_head_dim == 128)
+    hipLaunchKernelGGL((pack_kv_kernel<192, 128>), grid, dim3(256), 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bf16(const AttnParams &p, int32_t head_dim, int32_t nt, bool out_bf16,
-                            hipStream_t stream) {
-  if (head_dim == 128) return launch_d<128>(p, nt, out_bf16, stream);
-  if (head_dim == 64) return launch_d<64>(p, nt, out_bf16, stream);
+hipError_t launch_attn_bf16(const AttnParams &p, int32_t head_dim, int32_t v_head_dim, int32_t nt,
+                            bool out_bf16, hipStream_t stream) {
+  if (head_dim == 128 && v_head_dim == 128) return launch_d<128, 128>(p, nt, out_bf16, stream);
+  if (head_dim == 64 && v_head_dim == 64) return launch_d<64, 64>(p, nt, out_bf16, stream);
+  if (head_dim == 192 && v_head_dim == 128) return launch_d<192, 128>(p, nt, out_bf16, stream);
   return hipErrorInvalidValue;
 }
 

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
   if (p.acc_in_place && n == 0) return;  // partial stays as it is
   const uint32_t *lst = p.list + row * p.nkt;
   const float *kb = (const float *)p.k + b * p.kv_bs + (int64_t)g * D;
-  const float *vb = (const float *)p.v + b * p.kv_bs + (int64_t)g * D;
+  const float *vb = (const float *)p.v + b * p.v_bs + (int64_t)g * D;
   const int64_t kv_tok = p.kv_ts;
   const bool ragged = (p.tk % BN) != 0;
 
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
       const int r = u / D, d = u % D;
       const int key = kt * BN + r;
       ks[r][d] = key < p.tk ? kb[key * kv_tok + d] : 0.0f;
-      vs[r][d] = key < p.tk ? vb[key * kv_tok + d] : 0.0f;
+      vs[r][d] = key < p.tk ? vb[key * p.v_ts + d] : 0.0f;
     }
     if (tid < BN) {
       const int key = kt * BN + tid;

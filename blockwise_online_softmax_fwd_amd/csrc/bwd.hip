@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void bwd_pack_kv_kernel(BwdParams p) {
   const int64_t tile = ((int64_t)b * p.hkv + g) * p.nkt + kt;
   KvTile<D> *out = (KvTile<D> *)((char *)p.kvpack + tile * sizeof(KvTile<D>));
   const bf16 *kb = (const bf16 *)p.k + b * p.kv_bs + (int64_t)g * D;
-  const bf16 *vb = (const bf16 *)p.v + b * p.kv_bs + (int64_t)g * D;
+  const bf16 *vb = (const bf16 *)p.v + b * p.v_bs + (int64_t)g * D;
   const int64_t tok = p.kv_ts;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int u = tid; u < BN * RN; u += 256) {
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void bwd_pack_kv_kernel(BwdParams p) {
     const bool in = key < p.tk && c < DV;
     const u32x4 kv = in ? *(const u32x4 *)(kb + key * tok + c * 8) : zero;
     *(u32x4 *)(out->k + u * 8) = kv;
-    *(u32x4 *)(out->v + u * 8) = in ? *(const u32x4 *)(vb + key * tok + c * 8) : zero;
+    *(u32x4 *)(out->v + u * 8) = in ? *(const u32x4 *)(vb + key * p.v_ts + c * 8) : zero;
     if (c < DV) *(u32x4 *)&ks[r][c * 8] = kv;
   }
   if (tid < BN) {
@@ -523,9 +523,10 @@ bwd_dkdv_kernel(BwdParams p) {
   bf16x8 kf[DC];
   bf16 *const vmine = vrows + (wave * 32 + col) * kRowN<D> + 8 * half;
   {
-    const int64_t rel = (int64_t)key * p.kv_ts + (int64_t)g * D + 8 * half;
-    const bf16 *krow = (const bf16 *)p.k + b * p.kv_bs + rel;
-    const bf16 *vrow = (const bf16 *)p.v + b * p.kv_bs + rel;
+    const bf16 *krow = (const bf16 *)p.k + b * p.kv_bs + (int64_t)key * p.kv_ts + (int64_t)g * D +
+                       8 * half;
+    const bf16 *vrow = (const bf16 *)p.v + b * p.v_bs + (int64_t)key * p.v_ts + (int64_t)g * D +
+                       8 * half;
     const bool ld = kvalid && n > 0;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
@@ -646,7 +647,8 @@ bwd_dkdv_kernel(BwdParams p) {
   // per pass, 16 bytes per lane.
   const int key0 = kt * kBwdKvTile + wave * 32;
   const int rsub = lane >> 4, c4 = (lane & 15) * 4;
-  auto store = [&](const f32x16 (&acc)[DB], float mul, void *dst) __attribute__((always_inline)) {
+  auto store = [&](const f32x16 (&acc)[DB], float mul, void *dst, int64_t bs, int64_t ts)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int hd = 0; hd < DB / 2; ++hd) {
 #pragma unroll
@@ -664,22 +666,22 @@ bwd_dkdv_kernel(BwdParams p) {
         const int t = key0 + kr;
         const f32x4 val = *(const f32x4 *)&stage[wave][kr][c4];
         if (t < p.tk) {
-          const int64_t rel = (int64_t)t * p.kv_ts + (int64_t)g * D + 64 * hd + c4;
+          const int64_t rel = b * bs + (int64_t)t * ts + (int64_t)g * D + 64 * hd + c4;
           if (OUT_BF16) {
             bf16x4 hv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) hv[e] = (bf16)val[e];
-            *(bf16x4 *)((bf16 *)dst + b * p.dkv_bs + rel) = hv;
+            *(bf16x4 *)((bf16 *)dst + rel) = hv;
           } else {
-            *(f32x4 *)((float *)dst + b * p.dkv_bs + rel) = val;
+            *(f32x4 *)((float *)dst + rel) = val;
           }
         }
       }
     }
   };
   __syncthreads();  // the staging reuses the tile buffers
-  store(dk, p.scale, p.dk);
-  store(dv, 1.0f, p.dv);
+  store(dk, p.scale, p.dk, p.dkv_bs, p.kv_ts);
+  store(dv, 1.0f, p.dv, p.v_bs, p.v_ts);
 }
 
 // ----------------------------------------------------------------------------- launchers

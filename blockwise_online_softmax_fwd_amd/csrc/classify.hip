@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void pair_sum_kernel(const int64_t *__restrict
 }  // namespace
 
 WorkspaceLayout workspace_layout(int32_t batch, int32_t nqt, int32_t nkt, int32_t hkv,
-                                 int32_t packed_head_dim) {
+                                 int32_t packed_head_dim, int32_t packed_v_dim) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WorkspaceLayout w;
   size_t off = 0;
@@ -244,10 +244,11 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t nqt, int32_t nkt, int32_
   w.list = off;
   off = up(off + (size_t)batch * nqt * nkt * sizeof(uint32_t));
   const size_t tiles = packed_head_dim > 0 ? (size_t)batch * hkv * nkt : 0;
+  const int32_t vdim = packed_v_dim > 0 ? packed_v_dim : packed_head_dim;
   w.kpack = off;
-  off = up(off + tiles * kBnBf16 * packed_head_dim * 2);
+  off = up(off + tiles * (packed_head_dim > 0 ? packed_k_block_bytes(packed_head_dim) : 0));
   w.vpack = off;
-  off = up(off + tiles * kBnBf16 * packed_head_dim * 2);
+  off = up(off + tiles * kBnBf16 * vdim * 2);
   w.mpack = off;
   off = up(off + tiles * 2 * kBnBf16 * sizeof(int32_t));
   w.total = off;

@@ -44,9 +44,11 @@ struct WorkspaceLayout {
 };
 
 // packed_head_dim > 0 adds room for the packed K / V^T / metadata tiles of the
-// bf16 forward (batch * hkv * nkt tiles).
+// bf16 forward (batch * hkv * nkt tiles); packed_v_dim is V's head dim.
 WorkspaceLayout workspace_layout(int32_t batch, int32_t nqt, int32_t nkt, int32_t hkv = 0,
-                                 int32_t packed_head_dim = 0);
+                                 int32_t packed_head_dim = 0, int32_t packed_v_dim = 0);
+// Bytes of one packed 64-key K block for a Q/K head dim (rows padded for 192).
+size_t packed_k_block_bytes(int32_t head_dim);
 
 // Packed K/V tiles of the bf16 forward.
 struct PackParams {
@@ -55,10 +57,12 @@ struct PackParams {
   void *kpack, *vpack;
   int32_t *mpack;
   int64_t kv_bs, km_bs;
-  int64_t kv_ts;             // token stride of K and V (elements)
+  int64_t kv_ts;             // token stride of K (elements)
+  int64_t v_bs, v_ts;        // batch and token strides of V
   int32_t batch, tk, hkv, nkt;
 };
-hipError_t launch_pack_kv(const PackParams &p, int32_t head_dim, hipStream_t stream);
+hipError_t launch_pack_kv(const PackParams &p, int32_t head_dim, int32_t v_head_dim,
+                          hipStream_t stream);
 
 struct AttnParams {
   const void *q, *k, *v;
@@ -71,6 +75,7 @@ struct AttnParams {
   const int32_t *mpack;
   int64_t q_bs, kv_bs, o_bs, lse_bs, qm_bs, km_bs;  // batch strides (elements)
   int64_t q_ts, kv_ts, o_ts;  // token strides (elements); the running partial has o's
+  int64_t v_bs, v_ts;         // V's batch and token strides
   int32_t batch, tq, tk, hq, hkv, group;
   int32_t nqt, nkt;
   float scale;       // score scale
@@ -96,8 +101,8 @@ hipError_t launch_classify(const Schedule &s, const int32_t *qid, const int32_t 
 hipError_t launch_pair_sums(const int64_t *pairs, int32_t batch, int32_t nqt, int64_t *out,
                             hipStream_t stream);
 // bf16 MFMA forward; nt = token sub-tiles per workgroup (1, 2, 4 or 8).
-hipError_t launch_attn_bf16(const AttnParams &p, int32_t head_dim, int32_t nt, bool out_bf16,
-                            hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnParams &p, int32_t head_dim, int32_t v_head_dim, int32_t nt,
+                            bool out_bf16, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams &p, int32_t head_dim, bool out_bf16,
                            hipStream_t stream);
 
@@ -153,7 +158,8 @@ struct BwdParams {
   const int32_t *tcount;
   void *kvpack, *qpack;
   int64_t q_bs, kv_bs, o_bs, do_bs, lse_bs, qm_bs, km_bs, dq_bs, dkv_bs;
-  int64_t q_ts, kv_ts, o_ts;           // token strides: dq like q, dk/dv like k, dO like o
+  int64_t q_ts, kv_ts, o_ts;           // token strides: dq like q, dk like k, dO like o
+  int64_t v_bs, v_ts;                  // V's strides, also dv's
   int32_t batch, tq, tk, hq, hkv, group;
   int32_t nqt, nkt;                    // dQ schedule tiles
   int32_t tnk, tnq;                    // dK/dV schedule: key tiles (128), query tiles (32)

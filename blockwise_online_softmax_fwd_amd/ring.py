@@ -46,13 +46,18 @@ class RingBuffers:
     workspace: torch.Tensor | None = None
 
     @classmethod
-    def like(cls, q, k, ids, cp_size, partial_dtype=torch.float32, out_dtype=None, partials=True):
-        b, t, hq, d = q.shape
+    def like(cls, q, k, ids, cp_size, partial_dtype=torch.float32, out_dtype=None, partials=True,
+             v=None):
+        """Buffers for inputs shaped like q, k (and v, whose head dim O takes;
+        k's when v is not given)."""
+        b, t, hq, _ = q.shape
+        d = (k if v is None else v).shape[3]
         n = t // cp_size if partials else 0
         dev = q.device
         od = q.dtype if out_dtype is None else out_dtype
         return cls(
-            q=torch.empty_like(q), k=torch.empty_like(k), v=torch.empty_like(k),
+            q=torch.empty_like(q), k=torch.empty_like(k),
+            v=torch.empty_like(k if v is None else v),
             ids=torch.empty_like(ids), pos=torch.empty_like(ids),
             o=torch.empty((b, t, hq, d), dtype=od, device=dev),
             lse=torch.empty((b, t, hq), dtype=torch.float32, device=dev),
@@ -185,12 +190,13 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     if q.shape[1] != k.shape[1]:
         raise ValueError("the ring driver runs self-attention (Tq == Tk)")
     if bufs is None:
-        bufs = RingBuffers.like(q, k, ids, cp_size, partial_dtype, out_dtype)
+        bufs = RingBuffers.like(q, k, ids, cp_size, partial_dtype, out_dtype, v=v)
     if bufs.workspace is None:
         b, t = ids.shape
         n = t // cp_size
         desc = ra.make_desc(b, n, n, q.shape[2], k.shape[2], q.shape[3],
-                            ra._dtype_code(q.dtype), None, scale, causal, window)
+                            ra._dtype_code(q.dtype), None, scale, causal, window,
+                            {"v_head_dim": v.shape[3]})
         bufs.workspace = torch.empty(max(1, ra.workspace_size(desc)), dtype=torch.uint8,
                                      device=q.device)
     if step_hook:
@@ -228,10 +234,11 @@ def allgather_forward(q, k, v, ids, pos, cp_size, kind="striped", stripe_size=51
     b, t = ids.shape
     n = t // cp_size
     if bufs is None:
-        bufs = RingBuffers.like(q, k, ids, cp_size, out_dtype=out_dtype, partials=False)
+        bufs = RingBuffers.like(q, k, ids, cp_size, out_dtype=out_dtype, partials=False, v=v)
     if bufs.workspace is None:
         desc = ra.make_desc(b, n, t, q.shape[2], k.shape[2], q.shape[3],
-                            ra._dtype_code(q.dtype), None, scale, causal, window)
+                            ra._dtype_code(q.dtype), None, scale, causal, window,
+                            {"v_head_dim": v.shape[3]})
         bufs.workspace = torch.empty(max(1, ra.workspace_size(desc)), dtype=torch.uint8,
                                      device=q.device)
     if step_hook:

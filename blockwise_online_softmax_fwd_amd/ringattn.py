@@ -45,7 +45,9 @@ class AttnDesc(ctypes.Structure):
         (n, ctypes.c_int64) for n in (
             "q_batch_stride", "kv_batch_stride", "o_batch_stride", "lse_batch_stride",
             "q_meta_batch_stride", "kv_meta_batch_stride", "q_token_stride", "kv_token_stride",
-            "o_token_stride")]
+            "o_token_stride")] + [("v_head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                                  ("v_batch_stride", ctypes.c_int64),
+                                  ("v_token_stride", ctypes.c_int64)]
 
 
 class Partial(ctypes.Structure):
@@ -195,7 +197,7 @@ def workspace_size(desc: AttnDesc) -> int:
     return n.value
 
 
-def _attn_desc(q, k, q_ids, kv_ids, scale, causal, window, out_dtype, o, lse):
+def _attn_desc(q, k, q_ids, kv_ids, scale, causal, window, out_dtype, o, lse, v=None):
     b, tq, hq, d = q.shape
     tk, hkv = k.shape[1], k.shape[2]
     (qbs, qts), (kbs, kts) = _bt_strides(q), _bt_strides(k)
@@ -209,6 +211,9 @@ def _attn_desc(q, k, q_ids, kv_ids, scale, causal, window, out_dtype, o, lse):
         strides["o_batch_stride"], strides["o_token_stride"] = _bt_strides(o)
     if lse is not None:
         strides["lse_batch_stride"] = _batch_stride(lse, 2)
+    if v is not None:
+        strides["v_head_dim"] = v.shape[3]
+        strides["v_batch_stride"], strides["v_token_stride"] = _bt_strides(v)
     return make_desc(b, tq, tk, hq, hkv, d, _dtype_code(q.dtype), out_dtype, scale, causal,
                      window, strides)
 
@@ -217,17 +222,16 @@ def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
              causal=True, window=(-1, -1), out_dtype=None, out=None, lse=None, workspace=None):
     """Masked GQA attention forward.  Returns ``(o, lse)``.
 
-    q ``[B,Tq,Hq,D]``, k/v ``[B,Tk,Hkv,D]`` (bf16 or fp32, same dtype), ids/pos
-    int32 ``[B,T]``.  ``out``/``lse`` may be given (e.g. views into a larger
-    buffer along the sequence axis); otherwise they are allocated.
+    q ``[B,Tq,Hq,D]``, k ``[B,Tk,Hkv,D]``, v ``[B,Tk,Hkv,Dv]`` (bf16 or fp32,
+    same dtype; Dv = D, or D = 192 with Dv = 128 for MLA head dims in bf16),
+    ids/pos int32 ``[B,T]``.  O is ``[B,Tq,Hq,Dv]``.  ``out``/``lse`` may be
+    given (views into larger or packed buffers); otherwise they are allocated.
     """
     _require_gpu(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
-    if k.shape != v.shape:
-        raise ValueError("k and v must have the same shape")
-    if _bt_strides(v) != _bt_strides(k):
-        raise ValueError("k and v must have the same batch and token strides")
+    if k.shape[:3] != v.shape[:3]:
+        raise ValueError("k and v must have the same batch, length and heads")
     for t in (q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos):
         if t.dtype != torch.int32:
             raise TypeError("segment ids and positions must be int32")
@@ -236,12 +240,12 @@ def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
     b, tq, hq, d = q.shape
     oc = _dtype_code(q.dtype) if out_dtype is None else _dtype_code(out_dtype)
     if out is None:
-        out = torch.empty((b, tq, hq, d), dtype=_torch_dtype(oc), device=q.device)
+        out = torch.empty((b, tq, hq, v.shape[3]), dtype=_torch_dtype(oc), device=q.device)
     elif _dtype_code(out.dtype) != oc:
         raise TypeError("out has the wrong dtype")
     if lse is None:
         lse = torch.empty((b, tq, hq), dtype=torch.float32, device=q.device)
-    desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window, oc, out, lse)
+    desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window, oc, out, lse, v)
     ws_bytes = workspace_size(desc)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
@@ -262,10 +266,10 @@ def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, k
     _require_gpu(q, k, v, partial_o, partial_lse)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
-    if k.shape != v.shape or _bt_strides(v) != _bt_strides(k):
-        raise ValueError("k and v must have the same shape and strides")
+    if k.shape[:3] != v.shape[:3]:
+        raise ValueError("k and v must have the same batch, length and heads")
     b, tq, hq, d = q.shape
-    if tuple(partial_o.shape) != (b, tq, hq, d) or tuple(partial_lse.shape) != (b, tq, hq):
+    if tuple(partial_o.shape) != (b, tq, hq, v.shape[3]) or tuple(partial_lse.shape) != (b, tq, hq):
         raise ValueError("the partial must have o's and lse's shapes")
     if partial_lse.dtype != torch.float32:
         raise TypeError("partial lse must be float32")
@@ -276,7 +280,7 @@ def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, k
     oc = _dtype_code(out.dtype) if out_dtype is None else _dtype_code(out_dtype)
     if _dtype_code(out.dtype) != oc:
         raise TypeError("out has the wrong dtype")
-    desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window, oc, out, lse)
+    desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window, oc, out, lse, v)
     part = Partial()
     part.o, part.lse = partial_o.data_ptr(), partial_lse.data_ptr()
     part.dtype = _dtype_code(partial_o.dtype)
@@ -317,8 +321,8 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
         raise TypeError("the backward needs bfloat16 q, k and v")
     if dout.dtype != torch.bfloat16:
         raise TypeError("dout must be bfloat16")
-    if k.shape != v.shape or _bt_strides(v) != _bt_strides(k):
-        raise ValueError("k and v must have the same shape and strides")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape (the backward needs Dv == D)")
     if o.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != tuple(q.shape[:3]):
         raise ValueError("o and dout must have q's shape, lse [B,Tq,Hq]")
     if _bt_strides(dout) != _bt_strides(o):
@@ -339,12 +343,12 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
     if dk is None:
         dk = like(k)
     if dv is None:
-        dv = like(k)
-    for t, like in ((dq, q), (dk, k), (dv, k)):
-        if t.dtype != gdt or t.shape != like.shape or _bt_strides(t) != _bt_strides(like):
+        dv = like(v)
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.dtype != gdt or t.shape != ref.shape or _bt_strides(t) != _bt_strides(ref):
             raise ValueError("gradient buffers must have grad_dtype and their input's shape and strides")
     desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window,
-                      _dtype_code(o.dtype), o, lse)
+                      _dtype_code(o.dtype), o, lse, v)
     ws_bytes = bwd_workspace_size(desc)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
@@ -357,7 +361,7 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
 
 def classify_tiles(q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, *, num_q_heads,
                    num_kv_heads, head_dim=128, dtype=torch.bfloat16, causal=True, window=(-1, -1),
-                   workspace=None):
+                   workspace=None, v_head_dim=None):
     """Exact tile classes ``int8 [B, nqt, nkt]`` and visible pairs ``int64 [B]``."""
     _require_gpu(q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos)
     b, tq = q_segment_ids.shape
@@ -365,7 +369,8 @@ def classify_tiles(q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos,
     desc = make_desc(b, tq, tk, num_q_heads, num_kv_heads, head_dim, _dtype_code(dtype), None,
                      None, causal, window, {
                          "q_meta_batch_stride": _batch_stride(q_segment_ids, 1),
-                         "kv_meta_batch_stride": _batch_stride(kv_segment_ids, 1)})
+                         "kv_meta_batch_stride": _batch_stride(kv_segment_ids, 1),
+                         "v_head_dim": v_head_dim or 0})
     bm, bn = tile_shape(desc)
     nqt, nkt = -(-tq // bm), -(-tk // bn)
     dev = q_segment_ids.device

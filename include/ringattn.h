@@ -86,6 +86,10 @@ enum { RA_TILE_SKIP = 0, RA_TILE_PARTIAL = 1, RA_TILE_FULL = 2 };
  *   THD_T3HD (Q/K/V packed)       q = qkv, k = qkv + Hq*D, v = k + Hkv*D, all token
  *                                 strides (Hq + 2*Hkv)*D
  *   SBHD (sequence outermost)     token stride B*H*D, batch stride H*D
+ * MLA head dimensions ([TUT] "Next steps", single-GPU attention): v and o may have their own
+ * head dim Dv (v [B,Tk,Hkv,Dv], o [B,Tq,Hq,Dv]); the scale stays the caller's
+ * (head_dim^-1/2 of q and k in [TUT] s3).  Supported (head_dim, Dv) pairs: (64, 64),
+ * (128, 128) and, for the bf16 forward, (192, 128).
  * The (batch, token) rows of each tensor must nest without overlap: with
  * L = H*D, either token stride >= L and batch stride >= (T-1)*token stride + L,
  * or batch stride >= L and token stride >= (B-1)*batch stride + L.
@@ -111,7 +115,11 @@ typedef struct ra_attn_desc {
   int64_t kv_meta_batch_stride;
   int64_t q_token_stride;   /* elements between consecutive tokens of q; 0 = Hq*D          */
   int64_t kv_token_stride;  /* the same for k and v (one value for both); 0 = Hkv*D         */
-  int64_t o_token_stride;   /* the same for o (and a running partial, dout); 0 = Hq*D      */
+  int64_t o_token_stride;   /* the same for o (and a running partial, dout); 0 = Hq*Dv     */
+  int32_t v_head_dim;       /* Dv, head dim of v and o; 0 = head_dim (see below)           */
+  int32_t reserved;         /* 0                                                           */
+  int64_t v_batch_stride;   /* v's strides; 0 = k's when Dv == head_dim, else dense        */
+  int64_t v_token_stride;   /*   (Tk*Hkv*Dv and Hkv*Dv)                                    */
 } ra_attn_desc;
 
 /* Library identification and diagnostics.  The returned strings are static
@@ -125,8 +133,8 @@ const char *ra_last_error(void);
  * [CPP]): RA_OK if ra_attn_fwd implements this description, otherwise the
  * status it would return.  Supported: bf16 q/k/v (MFMA path) or fp32 q/k/v,
  * D in {64, 128}, bf16 or fp32 output, any Hq/Hkv group size, any lengths up to
- * 2^21 key tokens per call (2^20 for fp32).  Segment ids and positions must
- * be non-negative.  Makes no HIP call.
+ * 2^21 key tokens per call (2^20 for fp32), and the (head_dim, v_head_dim)
+ * pairs above.  Segment ids and positions must be non-negative.  Makes no HIP call.
  */
 ra_status ra_check_support(const ra_attn_desc *desc);
 

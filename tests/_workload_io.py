@@ -30,7 +30,7 @@ def device_inputs(w, zero_q=False, uniform_v=None):
     dt = torch.bfloat16
     q = torch.randn((w.batch, w.seq_len, w.num_q_heads, w.head_dim), generator=g, device=DEV).to(dt)
     k = torch.randn((w.batch, w.seq_len, w.num_kv_heads, w.head_dim), generator=g, device=DEV).to(dt)
-    v = torch.randn((w.batch, w.seq_len, w.num_kv_heads, w.head_dim), generator=g, device=DEV).to(dt)
+    v = torch.randn((w.batch, w.seq_len, w.num_kv_heads, w.dv), generator=g, device=DEV).to(dt)
     if zero_q:
         q.zero_()
     if uniform_v is not None:

@@ -338,3 +338,25 @@ def test_bwd_packed_gradients_are_not_aliases(lib):
                 dv=_p(base + 512 * 4)) == WS
     assert _bwd(lib, dq3, ws=None, dq=_p(base), dk=_p(base + 128 * 4),
                 dv=_p(base + 512 * 4)) == ALIAS
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=192, v_head_dim=128), OK),
+    (dict(head_dim=128, v_head_dim=128), OK),
+    (dict(head_dim=64, v_head_dim=0), OK),
+    (dict(head_dim=192), UNSUP),                       # v_head_dim 0 means 192
+    (dict(head_dim=128, v_head_dim=64), UNSUP),
+    (dict(head_dim=192, v_head_dim=128, qkv_dtype=ra.RA_F32), UNSUP),
+    (dict(v_head_dim=-1), SHAPE),
+    (dict(reserved=1), SHAPE),
+    (dict(head_dim=192, v_head_dim=128, v_token_stride=2 * 128 - 8), SHAPE),
+])
+def test_value_head_dim_support(lib, kw, status):
+    assert ra.check_support(_desc(**kw)) == status
+
+
+def test_mla_workspace_and_backward_rejected(lib):
+    d = _desc(head_dim=192, v_head_dim=128)
+    assert ra.workspace_size(d) > ra.workspace_size(_desc())
+    with pytest.raises(ra.RingAttnError, match="RA_ERR_UNSUPPORTED"):
+        ra.bwd_workspace_size(d)

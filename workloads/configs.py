@@ -42,6 +42,7 @@ class Workload:
     reorder: str = "none"   # "none" | "dual_chunk" | "striped"
     stripe: int = 1
     seed: int = field(default=0)
+    v_head_dim: int = 0     # head dim of V and O; 0 = head_dim
 
     @property
     def slot_len(self) -> int:
@@ -55,10 +56,15 @@ class Workload:
     def scale(self) -> float:
         return self.head_dim ** -0.5
 
+    @property
+    def dv(self) -> int:
+        return self.v_head_dim or self.head_dim
+
     def describe(self) -> str:
         w = self.window
+        dims = f"D{self.head_dim}" + (f"/Dv{self.dv}" if self.dv != self.head_dim else "")
         s = (f"B{self.batch} T{self.seq_len} Hq{self.num_q_heads}/Hkv{self.num_kv_heads} "
-             f"D{self.head_dim} {self.dtype} {'causal' if self.causal else 'full'} "
+             f"{dims} {self.dtype} {'causal' if self.causal else 'full'} "
              f"window({w[0]},{w[1]}) {self.slots}x({self.valid_per_slot} valid + "
              f"{self.slot_len - self.valid_per_slot} pad)")
         if self.cp_size > 1:
@@ -77,6 +83,12 @@ CONFIGS = {
                 1, 32768, seed=2030),
     5: Workload(5, "ring4_longctx_swa8192_gqa_bf16", 2, 65536, 128, 8, 128, "bf16", True,
                 (8192, 0), 4, 12288, cp_size=4, reorder="dual_chunk", seed=2031),
+    # DeepSeek-style MLA head dimensions (query/key 192 = 128 + 64 rotary, value
+    # 128), named by the tutorial's "Next steps" for single-GPU attention; the
+    # sizes are this suite's choice: one causal 8192-token segment per row,
+    # 128 heads with their own K/V (the decompressed form of MLA).
+    6: Workload(6, "mla_causal_bf16", 2, 8192, 128, 128, 192, "bf16", True, (-1, -1),
+                1, 8192, seed=2032, v_head_dim=128),
 }
 
 

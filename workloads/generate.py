@@ -40,12 +40,14 @@ def _dtype(name: str):
     return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
 
 
-def random_qkv(batch, q_len, kv_len, hq, hkv, d, dtype="bf16", seed=0, device="cpu"):
-    """Q ``[B,Tq,Hq,D]``, K and V ``[B,Tk,Hkv,D]``: N(0,1) drawn in fp32, then cast."""
+def random_qkv(batch, q_len, kv_len, hq, hkv, d, dtype="bf16", seed=0, device="cpu", dv=None):
+    """Q ``[B,Tq,Hq,D]``, K ``[B,Tk,Hkv,D]`` and V ``[B,Tk,Hkv,Dv]`` (Dv = D unless
+    given): N(0,1) drawn in fp32, then cast."""
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     out = []
-    for shape in ((batch, q_len, hq, d), (batch, kv_len, hkv, d), (batch, kv_len, hkv, d)):
+    dv = d if dv is None else dv
+    for shape in ((batch, q_len, hq, d), (batch, kv_len, hkv, d), (batch, kv_len, hkv, dv)):
         x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
         out.append(x.to(_dtype(dtype)))
     return tuple(out)
@@ -55,7 +57,7 @@ def qkv(w: Workload, device="cpu", seed=None):
     """Full-size Q, K, V of a workload (unsplit, original token order)."""
     s = w.seed if seed is None else seed
     return random_qkv(w.batch, w.seq_len, w.seq_len, w.num_q_heads, w.num_kv_heads,
-                      w.head_dim, w.dtype, s, device)
+                      w.head_dim, w.dtype, s, device, dv=w.dv)
 
 
 def random_layout(rng: np.random.Generator, batch: int, seq_len: int, max_segments: int = 4,
