@@ -146,7 +146,7 @@ def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, ste
 
 
 def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_heads, num_kv_heads,
-              head_dim=128, dtype=torch.bfloat16, causal=True, window=(-1, -1)):
+              head_dim=128, dtype=torch.bfloat16, causal=True, window=(-1, -1), v_head_dim=None):
     """Visible pairs of every ring step on this segment layout, ``int64 [R, R]``
     on the host (rank, step), from the library's tile classification.
 
@@ -169,7 +169,8 @@ def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_head
             _, pairs = ra.classify_tiles(ids_r[:, rows], pos_r[:, rows], ids_r[:, cols],
                                          pos_r[:, cols], num_q_heads=num_q_heads,
                                          num_kv_heads=num_kv_heads, head_dim=head_dim,
-                                         dtype=dtype, causal=causal, window=window)
+                                         dtype=dtype, causal=causal, window=window,
+                                         v_head_dim=v_head_dim)
             plan[r, s] = int(pairs.sum().item())
     return plan
 
