@@ -348,6 +348,39 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_bwd(w, q, k, v, do, q_ids, q_pos, kv_ids, kv_pos, budget_s):
+    """Backward oracle (fp64, host) on a bounded random sample of one shard's
+    query rows: dQ of each row over all heads (products S, dP, dQ: 6*D*Hq flops
+    per visible pair)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    qc, kc, vc, dc = q.cpu(), k.cpu(), v.cpu(), do.cpu()
+    iq, pq, ik, pk = q_ids.cpu(), q_pos.cpu(), kv_ids.cpu(), kv_pos.cpu()
+    rng = np.random.default_rng(1)
+    valid = np.argwhere(iq.numpy() != 0)
+    order = rng.permutation(len(valid))
+    rows, pairs, t0 = 0, 0, time.perf_counter()
+    for j in order:
+        b, i = int(valid[j][0]), int(valid[j][1])
+        oracle.backward_query_rows(qc, kc, vc, dc, iq, pq, ik, pk, [(b, i)], causal=w.causal,
+                                   window=w.window)
+        pairs += int(oracle.visible(iq[b, i:i + 1], pq[b, i:i + 1], ik[b], pk[b], w.causal,
+                                    w.window).sum())
+        rows += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 6.0 * w.head_dim * w.num_q_heads * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"dQ of {rows} random valid query rows of shard 0 x all {w.num_q_heads} heads "
+                      f"({pairs} visible pairs, {flops / 1e9:.1f} GFLOP fp64 at 6*D*Hq per pair) "
+                      f"in {dt:.1f} s"}
+
+
 BWD_METRIC = "attention bwd TFLOP/s (visible pairs, 10*D*Hq per pair) + % of bf16 MFMA peak, 1 MI355X"
 
 
@@ -424,6 +457,11 @@ def bench_backward(args, w, dev):
     call_ms = float(np.mean(calls))
     achieved = flops / cp / (call_ms / 1000.0) / 1e12
     log(f"{ms_step:.3f} ms/step, {value:.1f} TFLOP/s; attn_bwd {call_ms:.3f} ms per call")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 backward oracle on a host row sample")
+        qs, ds, iq, pq = shards[0][:4]
+        cpu = cpu_baseline_bwd(w, qs, k, v, ds, iq, pq, ids, pos, args.cpu_seconds)
     line = {
         "metric": BWD_METRIC,
         "value": value,
@@ -448,7 +486,7 @@ def bench_backward(args, w, dev):
                      "kernel": "attn_bwd call (prep, both classifications, packing, dq and "
                                "dk/dv passes)",
                      "per_launch_flops": flops / cp},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "detail": {"attn_bwd_calls_per_step": cp, "attn_bwd_avg_ms_per_call": call_ms,
                    "visible_pairs_per_step": visible,
                    "workspace_bytes": int(wsp.numel())},
