@@ -154,6 +154,19 @@ def _bt_strides(t):
     return bs, ts
 
 
+def _check_meta(q_ids, q_pos, kv_ids, kv_pos):
+    """Segment ids and positions: int32 [B, T], tokens contiguous, ids and
+    positions of one side sharing a batch stride."""
+    for t in (q_ids, q_pos, kv_ids, kv_pos):
+        if t.dtype != torch.int32 or t.dim() != 2:
+            raise TypeError("segment ids and positions must be int32 [B, T]")
+        if t.size(1) > 1 and t.stride(1) != 1:
+            raise ValueError("segment ids and positions must be contiguous along the tokens")
+    if (_batch_stride(q_pos, 1) != _batch_stride(q_ids, 1)
+            or _batch_stride(kv_pos, 1) != _batch_stride(kv_ids, 1)):
+        raise ValueError("segment ids and positions must share their batch stride")
+
+
 def _require_gpu(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
@@ -232,11 +245,7 @@ def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
         raise TypeError("q, k and v must share one dtype")
     if k.shape[:3] != v.shape[:3]:
         raise ValueError("k and v must have the same batch, length and heads")
-    for t in (q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos):
-        if t.dtype != torch.int32:
-            raise TypeError("segment ids and positions must be int32")
-    if q_segment_pos.stride() != q_segment_ids.stride() or kv_segment_pos.stride() != kv_segment_ids.stride():
-        raise ValueError("segment ids and positions must share strides")
+    _check_meta(q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos)
     b, tq, hq, d = q.shape
     oc = _dtype_code(q.dtype) if out_dtype is None else _dtype_code(out_dtype)
     if out is None:
@@ -271,6 +280,7 @@ def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, k
     b, tq, hq, d = q.shape
     if tuple(partial_o.shape) != (b, tq, hq, v.shape[3]) or tuple(partial_lse.shape) != (b, tq, hq):
         raise ValueError("the partial must have o's and lse's shapes")
+    _check_meta(q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos)
     if partial_lse.dtype != torch.float32:
         raise TypeError("partial lse must be float32")
     if out is None:
@@ -327,9 +337,7 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
         raise ValueError("o and dout must have q's shape, lse [B,Tq,Hq]")
     if _bt_strides(dout) != _bt_strides(o):
         raise ValueError("dout must have o's batch and token strides")
-    for t in (q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos):
-        if t.dtype != torch.int32:
-            raise TypeError("segment ids and positions must be int32")
+    _check_meta(q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos)
     gc = _dtype_code(grad_dtype)
     gdt = _torch_dtype(gc)
 
