@@ -22,6 +22,7 @@ from .ringattn import (  # noqa: F401
     inverse_reorder,
     load_library,
     make_desc,
+    profile_next_kernel,
     reorder,
     reorder_index,
     tile_shape,

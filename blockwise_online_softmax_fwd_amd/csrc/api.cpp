@@ -15,6 +15,8 @@
 namespace {
 
 thread_local std::string g_last_error;
+// Event pair armed by ra_profile_next_kernel for this thread's next forward call.
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 
 ra_status fail(ra_status st, const char *fmt, ...) {
   char buf[512];
@@ -289,6 +291,9 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
                         const int32_t *qid, const int32_t *qpos, const int32_t *kid,
                         const int32_t *kpos, const ra_partial *acc, void *o, float *lse,
                         void *workspace, size_t workspace_bytes, ra_stream_t stream) {
+  // an armed profiling pair belongs to this call, whatever its outcome
+  const hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
   Resolved r;
   ra_status st = check_desc(d, &r);
   if (st != RA_OK) return st;
@@ -418,10 +423,18 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
     if (pe != hipSuccess) return hip_fail(pe, "K/V tile packing");
   }
   const bool out_bf16 = d->out_dtype == RA_BF16;
+  if (ev0) {
+    const hipError_t ee = hipEventRecord(ev0, s);
+    if (ee != hipSuccess) return hip_fail(ee, "profiling start event");
+  }
   const hipError_t e = d->qkv_dtype == RA_BF16
                            ? ra::launch_attn_bf16(p, d->head_dim, r.dv, r.nt, out_bf16, s)
                            : ra::launch_attn_f32(p, d->head_dim, out_bf16, s);
   if (e != hipSuccess) return hip_fail(e, "attention forward");
+  if (ev1) {
+    const hipError_t ee = hipEventRecord(ev1, s);
+    if (ee != hipSuccess) return hip_fail(ee, "profiling stop event");
+  }
   return RA_OK;
 }
 
@@ -445,6 +458,14 @@ ra_status ra_attn_fwd_accumulate(const ra_attn_desc *d, const void *q, const voi
   if (!partial) return fail(RA_ERR_NULL, "partial is NULL");
   return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, partial, o, lse, workspace,
                        workspace_bytes, stream);
+}
+
+ra_status ra_profile_next_kernel(ra_event_t start, ra_event_t stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(RA_ERR_NULL, "profiling events: pass both or neither");
+  g_prof_start = (hipEvent_t)start;
+  g_prof_stop = (hipEvent_t)stop;
+  return RA_OK;
 }
 
 ra_status ra_classify_tiles(const ra_attn_desc *d, const int32_t *qid, const int32_t *qpos,

@@ -436,6 +436,31 @@ attn_fwd_bf16_kernel(AttnParams p) {
   const int c4 = (lane & 15) * 4;               // first of this lane's 4 columns
 #pragma unroll
   for (int hd = 0; hd < DB / 2; ++hd) {
+    // The running partial of the 8 pieces this lane writes in this half,
+    // loaded before any of them is stored so the loads are in flight
+    // together (in place, a lane reads exactly the addresses it writes);
+    // rows whose partial is empty (weight 0) are not read.
+    f32x4 acc[8];
+    if (p.acc_mode) {
+#pragma unroll
+      for (int pass = 0; pass < 8; ++pass) {
+        const int t = tq0 + 4 * pass + rsub;
+        const int64_t rel = (int64_t)t * p.o_ts + (int64_t)h * DVH + 64 * hd + c4;
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (t < p.tq && stage_w[wave][4 * pass + rsub] != 0.0f) {
+          if (p.acc_mode == 2) {
+            const bf16x4 ah = *(const bf16x4 *)((const bf16 *)p.acc_o + b * p.acc_o_bs + rel);
+            a[0] = (float)ah[0];
+            a[1] = (float)ah[1];
+            a[2] = (float)ah[2];
+            a[3] = (float)ah[3];
+          } else {
+            a = *(const f32x4 *)((const float *)p.acc_o + b * p.acc_o_bs + rel);
+          }
+        }
+        acc[pass] = a;
+      }
+    }
     // fragment columns of db = 2*hd, 2*hd+1 -> stage[wave][query][0..63]
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -457,19 +482,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
       if (t < p.tq) {
         const int64_t rel = (int64_t)t * p.o_ts + (int64_t)h * DVH + 64 * hd + c4;
         const float wa = stage_w[wave][qrow];
-        if (wa != 0.0f) {
-          f32x4 a;
-          if (p.acc_mode == 2) {
-            const bf16x4 ah = *(const bf16x4 *)((const bf16 *)p.acc_o + b * p.acc_o_bs + rel);
-            a[0] = (float)ah[0];
-            a[1] = (float)ah[1];
-            a[2] = (float)ah[2];
-            a[3] = (float)ah[3];
-          } else {
-            a = *(const f32x4 *)((const float *)p.acc_o + b * p.acc_o_bs + rel);
-          }
-          val += wa * a;
-        }
+        if (wa != 0.0f) val += wa * acc[pass];
         if (OUT_BF16) {
           bf16x4 hv;
           hv[0] = (bf16)val[0];

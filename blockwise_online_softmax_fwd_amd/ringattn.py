@@ -28,7 +28,8 @@ STATUS = {0: "RA_OK", 1: "RA_ERR_NULL", 2: "RA_ERR_SHAPE", 3: "RA_ERR_DTYPE", 4:
 EXPORTS = ["ra_version", "ra_status_string", "ra_last_error", "ra_check_support", "ra_tile_shape",
            "ra_attn_fwd_workspace_size", "ra_attn_fwd", "ra_attn_fwd_accumulate",
            "ra_classify_tiles", "ra_attn_merge", "ra_reorder", "ra_inverse_reorder",
-           "ra_reorder_index", "ra_attn_bwd_workspace_size", "ra_attn_bwd"]
+           "ra_reorder_index", "ra_attn_bwd_workspace_size", "ra_attn_bwd",
+           "ra_profile_next_kernel"]
 
 
 class RingAttnError(RuntimeError):
@@ -94,6 +95,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ra_reorder_index": ([I32, I32, I32, I32, I32, P], I32),
         "ra_attn_bwd_workspace_size": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)], I32),
         "ra_attn_bwd": ([ctypes.POINTER(AttnDesc)] + [P] * 10 + [I32] + [P] * 3 + [P, SZ, P], I32),
+        "ra_profile_next_kernel": ([P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -365,6 +367,21 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
         _ptr(kv_segment_ids), _ptr(kv_segment_pos), _ptr(o), _ptr(lse), _ptr(dout), gc, _ptr(dq),
         _ptr(dk), _ptr(dv), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(q)))
     return dq, dk, dv
+
+
+def profile_next_kernel(start, stop):
+    """Arm a pair of ``torch.cuda.Event(enable_timing=True)`` for the next
+    forward call on this thread: ``start`` is recorded right before its
+    attention kernel and ``stop`` right after it (classification and K/V
+    packing fall outside).  ``None, None`` disarms."""
+    if start is None and stop is None:
+        _check(load_library().ra_profile_next_kernel(None, None))
+        return
+    for ev in (start, stop):
+        if ev.cuda_event == 0:   # torch creates the event on its first record
+            ev.record()
+    _check(load_library().ra_profile_next_kernel(ctypes.c_void_p(start.cuda_event),
+                                                 ctypes.c_void_p(stop.cuda_event)))
 
 
 def classify_tiles(q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, *, num_q_heads,

@@ -40,6 +40,8 @@ extern "C" {
 
 /* Same type as hipStream_t. */
 typedef struct ihipStream_t *ra_stream_t;
+/* Same type as hipEvent_t. */
+typedef struct ihipEvent_t *ra_event_t;
 
 typedef enum ra_status {
   RA_OK = 0,
@@ -199,6 +201,19 @@ ra_status ra_attn_fwd_accumulate(const ra_attn_desc *desc, const void *q, const 
                                  const int32_t *kv_segment_pos, const ra_partial *partial, void *o,
                                  float *lse, void *workspace, size_t workspace_bytes,
                                  ra_stream_t stream);
+
+/*
+ * Measurement hook (for timing the attention kernel apart from the tile
+ * classification and K/V packing that precede it in the same call).  The next
+ * ra_attn_fwd or ra_attn_fwd_accumulate call made on the calling thread
+ * records `start` on its stream immediately before its attention kernel and
+ * `stop` immediately after it.  Both are events the caller created
+ * (hipEventCreate) and keeps owning; both NULL disarms a pending pair, exactly
+ * one NULL is RA_ERR_NULL.  The pair is consumed by that one call: a call that
+ * fails, or that launches no attention kernel (an empty batch), leaves the
+ * events unrecorded.  Records only; it never synchronises.
+ */
+ra_status ra_profile_next_kernel(ra_event_t start, ra_event_t stop);
 
 /*
  * The exact tile classes of the mask at the tile shape of ra_tile_shape()

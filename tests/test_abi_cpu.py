@@ -104,6 +104,19 @@ def test_null_desc(lib):
     assert lib.ra_attn_fwd(None, *([None] * 9), None, 0, None) == NULL
 
 
+def test_profile_hook_arguments(lib):
+    """Both events or neither; an armed pair is consumed by the next forward
+    call even when that call fails validation (here before any HIP call, so
+    the placeholder handles are never touched)."""
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.ra_profile_next_kernel(fake, None) == NULL
+    assert lib.ra_profile_next_kernel(None, fake) == NULL
+    assert lib.ra_profile_next_kernel(None, None) == OK
+    assert lib.ra_profile_next_kernel(fake, ctypes.c_void_p(0x2000)) == OK
+    assert lib.ra_attn_fwd(None, *([None] * 9), None, 0, None) == NULL
+    assert lib.ra_profile_next_kernel(None, None) == OK
+
+
 @pytest.mark.parametrize("hq,hkv,bm", [(16, 2, 32), (128, 8, 32), (64, 8, 32), (8, 2, 64),
                                        (4, 1, 64), (3, 1, 256), (12, 1, 64), (6, 3, 128)])
 def test_tile_shape_bf16(hq, hkv, bm):
