@@ -270,6 +270,10 @@ attn_fwd_bf16_kernel(AttnParams p) {
       }
     }
   }
+  // LSE of the running partial for this lane's row, read now so the epilogue
+  // does not wait for it
+  const float la = p.acc_mode && qvalid ? p.acc_lse[b * p.acc_lse_bs + (int64_t)tq * p.hq + h]
+                                        : -INFINITY;
   LaneMask lm;
   {
     const int my_qid = qvalid ? p.qid[b * p.qm_bs + tq] : 0;
@@ -423,7 +427,6 @@ attn_fwd_bf16_kernel(AttnParams p) {
   float w_own = live ? 1.0f / zt : 0.0f;
   float w_acc = 0.0f, l_out = l_own;
   if (p.acc_mode && qvalid) {
-    const float la = p.acc_lse[b * p.acc_lse_bs + (int64_t)tq * p.hq + h];
     l_out = lse_add(l_own, la);
     w_acc = lse_weight(la, l_out);
     w_own = live ? lse_weight(l_own, l_out) / zt : 0.0f;
@@ -434,33 +437,40 @@ attn_fwd_bf16_kernel(AttnParams p) {
   const int tq0 = qt * BM + (wave / NH) * 32;   // first query token of this wave
   const int rsub = lane >> 4;                   // row within a group of 4 rows
   const int c4 = (lane & 15) * 4;               // first of this lane's 4 columns
+  // The running partial of the pieces this lane writes, loaded before any of
+  // them is stored so the loads are in flight together (in place, a lane
+  // reads exactly the addresses it later writes); rows whose partial is empty
+  // (weight 0) are not read.  Both halves at once where registers allow
+  // (MLA's kernel has none to spare: one half at a time there).
+  constexpr int PH = D == 192 ? 1 : DB / 2;   // halves loaded up front
+  f32x4 acc[DB / 2][8];
+  auto load_half = [&](int hd) {
+#pragma unroll
+    for (int pass = 0; pass < 8; ++pass) {
+      const int t = tq0 + 4 * pass + rsub;
+      const int64_t rel = (int64_t)t * p.o_ts + (int64_t)h * DVH + 64 * hd + c4;
+      f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (t < p.tq && stage_w[wave][4 * pass + rsub] != 0.0f) {
+        if (p.acc_mode == 2) {
+          const bf16x4 ah = *(const bf16x4 *)((const bf16 *)p.acc_o + b * p.acc_o_bs + rel);
+          a[0] = (float)ah[0];
+          a[1] = (float)ah[1];
+          a[2] = (float)ah[2];
+          a[3] = (float)ah[3];
+        } else {
+          a = *(const f32x4 *)((const float *)p.acc_o + b * p.acc_o_bs + rel);
+        }
+      }
+      acc[hd][pass] = a;
+    }
+  };
+  if (p.acc_mode) {
+#pragma unroll
+    for (int hd = 0; hd < PH; ++hd) load_half(hd);
+  }
 #pragma unroll
   for (int hd = 0; hd < DB / 2; ++hd) {
-    // The running partial of the 8 pieces this lane writes in this half,
-    // loaded before any of them is stored so the loads are in flight
-    // together (in place, a lane reads exactly the addresses it writes);
-    // rows whose partial is empty (weight 0) are not read.
-    f32x4 acc[8];
-    if (p.acc_mode) {
-#pragma unroll
-      for (int pass = 0; pass < 8; ++pass) {
-        const int t = tq0 + 4 * pass + rsub;
-        const int64_t rel = (int64_t)t * p.o_ts + (int64_t)h * DVH + 64 * hd + c4;
-        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (t < p.tq && stage_w[wave][4 * pass + rsub] != 0.0f) {
-          if (p.acc_mode == 2) {
-            const bf16x4 ah = *(const bf16x4 *)((const bf16 *)p.acc_o + b * p.acc_o_bs + rel);
-            a[0] = (float)ah[0];
-            a[1] = (float)ah[1];
-            a[2] = (float)ah[2];
-            a[3] = (float)ah[3];
-          } else {
-            a = *(const f32x4 *)((const float *)p.acc_o + b * p.acc_o_bs + rel);
-          }
-        }
-        acc[pass] = a;
-      }
-    }
+    if (hd >= PH && p.acc_mode) load_half(hd);
     // fragment columns of db = 2*hd, 2*hd+1 -> stage[wave][query][0..63]
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -482,7 +492,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
       if (t < p.tq) {
         const int64_t rel = (int64_t)t * p.o_ts + (int64_t)h * DVH + 64 * hd + c4;
         const float wa = stage_w[wave][qrow];
-        if (wa != 0.0f) val += wa * acc[pass];
+        if (wa != 0.0f) val += wa * acc[hd][pass];
         if (OUT_BF16) {
           bf16x4 hv;
           hv[0] = (bf16)val[0];
