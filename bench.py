@@ -12,9 +12,11 @@ and LSE.  All four shards are computed, so a step is the complete forward of
 B=2 x 65536 tokens; FLOPs count only visible pairs (4 * head_dim * Hq per pair).
 attn_merge is also timed on its own at the shard partials' shape.
 
-Prints one JSON line.  ``roofline`` is measured live with HIP events around
-every attn_fwd call (on the stream the library launches on); ``cpu_baseline``
-times the fp64 oracle on a bounded row sample of the same inputs.
+Prints one JSON line.  ``roofline`` is measured live with HIP events that the
+library records on its stream right before and after the attention kernel of
+every forward call (``ra_profile_next_kernel``; the call's tile classification
+and K/V repack fall outside); ``cpu_baseline`` times the fp64 oracle on a
+bounded row sample of the same inputs.
 """
 
 from __future__ import annotations
