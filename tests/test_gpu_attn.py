@@ -314,3 +314,41 @@ def test_workload_uniform_v_every_row(cfg):
     err = (o[live].float() - ref[None]).abs().max().item()
     assert err <= 2e-2, err
     assert torch.isneginf(lse[~live]).all() and (o[~live] == 0).all()
+
+
+def _ramp_inputs(kind, b=1, tq=256, tk=1024, hq=8, hkv=1, d=128):
+    """Q and K whose scores sweep a range of ~300 natural-log units: rising
+    along the keys (the running max must be raised on every tile), falling
+    (the first tile holds the max and later probabilities underflow to 0), or
+    random with a spread of ~+-100."""
+    g = torch.Generator().manual_seed({"up": 11, "down": 12, "wide": 13}[kind])
+    v = torch.randn((b, tk, hkv, d), generator=g).to(torch.bfloat16)
+    if kind == "wide":
+        q = (6.0 * torch.randn((b, tq, hq, d), generator=g)).to(torch.bfloat16)
+        k = (6.0 * torch.randn((b, tk, hkv, d), generator=g)).to(torch.bfloat16)
+        return q, k, v
+    q = torch.ones((b, tq, hq, d)).to(torch.bfloat16)
+    j = torch.arange(tk, dtype=torch.float32)
+    ramp = (j if kind == "up" else tk - 1 - j) / tk * 26.5
+    k = ramp[None, :, None, None].expand(b, tk, hkv, d).to(torch.bfloat16).contiguous()
+    return q, k, v
+
+
+@pytest.mark.parametrize("kind", ["up", "down", "wide"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_over_wide_score_ranges(kind, causal):
+    """The lazy running max: raised on (nearly) every tile, never raised, and
+    raised at random, with O and LSE against the oracle.  Without the rescale
+    the rising case would overflow (e^300)."""
+    q, k, v = _ramp_inputs(kind)
+    tq, tk = q.shape[1], k.shape[1]
+    qi = torch.ones((1, tq), dtype=torch.int32)
+    ki = torch.ones((1, tk), dtype=torch.int32)
+    qp = torch.arange(tk - tq, tk, dtype=torch.int32)[None]   # queries see every key causally
+    kp = torch.arange(tk, dtype=torch.int32)[None]
+    o, lse = bosf.attn_fwd(*_dev(q, k, v, qi, qp, ki, kp), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q, k, v, qi, qp, ki, kp, causal=causal)
+    e = compare(o, lse, ro, rl, "bf16", f"{kind} causal={causal}")
+    print(f"{kind} causal={causal}: LSE range {rl.min():.1f}..{rl.max():.1f}, "
+          f"max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
