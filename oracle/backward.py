@@ -131,7 +131,8 @@ def backward_query_rows(q, k, v, do, qid, qpos, kid, kpos, rows, scale=None, cau
 
 def backward_key_rows(q, k, v, do, qid, qpos, kid, kpos, keys, scale=None, causal=True,
                       window=(-1, -1)):
-    """(dK, dV) of selected key rows ``[(b, t), ...]``: each ``[len(keys), Hkv, D]``.
+    """(dK, dV) of selected key rows ``[(b, t), ...]``: ``[len(keys), Hkv, D]`` and
+    ``[len(keys), Hkv, Dv]`` (dV has V's head dim).
 
     A key's gradients gather every query that sees it; each such query's
     softmax needs that query's whole visible key set.
@@ -142,7 +143,7 @@ def backward_key_rows(q, k, v, do, qid, qpos, kid, kpos, keys, scale=None, causa
     if scale is None:
         scale = d ** -0.5
     dk = np.zeros((len(keys), hkv, d))
-    dv = np.zeros((len(keys), hkv, d))
+    dv = np.zeros((len(keys), hkv, v.shape[3]))
     for n, (b, j) in enumerate(keys):
         seen = visible(i64(qid[b]), i64(qpos[b]), i64(kid[b, j:j + 1]), i64(kpos[b, j:j + 1]),
                        causal, window)[:, 0]

@@ -179,3 +179,11 @@ def test_backward_value_head_dim_differs_torch_autograd():
     np.testing.assert_allclose(dq, tq_.grad.numpy(), atol=1e-11, rtol=0)
     np.testing.assert_allclose(dk, tk_.grad.numpy(), atol=1e-11, rtol=0)
     np.testing.assert_allclose(dv_, tv_.grad.numpy(), atol=1e-11, rtol=0)
+    # the sampled forms agree with the full one at a distinct V head dim too
+    rows = [(0, 0), (0, 12), (1, 30)]
+    gq = oracle.backward_query_rows(q, k, v, do, qi, qp, qi, qp, rows, window=(7, 0))
+    np.testing.assert_allclose(gq, np.stack([dq[b_, t_] for b_, t_ in rows]), atol=1e-12, rtol=0)
+    gk, gv = oracle.backward_key_rows(q, k, v, do, qi, qp, qi, qp, rows, window=(7, 0))
+    assert gv.shape == (len(rows), hkv, dv)
+    np.testing.assert_allclose(gk, np.stack([dk[b_, t_] for b_, t_ in rows]), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(gv, np.stack([dv_[b_, t_] for b_, t_ in rows]), atol=1e-12, rtol=0)
