@@ -365,8 +365,8 @@ def main():
 
 def cpu_baseline_bwd(w, q, k, v, do, q_ids, q_pos, kv_ids, kv_pos, budget_s):
     """Backward oracle (fp64, host) on a bounded random sample of one shard's
-    query rows: dQ of each row over all heads (products S, dP, dQ: 6*D*Hq flops
-    per visible pair)."""
+    query rows: dQ of each row over all heads (products S, dP, dQ: 2*(2D+Dv)*Hq
+    flops per visible pair, 6*D*Hq when D = Dv)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -389,14 +389,14 @@ def cpu_baseline_bwd(w, q, k, v, do, q_ids, q_pos, kv_ids, kv_pos, budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    flops = 6.0 * w.head_dim * w.num_q_heads * pairs
+    flops = 2.0 * (2 * w.head_dim + w.dv) * w.num_q_heads * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"dQ of {rows} random valid query rows of shard 0 x all {w.num_q_heads} heads "
-                      f"({pairs} visible pairs, {flops / 1e9:.1f} GFLOP fp64 at 6*D*Hq per pair) "
+                      f"({pairs} visible pairs, {flops / 1e9:.1f} GFLOP fp64 at 2*(2D+Dv)*Hq per pair) "
                       f"in {dt:.1f} s"}
 
 
-BWD_METRIC = "attention bwd TFLOP/s (visible pairs, 10*D*Hq per pair) + % of bf16 MFMA peak, 1 MI355X"
+BWD_METRIC = "attention bwd TFLOP/s (visible pairs, 2*(3D+2Dv)*Hq per pair) + % of bf16 MFMA peak, 1 MI355X"
 
 
 def bench_backward(args, w, dev):
@@ -404,7 +404,9 @@ def bench_backward(args, w, dev):
     (striped reorder) against the whole gathered K/V, with dout ~ N(0, 1).
     One step computes dq of every query and each shard's dk/dv contribution
     (what a reduce-scatter would sum across devices).  FLOPs count only visible
-    pairs, 10 * head_dim * Hq per pair (the five products S, dP, dV, dK, dQ)."""
+    pairs, 2 * (3 * D + 2 * Dv) * Hq per pair (the five products S, dK and dQ
+    over Q/K's head dim D, dP and dV over V's head dim Dv; 10 * D * Hq when
+    they are equal)."""
     if w.cp_size > 1:
         w = dataclasses.replace(w, reorder="striped", stripe=args.stripe)
     desc = w.describe()
@@ -416,7 +418,7 @@ def bench_backward(args, w, dev):
     q, k, v, ids, pos = make_inputs(w, dev)
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed + 17)
-    do = torch.randn(q.shape, generator=g, device=dev).to(torch.bfloat16)
+    do = torch.randn(q.shape[:3] + (w.dv,), generator=g, device=dev).to(torch.bfloat16)
     cp = max(1, w.cp_size)
     if cp > 1:
         q, k, v, ids, pos, do = (bosf.reorder(t, cp, w.reorder, w.stripe) for t in (q, k, v, ids, pos, do))
@@ -429,19 +431,20 @@ def bench_backward(args, w, dev):
         iq, pq = ids[:, sl], pos[:, sl]
         o, lse = bosf.attn_fwd(qs, k, v, iq, pq, ids, pos, causal=w.causal, window=w.window)
         dk = torch.empty(k.shape, dtype=gdt, device=dev)
-        dv = torch.empty(k.shape, dtype=gdt, device=dev)
+        dv = torch.empty(v.shape, dtype=gdt, device=dev)
         dq = torch.empty(qs.shape, dtype=gdt, device=dev)
         shards.append((qs, ds, iq, pq, o, lse, dq, dk, dv))
     del q, do
     bdesc = bosf.make_desc(w.batch, n, w.seq_len, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                           strides={"q_meta_batch_stride": ids.stride(0)})
+                           strides={"q_meta_batch_stride": ids.stride(0), "v_head_dim": w.dv})
     wsp = torch.empty(bosf.bwd_workspace_size(bdesc), dtype=torch.uint8, device=dev)
     log(f"backward workspace {wsp.numel() / 2**30:.2f} GiB")
     _, pairs = bosf.classify_tiles(ids, pos, ids, pos, num_q_heads=w.num_q_heads,
                                    num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
-                                   dtype=k.dtype, causal=w.causal, window=w.window)
+                                   v_head_dim=w.dv, dtype=k.dtype, causal=w.causal,
+                                   window=w.window)
     visible = int(pairs.sum().item())
-    flops = 10.0 * w.head_dim * w.num_q_heads * visible
+    flops = 2.0 * (3 * w.head_dim + 2 * w.dv) * w.num_q_heads * visible
     log(f"visible pairs {visible}, {flops / 1e12:.3f} TFLOP per backward step")
     stream = torch.cuda.current_stream(dev)
     evs = []
@@ -493,7 +496,7 @@ def bench_backward(args, w, dev):
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "config": {"workload": f"{w.name} backward{' all-gather' if cp > 1 else ''}: {desc}",
                    "batch": w.batch, "seq_len": w.seq_len, "num_q_heads": w.num_q_heads,
-                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "v_head_dim": w.dv,
                    "window": list(w.window), "cp_shards": cp, "reorder": w.reorder,
                    "stripe": w.stripe, "grad_dtype": args.grad_dtype},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,

@@ -568,10 +568,10 @@ ra_status ra_attn_merge(const ra_merge_desc *d, const void *o_a, const float *ls
 namespace {
 
 // The backward's tile shapes: the dq pass uses the forward's (bm = 32 nt
-// queries, bn = 64 keys); the dk/dv pass tiles keys by kBwdKvTile and queries
-// by kBwdQTile.
+// queries, bn = 64 keys); the dk/dv pass tiles keys by bwd_kv_tile(head_dim)
+// and queries by kBwdQTile.
 struct BwdShape {
-  int32_t tnk, tnq;
+  int32_t tnk, tnq, kvt;
 };
 
 ra_status check_bwd_desc(const ra_attn_desc *d, Resolved *r, BwdShape *bs) {
@@ -579,9 +579,9 @@ ra_status check_bwd_desc(const ra_attn_desc *d, Resolved *r, BwdShape *bs) {
   if (st != RA_OK) return st;
   if (d->qkv_dtype != RA_BF16)
     return fail(RA_ERR_UNSUPPORTED, "the backward needs bf16 q, k and v");
-  if (r->dv != d->head_dim)
-    return fail(RA_ERR_UNSUPPORTED, "the backward needs v_head_dim == head_dim");
-  const int64_t tnk = ((int64_t)d->kv_len + ra::kBwdKvTile - 1) / ra::kBwdKvTile;
+  // check_desc admits only the head-dim pairs the kernels have: equal, or MLA's 192 / 128
+  const int kvt = ra::bwd_kv_tile(d->head_dim);
+  const int64_t tnk = ((int64_t)d->kv_len + kvt - 1) / kvt;
   const int64_t tnq = ((int64_t)d->q_len + ra::kBwdQTile - 1) / ra::kBwdQTile;
   if (tnq > kMaxKeyTiles)
     return fail(RA_ERR_UNSUPPORTED, "q_len %d exceeds %lld query tiles of %d tokens", d->q_len,
@@ -590,12 +590,13 @@ ra_status check_bwd_desc(const ra_attn_desc *d, Resolved *r, BwdShape *bs) {
     return fail(RA_ERR_UNSUPPORTED, "too many key tiles for one launch");
   bs->tnk = (int32_t)tnk;
   bs->tnq = (int32_t)tnq;
+  bs->kvt = kvt;
   return RA_OK;
 }
 
 ra::BwdLayout bwd_layout_of(const ra_attn_desc *d, const Resolved &r, const BwdShape &bs) {
   return ra::bwd_workspace_layout(d->batch, d->q_len, d->num_q_heads, d->num_kv_heads,
-                                  d->head_dim, r.nqt, r.nkt, bs.tnq, bs.tnk);
+                                  d->head_dim, r.dv, r.nqt, r.nkt, bs.tnq, bs.tnk);
 }
 
 // The mask with the roles of queries and keys swapped: with d = pos_q - pos_k
@@ -652,16 +653,19 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
   const int64_t D = d->head_dim;
   const int64_t B = d->batch, Tq = d->q_len, Tk = d->kv_len;
+  // row widths (elements): Q and K rows hold head_dim per head, V, O and dO
+  // rows v_head_dim per head
   const int64_t Lq = (int64_t)d->num_q_heads * D, Lk = (int64_t)d->num_kv_heads * D;
+  const int64_t Lo = (int64_t)d->num_q_heads * r.dv, Lv = (int64_t)d->num_kv_heads * r.dv;
   const size_t q_span = span_bytes2(B, Tq, Lq, r.q_bs, r.q_ts, 2);
   const size_t kv_span = span_bytes2(B, Tk, Lk, r.kv_bs, r.kv_ts, 2);
-  const size_t v_span = span_bytes2(B, Tk, Lk, r.v_bs, r.v_ts, 2);
-  const size_t o_span = span_bytes2(B, Tq, Lq, r.o_bs, r.o_ts, os);
-  const size_t do_span = span_bytes2(B, Tq, Lq, r.o_bs, r.o_ts, 2);
+  const size_t v_span = span_bytes2(B, Tk, Lv, r.v_bs, r.v_ts, 2);
+  const size_t o_span = span_bytes2(B, Tq, Lo, r.o_bs, r.o_ts, os);
+  const size_t do_span = span_bytes2(B, Tq, Lo, r.o_bs, r.o_ts, 2);
   const size_t l_span = span_bytes(B, r.lse_bs, Tq * d->num_q_heads, 4);
   const size_t dq_span = span_bytes2(B, Tq, Lq, r.q_bs, r.q_ts, gs);
   const size_t dkv_span = span_bytes2(B, Tk, Lk, r.kv_bs, r.kv_ts, gs);
-  const size_t dvv_span = span_bytes2(B, Tk, Lk, r.v_bs, r.v_ts, gs);
+  const size_t dvv_span = span_bytes2(B, Tk, Lv, r.v_bs, r.v_ts, gs);
   const void *ins[6] = {q, k, v, o, lse, dout};
   const size_t in_span[6] = {q_span, kv_span, v_span, o_span, l_span, do_span};
   const void *outs[3] = {dq, dk, dv};
@@ -674,7 +678,7 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   // strides, e.g. dk/dv of a packed K/V layout); otherwise their spans must not meet.
   const int64_t g = (int64_t)gs;
   const bool kv_same = r.kv_bs == r.v_bs && r.kv_ts == r.v_ts;
-  if (kv_same ? rows_overlap(dk, Tk, Lk * g, dv, Tk, Lk * g, B, r.kv_bs * g, r.kv_ts * g)
+  if (kv_same ? rows_overlap(dk, Tk, Lk * g, dv, Tk, Lv * g, B, r.kv_bs * g, r.kv_ts * g)
               : overlaps(dk, dkv_span, dv, dvv_span))
     return fail(RA_ERR_ALIAS, "dk and dv overlap");
   const bool qk_same = r.q_bs == r.kv_bs && r.q_ts == r.kv_ts;
@@ -682,7 +686,7 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   if (qk_same ? rows_overlap(dq, Tq, Lq * g, dk, Tk, Lk * g, B, r.q_bs * g, r.q_ts * g)
               : overlaps(dq, dq_span, dk, dkv_span))
     return fail(RA_ERR_ALIAS, "dq overlaps dk");
-  if (qv_same ? rows_overlap(dq, Tq, Lq * g, dv, Tk, Lk * g, B, r.q_bs * g, r.q_ts * g)
+  if (qv_same ? rows_overlap(dq, Tq, Lq * g, dv, Tk, Lv * g, B, r.q_bs * g, r.q_ts * g)
               : overlaps(dq, dq_span, dv, dvv_span))
     return fail(RA_ERR_ALIAS, "dq overlaps dv");
   if (!has_q && !has_k) return RA_OK;
@@ -747,7 +751,7 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   const bool out_bf16 = grad_dtype == RA_BF16;
 
   // Schedules: the forward's (query tiles x 64-key tiles) for dq, and the
-  // swapped one (128-key tiles x 32-query tiles) for dk/dv.
+  // swapped one (key tiles of bwd_kv_tile(head_dim) x 32-query tiles) for dk/dv.
   ra::Schedule fs;
   fs.qsum = (ra::TileSum *)(ws + L.qsum);
   fs.ksum = (ra::TileSum *)(ws + L.ksum);
@@ -764,27 +768,27 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   if (has_q) {
     st = run_schedule(d, r, fs, qid, qpos, kid, kpos, nullptr, s);
     if (st != RA_OK) return st;
-    e = ra::launch_bwd_prep(p, d->head_dim, d->out_dtype == RA_BF16, s);
+    e = ra::launch_bwd_prep(p, r.dv, d->out_dtype == RA_BF16, s);
     if (e != hipSuccess) return hip_fail(e, "backward prep");
   }
   if (has_k) {
-    e = ra::launch_summaries(kid, kpos, r.km_bs, d->batch, d->kv_len, ra::kBwdKvTile, bs.tnk, ts.qsum, s);
+    e = ra::launch_summaries(kid, kpos, r.km_bs, d->batch, d->kv_len, bs.kvt, bs.tnk, ts.qsum, s);
     if (e != hipSuccess) return hip_fail(e, "tile summaries (keys, swapped)");
     e = ra::launch_summaries(qid, qpos, r.qm_bs, d->batch, d->q_len, ra::kBwdQTile, bs.tnq, ts.ksum, s);
     if (e != hipSuccess) return hip_fail(e, "tile summaries (queries, swapped)");
     e = ra::launch_classify(ts, kid, kpos, qid, qpos, r.km_bs, r.qm_bs, d->batch, d->kv_len,
-                            d->q_len, ra::kBwdKvTile, ra::kBwdQTile, bs.tnk, bs.tnq,
+                            d->q_len, bs.kvt, ra::kBwdQTile, bs.tnk, bs.tnq,
                             swapped_mask(d), nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "tile classification (swapped)");
   }
-  e = ra::launch_bwd_pack(p, d->head_dim, s);
+  e = ra::launch_bwd_pack(p, d->head_dim, r.dv, s);
   if (e != hipSuccess) return hip_fail(e, "backward tile packing");
   if (has_q) {
-    e = ra::launch_bwd_dq(p, d->head_dim, r.nt, out_bf16, s);
+    e = ra::launch_bwd_dq(p, d->head_dim, r.dv, r.nt, out_bf16, s);
     if (e != hipSuccess) return hip_fail(e, "backward dq pass");
   }
   if (has_k) {
-    e = ra::launch_bwd_dkdv(p, d->head_dim, out_bf16, s);
+    e = ra::launch_bwd_dkdv(p, d->head_dim, r.dv, out_bf16, s);
     if (e != hipSuccess) return hip_fail(e, "backward dk/dv pass");
   }
   return RA_OK;

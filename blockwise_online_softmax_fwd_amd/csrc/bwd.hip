@@ -31,6 +31,9 @@
 //    without atomics.
 //    Per visit: S = Q K^T and dP = dO V^T (lane = key, rows = queries), then
 //    dV^T += dO^T P and dK^T += Q^T dS.
+// D is the head dim of Q and K, DV that of V, O and dO (equal, or the MLA pair
+// 192 / 128, for which the dK/dV workgroup has 4 waves: one per SIMD, whose
+// registers then hold the 192-wide K rows and both accumulators).
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <math.h>
@@ -52,9 +55,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ----------------------------------------------------------------------------- prep
 
-template <int D, bool OBF>
+// DV: head dim of O and dO.
+template <int DV, bool OBF>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
-  constexpr int TPR = D / 4;       // threads per row, 4 elements each
+  constexpr int TPR = DV / 4;      // threads per row, 4 elements each
   constexpr int RPB = 256 / TPR;   // rows per block and step
   const int64_t rows = (int64_t)p.batch * p.tq * p.hq;
   const int sub = threadIdx.x % TPR;
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
        r += (int64_t)gridDim.x * RPB) {
     const int64_t b = r / per_b, rr = r - b * per_b;   // rr = t * hq + h
     const int64_t t = rr / p.hq, h = rr - t * p.hq;
-    const int64_t col = t * p.o_ts + h * D + sub * 4;
+    const int64_t col = t * p.o_ts + h * DV + sub * 4;
     const bf16x4 dov = *(const bf16x4 *)((const bf16 *)p.dout + b * p.do_bs + col);
     float dot = 0.0f;
     if (OBF) {
@@ -92,49 +96,56 @@ template <int D> constexpr int kRowN = D + 8;        // [token][d] rows
 constexpr int kRowTK = BN + 8;                       // K^T rows (64 keys)
 constexpr int kRowTQ = BQ + 8;                       // Q^T / dO^T rows (32 queries)
 
-template <int D>
+template <int D, int DV>
 struct KvTile {                 // one packed tile of the dQ pass
   bf16 k[BN * kRowN<D>];        // [key][d]
-  bf16 v[BN * kRowN<D>];        // [key][d]
+  bf16 v[BN * kRowN<DV>];       // [key][d]
   bf16 kt[D * kRowTK];          // [d][key], token order vt_key
   int32_t meta[2 * BN];         // ids, positions (0 past the end)
 };
 
-template <int D>
+template <int D, int DV>
 struct QTile {                  // one packed tile of the dK/dV pass
   bf16 qn[BQ * kRowN<D>];       // [query][d]
-  bf16 don[BQ * kRowN<D>];      // [query][d]
+  bf16 don[BQ * kRowN<DV>];     // [query][d]
   bf16 qt[D * kRowTQ];          // [d][query], token order vt_key
-  bf16 dot[D * kRowTQ];         // [d][query], token order vt_key
+  bf16 dot[DV * kRowTQ];        // [d][query], token order vt_key
   float lse2[BQ];               // LSE * log2(e); +inf past the end or for a row without keys
   float dsum[BQ];               // rowsum(dO * O)
   int32_t qid[BQ];
   int32_t qpos[BQ];
 };
 
-template <int D>
+template <int D, int DV>
 __global__ __launch_bounds__(256) void bwd_pack_kv_kernel(BwdParams p) {
-  constexpr int DV = D / 8;              // 16-byte chunks of data per [key][d] row
-  constexpr int RN = kRowN<D> / 8;       // chunks per padded row
+  constexpr int KC = D / 8;              // 16-byte chunks of data per [key][d] row of K
+  constexpr int VC = DV / 8;             // ... of V
+  constexpr int RN = kRowN<D> / 8;       // chunks per padded row of K
+  constexpr int RNV = kRowN<DV> / 8;     // ... of V
   constexpr int RT = kRowTK / 8;
-  static_assert(sizeof(KvTile<D>) == bwd_kv_tile_bytes(D), "packed K/V tile size");
+  static_assert(sizeof(KvTile<D, DV>) == bwd_kv_tile_bytes(D, DV), "packed K/V tile size");
   __shared__ __attribute__((aligned(16))) bf16 ks[BN][D + 8];
   const int kt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t tile = ((int64_t)b * p.hkv + g) * p.nkt + kt;
-  KvTile<D> *out = (KvTile<D> *)((char *)p.kvpack + tile * sizeof(KvTile<D>));
+  KvTile<D, DV> *out = (KvTile<D, DV> *)((char *)p.kvpack + tile * sizeof(KvTile<D, DV>));
   const bf16 *kb = (const bf16 *)p.k + b * p.kv_bs + (int64_t)g * D;
-  const bf16 *vb = (const bf16 *)p.v + b * p.v_bs + (int64_t)g * D;
+  const bf16 *vb = (const bf16 *)p.v + b * p.v_bs + (int64_t)g * DV;
   const int64_t tok = p.kv_ts;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int u = tid; u < BN * RN; u += 256) {
     const int r = u / RN, c = u % RN;
     const int key = kt * BN + r;
-    const bool in = key < p.tk && c < DV;
+    const bool in = key < p.tk && c < KC;
     const u32x4 kv = in ? *(const u32x4 *)(kb + key * tok + c * 8) : zero;
     *(u32x4 *)(out->k + u * 8) = kv;
+    if (c < KC) *(u32x4 *)&ks[r][c * 8] = kv;
+  }
+  for (int u = tid; u < BN * RNV; u += 256) {
+    const int r = u / RNV, c = u % RNV;
+    const int key = kt * BN + r;
+    const bool in = key < p.tk && c < VC;
     *(u32x4 *)(out->v + u * 8) = in ? *(const u32x4 *)(vb + key * p.v_ts + c * 8) : zero;
-    if (c < DV) *(u32x4 *)&ks[r][c * 8] = kv;
   }
   if (tid < BN) {
     const int key = kt * BN + tid;
@@ -158,33 +169,36 @@ __global__ __launch_bounds__(256) void bwd_pack_kv_kernel(BwdParams p) {
   }
 }
 
-template <int D>
+template <int D, int DV>
 __global__ __launch_bounds__(256) void bwd_pack_q_kernel(BwdParams p) {
-  constexpr int DV = D / 8;
-  constexpr int RN = kRowN<D> / 8;
+  constexpr int QC = D / 8, GC = DV / 8;            // 16-byte data chunks per row of Q, dO
+  constexpr int RN = kRowN<D> / 8, RNG = kRowN<DV> / 8;
   constexpr int RT = kRowTQ / 8;
-  static_assert(sizeof(QTile<D>) == bwd_q_tile_bytes(D), "packed Q/dO tile size");
+  static_assert(sizeof(QTile<D, DV>) == bwd_q_tile_bytes(D, DV), "packed Q/dO tile size");
   __shared__ __attribute__((aligned(16))) bf16 qs[BQ][D + 8];
-  __shared__ __attribute__((aligned(16))) bf16 gs[BQ][D + 8];
+  __shared__ __attribute__((aligned(16))) bf16 gs[BQ][DV + 8];
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t tile = ((int64_t)b * p.hq + h) * p.tnq + qt;
-  QTile<D> *out = (QTile<D> *)((char *)p.qpack + tile * sizeof(QTile<D>));
+  QTile<D, DV> *out = (QTile<D, DV> *)((char *)p.qpack + tile * sizeof(QTile<D, DV>));
   const bf16 *qb = (const bf16 *)p.q + b * p.q_bs + (int64_t)h * D;
-  const bf16 *gb = (const bf16 *)p.dout + b * p.do_bs + (int64_t)h * D;
+  const bf16 *gb = (const bf16 *)p.dout + b * p.do_bs + (int64_t)h * DV;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int u = tid; u < BQ * RN; u += 256) {
     const int r = u / RN, c = u % RN;
     const int t = qt * BQ + r;
-    const bool in = t < p.tq && c < DV;
+    const bool in = t < p.tq && c < QC;
     const u32x4 qv = in ? *(const u32x4 *)(qb + t * p.q_ts + c * 8) : zero;
-    const u32x4 gv = in ? *(const u32x4 *)(gb + t * p.o_ts + c * 8) : zero;
     *(u32x4 *)(out->qn + u * 8) = qv;
+    if (c < QC) *(u32x4 *)&qs[r][c * 8] = qv;
+  }
+  for (int u = tid; u < BQ * RNG; u += 256) {
+    const int r = u / RNG, c = u % RNG;
+    const int t = qt * BQ + r;
+    const bool in = t < p.tq && c < GC;
+    const u32x4 gv = in ? *(const u32x4 *)(gb + t * p.o_ts + c * 8) : zero;
     *(u32x4 *)(out->don + u * 8) = gv;
-    if (c < DV) {
-      *(u32x4 *)&qs[r][c * 8] = qv;
-      *(u32x4 *)&gs[r][c * 8] = gv;
-    }
+    if (c < GC) *(u32x4 *)&gs[r][c * 8] = gv;
   }
   if (tid < BQ) {
     const int t = qt * BQ + tid;
@@ -200,16 +214,26 @@ __global__ __launch_bounds__(256) void bwd_pack_q_kernel(BwdParams p) {
   const uint16_t *gsu = (const uint16_t *)&gs[0][0];
   for (int u = tid; u < D * RT; u += 256) {
     const int d = u / RT, c = u % RT;
-    u32x4 oq = zero, og = zero;
+    u32x4 oq = zero;
     if (c < BQ / 8) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t0 = vt_key(c * 8 + 2 * j), t1 = vt_key(c * 8 + 2 * j + 1);
         oq[j] = (uint32_t)qsu[t0 * (D + 8) + d] | ((uint32_t)qsu[t1 * (D + 8) + d] << 16);
-        og[j] = (uint32_t)gsu[t0 * (D + 8) + d] | ((uint32_t)gsu[t1 * (D + 8) + d] << 16);
       }
     }
     *(u32x4 *)(out->qt + u * 8) = oq;
+  }
+  for (int u = tid; u < DV * RT; u += 256) {
+    const int d = u / RT, c = u % RT;
+    u32x4 og = zero;
+    if (c < BQ / 8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t0 = vt_key(c * 8 + 2 * j), t1 = vt_key(c * 8 + 2 * j + 1);
+        og[j] = (uint32_t)gsu[t0 * (DV + 8) + d] | ((uint32_t)gsu[t1 * (DV + 8) + d] << 16);
+      }
+    }
     *(u32x4 *)(out->dot + u * 8) = og;
   }
 }
@@ -244,21 +268,23 @@ __device__ __forceinline__ void mask_bounds(const MaskParams &m, int &lo, int &h
 
 // ----------------------------------------------------------------------------- dQ pass
 
-template <int D, int NT, bool OUT_BF16>
+template <int D, int DV, int NT, bool OUT_BF16>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 bwd_dq_kernel(BwdParams p) {
   constexpr int NH = kWaves / NT;
   constexpr int BM = 32 * NT;
-  constexpr int DC = D / 16;
+  constexpr int DC = D / 16;               // MFMA steps of S^T (over Q/K's head dim)
+  constexpr int DCV = DV / 16;             // MFMA steps of dP^T (over V/dO's head dim)
   constexpr int DB = D / 32;
-  constexpr int TILE = (int)sizeof(KvTile<D>);
-  constexpr int BLK = (int)offsetof(KvTile<D>, meta);   // bytes of the three bf16 blocks
+  typedef KvTile<D, DV> Tile;
+  constexpr int TILE = (int)sizeof(Tile);
+  constexpr int BLK = (int)offsetof(Tile, meta);   // bytes of the three bf16 blocks
   static_assert(BLK % 1024 == 0, "tile blocks are loaded 1 KB per wave instruction");
   constexpr int CHUNKS = BLK / 1024;
   constexpr int kStageBytes = kWaves * 32 * 68 * 4;
   constexpr int kSmemBytes = 2 * TILE > kStageBytes ? 2 * TILE : kStageBytes;
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  KvTile<D> &t0 = *reinterpret_cast<KvTile<D> *>(smem);
+  Tile &t0 = *reinterpret_cast<Tile *>(smem);
   float(*stage)[32][68] = reinterpret_cast<float(*)[32][68]>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -286,7 +312,7 @@ bwd_dq_kernel(BwdParams p) {
   const const_list_t lst = (const_list_t)(p.list + row * p.nkt);
   const char *pack = (const char *)p.kvpack + ((int64_t)b * p.hkv + g) * p.nkt * TILE;
 
-  auto issue = [&](KvTile<D> &dst, int kt) __attribute__((always_inline)) {
+  auto issue = [&](Tile &dst, int kt) __attribute__((always_inline)) {
     const char *src = pack + (int64_t)kt * TILE;
 #pragma unroll
     for (int i = 0; i < (CHUNKS + kWaves - 1) / kWaves; ++i) {
@@ -304,17 +330,18 @@ bwd_dq_kernel(BwdParams p) {
 
   // B operands: Q (for S^T = K Q^T) and dO (for dP^T = V dO^T), 8 head_dim
   // values per step.
-  bf16x8 qf[DC], gf[DC];
+  bf16x8 qf[DC], gf[DCV];
   {
     const bf16 *qrow = (const bf16 *)p.q + b * p.q_bs + (int64_t)tq * p.q_ts + (int64_t)h * D + 8 * half;
-    const bf16 *grow = (const bf16 *)p.dout + b * p.do_bs + (int64_t)tq * p.o_ts + (int64_t)h * D +
+    const bf16 *grow = (const bf16 *)p.dout + b * p.do_bs + (int64_t)tq * p.o_ts + (int64_t)h * DV +
                        8 * half;
+    const bool ld = qvalid && n > 0;
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const bool ld = qvalid && n > 0;
+    for (int c = 0; c < DC; ++c)
       qf[c] = ld ? *(const bf16x8 *)(qrow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int c = 0; c < DCV; ++c)
       gf[c] = ld ? *(const bf16x8 *)(grow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
   }
   const int64_t rowidx = ((int64_t)b * p.tq + tq) * p.hq + h;
   const float l2 = qvalid ? p.lse2[rowidx] : INFINITY;
@@ -341,14 +368,14 @@ bwd_dq_kernel(BwdParams p) {
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
   // One 32-key block of S^T (or dP^T): A operand rows kb*32 + col of an
-  // [key][d] block, B operand the lane's query row.
-  auto scores = [&](f32x16 &s, const bf16 *blk, const bf16x8 (&bop)[DC])
-      __attribute__((always_inline)) {
-    const bf16 *arow = blk + col * kRowN<D> + 8 * half;
+  // [key][d] block of NC 16-element steps, B operand the lane's query row.
+  auto scores = [&](f32x16 &s, const bf16 *blk, const auto &bop) __attribute__((always_inline)) {
+    constexpr int NC = sizeof(bop) / sizeof(bop[0]);
+    const bf16 *arow = blk + col * (16 * NC + 8) + 8 * half;   // rows of kRowN elements
     const f32x16 zero16 = {};
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)arow, bop[0], zero16, 0, 0, 0);
 #pragma unroll
-    for (int c = 1; c < DC; ++c)
+    for (int c = 1; c < NC; ++c)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(arow + 16 * c), bop[c], s, 0,
                                                   0, 0);
   };
@@ -356,12 +383,12 @@ bwd_dq_kernel(BwdParams p) {
   // One tile, one 32-key block at a time: S^T and dP^T, the mask (boundary
   // tiles only), dS^T = P^T (dP^T - D) with P^T = 2^(s c2 - LSE log2 e) packed
   // to bf16 B operands, then dQ^T += K^T dS^T over the block's two 16-key chunks.
-  auto compute = [&](const KvTile<D> &tl, bool masked) __attribute__((always_inline)) {
+  auto compute = [&](const Tile &tl, bool masked) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s, dp;
       scores(s, tl.k + kb * 32 * kRowN<D>, qf);
-      scores(dp, tl.v + kb * 32 * kRowN<D>, gf);
+      scores(dp, tl.v + kb * 32 * kRowN<DV>, gf);
       if (masked) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
@@ -395,9 +422,7 @@ bwd_dq_kernel(BwdParams p) {
 
   // Double-buffered loop with one body: tile it computes from buffer it & 1
   // while tile it + 1 streams into the other.
-  auto buffer = [&](int i) -> KvTile<D> & {
-    return *reinterpret_cast<KvTile<D> *>(smem + i * TILE);
-  };
+  auto buffer = [&](int i) -> Tile & { return *reinterpret_cast<Tile *>(smem + i * TILE); };
   if (n > 0) {
     issue(t0, entry_tile(0));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -448,22 +473,25 @@ bwd_dq_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------------------- dK/dV pass
 
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(64 * kBwdKvWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+template <int D, int DV, bool OUT_BF16>
+__global__ __launch_bounds__(64 * bwd_kv_waves(D))
+__attribute__((amdgpu_waves_per_eu(bwd_kv_waves(D) / 4, bwd_kv_waves(D) / 4))) void
 bwd_dkdv_kernel(BwdParams p) {
-  constexpr int W = kBwdKvWaves;
-  constexpr int DC = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int TILE = (int)sizeof(QTile<D>);
-  constexpr int BLK = (int)offsetof(QTile<D>, lse2);    // bytes of the four bf16 blocks
+  constexpr int W = bwd_kv_waves(D);
+  constexpr int KT = bwd_kv_tile(D);       // keys per workgroup
+  constexpr int DC = D / 16, DCV = DV / 16;
+  constexpr int DB = D / 32, DBV = DV / 32;
+  typedef QTile<D, DV> Tile;
+  constexpr int TILE = (int)sizeof(Tile);
+  constexpr int BLK = (int)offsetof(Tile, lse2);    // bytes of the four bf16 blocks
   static_assert(BLK % 1024 == 0, "tile blocks are loaded 1 KB per wave instruction");
   constexpr int CHUNKS = BLK / 1024;
   constexpr int SROW = 68;        // staging row: 64 fp32 columns of one key, padded
   constexpr int kStageBytes = W * 32 * SROW * 4;
   constexpr int kTileBytes = 2 * TILE > kStageBytes ? 2 * TILE : kStageBytes;
-  constexpr int kVBytes = W * 32 * kRowN<D> * 2;   // the workgroup's V rows, [key][d] padded
+  constexpr int kVBytes = W * 32 * kRowN<DV> * 2;   // the workgroup's V rows, [key][d] padded
   __shared__ __attribute__((aligned(16))) char smem[kTileBytes + kVBytes];
-  QTile<D> &t0 = *reinterpret_cast<QTile<D> *>(smem);
+  Tile &t0 = *reinterpret_cast<Tile *>(smem);
   float(*stage)[32][SROW] = reinterpret_cast<float(*)[32][SROW]>(smem);
   bf16 *vrows = reinterpret_cast<bf16 *>(smem + kTileBytes);
 
@@ -477,7 +505,7 @@ bwd_dkdv_kernel(BwdParams p) {
   const int kt = (int)(item % p.tnk);
   const int g = (int)((item / p.tnk) % p.hkv);
   const int b = (int)(item / ((int64_t)p.tnk * p.hkv));
-  const int key = kt * kBwdKvTile + wave * 32 + col;
+  const int key = kt * KT + wave * 32 + col;
   const bool kvalid = key < p.tk;
 
   const int64_t row = (int64_t)b * p.tnk + kt;
@@ -500,7 +528,7 @@ bwd_dkdv_kernel(BwdParams p) {
     const uint32_t e = lst[it % nq];
     return (e >> 31) != 0 || (ragged_q && (int)(e & 0x7fffffffu) == p.tnq - 1) || !kvalid;
   };
-  auto issue = [&](QTile<D> &dst, int64_t tile) __attribute__((always_inline)) {
+  auto issue = [&](Tile &dst, int64_t tile) __attribute__((always_inline)) {
     const char *src = (const char *)p.qpack + tile * TILE;
 #pragma unroll
     for (int i = 0; i < (CHUNKS + W - 1) / W; ++i) {
@@ -521,19 +549,20 @@ bwd_dkdv_kernel(BwdParams p) {
   // and are read back per visit, which keeps the persistent register state at
   // K plus the two accumulators.
   bf16x8 kf[DC];
-  bf16 *const vmine = vrows + (wave * 32 + col) * kRowN<D> + 8 * half;
+  bf16 *const vmine = vrows + (wave * 32 + col) * kRowN<DV> + 8 * half;
   {
     const bf16 *krow = (const bf16 *)p.k + b * p.kv_bs + (int64_t)key * p.kv_ts + (int64_t)g * D +
                        8 * half;
-    const bf16 *vrow = (const bf16 *)p.v + b * p.v_bs + (int64_t)key * p.v_ts + (int64_t)g * D +
+    const bf16 *vrow = (const bf16 *)p.v + b * p.v_bs + (int64_t)key * p.v_ts + (int64_t)g * DV +
                        8 * half;
     const bool ld = kvalid && n > 0;
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
+    for (int c = 0; c < DC; ++c)
       kf[c] = ld ? *(const bf16x8 *)(krow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int c = 0; c < DCV; ++c)
       *(bf16x8 *)(vmine + 16 * c) =
           ld ? *(const bf16x8 *)(vrow + 16 * c) : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
   }
   KeyMask km;
   {
@@ -544,33 +573,44 @@ bwd_dkdv_kernel(BwdParams p) {
   }
   const float c2 = p.scale_log2;
 
-  f32x16 dk[DB], dv[DB];
+  f32x16 dk[DB], dv[DBV];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[db][r] = 0.0f;
-      dv[db][r] = 0.0f;
-    }
+    for (int r = 0; r < 16; ++r) dk[db][r] = 0.0f;
+#pragma unroll
+  for (int db = 0; db < DBV; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[db][r] = 0.0f;
 
-  auto compute = [&](const QTile<D> &tl, bool masked) __attribute__((always_inline)) {
+  auto compute = [&](const Tile &tl, bool masked) __attribute__((always_inline)) {
     // S = Q K^T and dP = dO V^T for the 32 queries of the tile: lane = key,
     // element r of the accumulator = query row 8(r/4) + 4 half + r%4.
     f32x16 s = {}, dp = {};
     {
       const bf16 *qa = tl.qn + col * kRowN<D> + 8 * half;
-      const bf16 *ga = tl.don + col * kRowN<D> + 8 * half;
+      const bf16 *ga = tl.don + col * kRowN<DV> + 8 * half;
+      if constexpr (D == DV) {
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(qa + 16 * c), kf[c], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(ga + 16 * c),
-                                                     *(const bf16x8 *)(vmine + 16 * c), dp, 0, 0, 0);
-      }
-      // operand reads three at a time, each group followed by its two products
+        for (int c = 0; c < DC; ++c) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(qa + 16 * c), kf[c], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(ga + 16 * c),
+                                                       *(const bf16x8 *)(vmine + 16 * c), dp, 0, 0, 0);
+        }
+        // operand reads three at a time, each group followed by its two products
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        for (int c = 0; c < DC; ++c) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(qa + 16 * c), kf[c], s, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < DCV; ++c)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(ga + 16 * c),
+                                                       *(const bf16x8 *)(vmine + 16 * c), dp, 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -604,20 +644,38 @@ bwd_dkdv_kernel(BwdParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end).
+    if constexpr (D == DV) {
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch)
+      for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int off = (db * 32 + col) * kRowTQ + 16 * ch + 8 * half;
-        const bf16x8 ag = *(const bf16x8 *)(tl.dot + off);
-        const bf16x8 aq = *(const bf16x8 *)(tl.qt + off);
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[ch], dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, df[ch], dk[db], 0, 0, 0);
+        for (int db = 0; db < DB; ++db) {
+          const int off = (db * 32 + col) * kRowTQ + 16 * ch + 8 * half;
+          const bf16x8 ag = *(const bf16x8 *)(tl.dot + off);
+          const bf16x8 aq = *(const bf16x8 *)(tl.qt + off);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[ch], dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, df[ch], dk[db], 0, 0, 0);
+        }
+#pragma unroll
+      for (int i = 0; i < 2 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
+    } else {
 #pragma unroll
-    for (int i = 0; i < 2 * DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll
+        for (int db = 0; db < DBV; ++db) {
+          const int off = (db * 32 + col) * kRowTQ + 16 * ch + 8 * half;
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(tl.dot + off), pf[ch],
+                                                           dv[db], 0, 0, 0);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int off = (db * 32 + col) * kRowTQ + 16 * ch + 8 * half;
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(tl.qt + off), df[ch],
+                                                           dk[db], 0, 0, 0);
+        }
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -625,9 +683,7 @@ bwd_dkdv_kernel(BwdParams p) {
   // Double-buffered loop with one body: visit it computes from buffer it & 1
   // while visit it + 1 streams into the other (a single copy of the body keeps
   // the accumulators in one set of registers).
-  auto buffer = [&](int i) -> QTile<D> & {
-    return *reinterpret_cast<QTile<D> *>(smem + i * TILE);
-  };
+  auto buffer = [&](int i) -> Tile & { return *reinterpret_cast<Tile *>(smem + i * TILE); };
   if (n > 0) {
     issue(t0, visit_tile(0));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -645,12 +701,13 @@ bwd_dkdv_kernel(BwdParams p) {
   // dK = scale * (dK^T)^T and dV = (dV^T)^T through LDS: each wave stages its
   // 32 keys x 64 columns at a time, then writes 4 whole 256-byte row pieces
   // per pass, 16 bytes per lane.
-  const int key0 = kt * kBwdKvTile + wave * 32;
+  const int key0 = kt * KT + wave * 32;
   const int rsub = lane >> 4, c4 = (lane & 15) * 4;
-  auto store = [&](const f32x16 (&acc)[DB], float mul, void *dst, int64_t bs, int64_t ts)
+  auto store = [&](const auto &acc, float mul, void *dst, int64_t bs, int64_t ts, int width)
       __attribute__((always_inline)) {
+    constexpr int NB = sizeof(acc) / sizeof(acc[0]);   // 32-column blocks
 #pragma unroll
-    for (int hd = 0; hd < DB / 2; ++hd) {
+    for (int hd = 0; hd < NB / 2; ++hd) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -666,7 +723,7 @@ bwd_dkdv_kernel(BwdParams p) {
         const int t = key0 + kr;
         const f32x4 val = *(const f32x4 *)&stage[wave][kr][c4];
         if (t < p.tk) {
-          const int64_t rel = b * bs + (int64_t)t * ts + (int64_t)g * D + 64 * hd + c4;
+          const int64_t rel = b * bs + (int64_t)t * ts + (int64_t)g * width + 64 * hd + c4;
           if (OUT_BF16) {
             bf16x4 hv;
 #pragma unroll
@@ -680,56 +737,55 @@ bwd_dkdv_kernel(BwdParams p) {
     }
   };
   __syncthreads();  // the staging reuses the tile buffers
-  store(dk, p.scale, p.dk, p.dkv_bs, p.kv_ts);
-  store(dv, 1.0f, p.dv, p.v_bs, p.v_ts);
+  store(dk, p.scale, p.dk, p.dkv_bs, p.kv_ts, D);
+  store(dv, 1.0f, p.dv, p.v_bs, p.v_ts, DV);
 }
 
 // ----------------------------------------------------------------------------- launchers
 
-template <int D, int NT>
+template <int D, int DV, int NT>
 hipError_t launch_dq_nt(const BwdParams &p, bool out_bf16, hipStream_t stream) {
   constexpr int NH = kWaves / NT;
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.nqt * (p.group / NH);
   if (nwork == 0) return hipSuccess;
   const int64_t grid = (nwork + 7) / 8 * 8;
   if (out_bf16)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NT, true>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
-                       stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, DV, NT, true>), dim3((unsigned)grid), dim3(64 * kWaves),
+                       0, stream, p);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NT, false>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
-                       stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, DV, NT, false>), dim3((unsigned)grid), dim3(64 * kWaves),
+                       0, stream, p);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int DV>
 hipError_t launch_dq_d(const BwdParams &p, int32_t nt, bool out_bf16, hipStream_t stream) {
   switch (nt) {
-    case 1: return launch_dq_nt<D, 1>(p, out_bf16, stream);
-    case 2: return launch_dq_nt<D, 2>(p, out_bf16, stream);
-    case 4: return launch_dq_nt<D, 4>(p, out_bf16, stream);
-    case 8: return launch_dq_nt<D, 8>(p, out_bf16, stream);
+    case 1: return launch_dq_nt<D, DV, 1>(p, out_bf16, stream);
+    case 2: return launch_dq_nt<D, DV, 2>(p, out_bf16, stream);
+    case 4: return launch_dq_nt<D, DV, 4>(p, out_bf16, stream);
+    case 8: return launch_dq_nt<D, DV, 8>(p, out_bf16, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int D>
+template <int D, int DV>
 hipError_t launch_dkdv_d(const BwdParams &p, bool out_bf16, hipStream_t stream) {
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.tnk;
   if (nwork == 0) return hipSuccess;
   const int64_t grid = (nwork + 7) / 8 * 8;
+  const dim3 block(64 * bwd_kv_waves(D));
   if (out_bf16)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)grid), dim3(64 * kBwdKvWaves), 0,
-                       stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DV, true>), dim3((unsigned)grid), block, 0, stream, p);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)grid), dim3(64 * kBwdKvWaves), 0,
-                       stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DV, false>), dim3((unsigned)grid), block, 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 BwdLayout bwd_workspace_layout(int32_t batch, int32_t tq, int32_t hq, int32_t hkv, int32_t d,
-                               int32_t nqt, int32_t nkt, int32_t tnq, int32_t tnk) {
+                               int32_t dv, int32_t nqt, int32_t nkt, int32_t tnq, int32_t tnk) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   BwdLayout w;
   size_t off = 0;
@@ -746,23 +802,24 @@ BwdLayout bwd_workspace_layout(int32_t batch, int32_t tq, int32_t hq, int32_t hk
   w.tlist = off;  off = up(off + B * tnk * tnq * sizeof(uint32_t));
   w.lse2 = off;   off = up(off + B * tq * hq * sizeof(float));
   w.dsum = off;   off = up(off + B * tq * hq * sizeof(float));
-  w.kvpack = off; off = up(off + B * hkv * nkt * bwd_kv_tile_bytes(d));
-  w.qpack = off;  off = up(off + B * hq * tnq * bwd_q_tile_bytes(d));
+  w.kvpack = off; off = up(off + B * hkv * nkt * bwd_kv_tile_bytes(d, dv));
+  w.qpack = off;  off = up(off + B * hq * tnq * bwd_q_tile_bytes(d, dv));
   w.total = off;
   return w;
 }
 
-hipError_t launch_bwd_prep(const BwdParams &p, int32_t head_dim, bool o_bf16, hipStream_t stream) {
+hipError_t launch_bwd_prep(const BwdParams &p, int32_t v_head_dim, bool o_bf16,
+                           hipStream_t stream) {
   const int64_t rows = (int64_t)p.batch * p.tq * p.hq;
   if (rows == 0) return hipSuccess;
-  const int64_t rpb = 256 / (head_dim / 4);
+  const int64_t rpb = 256 / (v_head_dim / 4);
   int64_t blocks = (rows + rpb - 1) / rpb;
   if (blocks > 16384) blocks = 16384;
   const dim3 grid((unsigned)blocks);
-  if (head_dim == 128) {
+  if (v_head_dim == 128) {
     if (o_bf16) hipLaunchKernelGGL((bwd_prep_kernel<128, true>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((bwd_prep_kernel<128, false>), grid, dim3(256), 0, stream, p);
-  } else if (head_dim == 64) {
+  } else if (v_head_dim == 64) {
     if (o_bf16) hipLaunchKernelGGL((bwd_prep_kernel<64, true>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((bwd_prep_kernel<64, false>), grid, dim3(256), 0, stream, p);
   } else {
@@ -771,35 +828,42 @@ hipError_t launch_bwd_prep(const BwdParams &p, int32_t head_dim, bool o_bf16, hi
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_pack(const BwdParams &p, int32_t head_dim, hipStream_t stream) {
-  if (p.batch == 0) return hipSuccess;
-  if (head_dim != 128 && head_dim != 64) return hipErrorInvalidValue;
+template <int D, int DV>
+hipError_t pack_dd(const BwdParams &p, hipStream_t stream) {
   if (p.nkt > 0) {
-    const dim3 grid(p.nkt, p.hkv, p.batch);
-    if (head_dim == 128) hipLaunchKernelGGL(bwd_pack_kv_kernel<128>, grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(bwd_pack_kv_kernel<64>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_pack_kv_kernel<D, DV>), dim3(p.nkt, p.hkv, p.batch), dim3(256), 0,
+                       stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.tnq > 0) {
-    const dim3 grid(p.tnq, p.hq, p.batch);
-    if (head_dim == 128) hipLaunchKernelGGL(bwd_pack_q_kernel<128>, grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(bwd_pack_q_kernel<64>, grid, dim3(256), 0, stream, p);
-  }
+  if (p.tnq > 0)
+    hipLaunchKernelGGL((bwd_pack_q_kernel<D, DV>), dim3(p.tnq, p.hq, p.batch), dim3(256), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const BwdParams &p, int32_t head_dim, int32_t nt, bool out_bf16,
-                         hipStream_t stream) {
-  if (head_dim == 128) return launch_dq_d<128>(p, nt, out_bf16, stream);
-  if (head_dim == 64) return launch_dq_d<64>(p, nt, out_bf16, stream);
+hipError_t launch_bwd_pack(const BwdParams &p, int32_t head_dim, int32_t v_head_dim,
+                           hipStream_t stream) {
+  if (p.batch == 0) return hipSuccess;
+  if (head_dim == 128 && v_head_dim == 128) return pack_dd<128, 128>(p, stream);
+  if (head_dim == 64 && v_head_dim == 64) return pack_dd<64, 64>(p, stream);
+  if (head_dim == 192 && v_head_dim == 128) return pack_dd<192, 128>(p, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dkdv(const BwdParams &p, int32_t head_dim, bool out_bf16,
-                           hipStream_t stream) {
-  if (head_dim == 128) return launch_dkdv_d<128>(p, out_bf16, stream);
-  if (head_dim == 64) return launch_dkdv_d<64>(p, out_bf16, stream);
+hipError_t launch_bwd_dq(const BwdParams &p, int32_t head_dim, int32_t v_head_dim, int32_t nt,
+                         bool out_bf16, hipStream_t stream) {
+  if (head_dim == 128 && v_head_dim == 128) return launch_dq_d<128, 128>(p, nt, out_bf16, stream);
+  if (head_dim == 64 && v_head_dim == 64) return launch_dq_d<64, 64>(p, nt, out_bf16, stream);
+  if (head_dim == 192 && v_head_dim == 128) return launch_dq_d<192, 128>(p, nt, out_bf16, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dkdv(const BwdParams &p, int32_t head_dim, int32_t v_head_dim,
+                           bool out_bf16, hipStream_t stream) {
+  if (head_dim == 128 && v_head_dim == 128) return launch_dkdv_d<128, 128>(p, out_bf16, stream);
+  if (head_dim == 64 && v_head_dim == 64) return launch_dkdv_d<64, 64>(p, out_bf16, stream);
+  if (head_dim == 192 && v_head_dim == 128) return launch_dkdv_d<192, 128>(p, out_bf16, stream);
   return hipErrorInvalidValue;
 }
 

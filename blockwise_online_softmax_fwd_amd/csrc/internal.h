@@ -124,18 +124,24 @@ hipError_t launch_reorder(const void *src, void *dst, int32_t batch, int32_t seq
 // ----------------------------------------------------------------------------- backward
 
 constexpr int kBwdQTile = 32;    // queries per packed tile of the dK/dV pass
-constexpr int kBwdKvWaves = 8;   // dK/dV workgroup: 8 waves of 32 keys
-constexpr int kBwdKvTile = 32 * kBwdKvWaves;
+// dK/dV workgroup: waves of 32 keys each; 8 (two per SIMD) for head dims up
+// to 128, 4 (one per SIMD, whose registers hold the 192-wide K rows and both
+// accumulators) for the MLA head dims.
+constexpr int bwd_kv_waves(int d) { return d == 192 ? 4 : 8; }
+constexpr int bwd_kv_tile(int d) { return 32 * bwd_kv_waves(d); }
 
 // Bytes of one packed K/V tile of the dQ pass (K, V and K^T blocks, ids and
 // positions) and of one packed Q/dO tile of the dK/dV pass (Q, dO, Q^T, dO^T
-// blocks, then LSE*log2(e), rowsum(dO*O), ids and positions).  Every bf16 row
-// carries 8 elements of padding.
-constexpr size_t bwd_kv_tile_bytes(int d) {
-  return 2 * (size_t)kBnBf16 * (d + 8) * 2 + (size_t)d * (kBnBf16 + 8) * 2 + 2 * kBnBf16 * 4;
+// blocks, then LSE*log2(e), rowsum(dO*O), ids and positions).  d is the head
+// dim of Q and K, dv that of V, O and dO.  Every bf16 row carries 8 elements
+// of padding.
+constexpr size_t bwd_kv_tile_bytes(int d, int dv) {
+  return (size_t)kBnBf16 * (d + 8) * 2 + (size_t)kBnBf16 * (dv + 8) * 2 +
+         (size_t)d * (kBnBf16 + 8) * 2 + 2 * kBnBf16 * 4;
 }
-constexpr size_t bwd_q_tile_bytes(int d) {
-  return 2 * (size_t)kBwdQTile * (d + 8) * 2 + 2 * (size_t)d * (kBwdQTile + 8) * 2 + 4 * kBwdQTile * 4;
+constexpr size_t bwd_q_tile_bytes(int d, int dv) {
+  return (size_t)kBwdQTile * (d + 8) * 2 + (size_t)kBwdQTile * (dv + 8) * 2 +
+         (size_t)(d + dv) * (kBwdQTile + 8) * 2 + 4 * kBwdQTile * 4;
 }
 
 struct BwdLayout {
@@ -144,7 +150,7 @@ struct BwdLayout {
   size_t lse2, dsum, kvpack, qpack, total;
 };
 BwdLayout bwd_workspace_layout(int32_t batch, int32_t tq, int32_t hq, int32_t hkv, int32_t d,
-                               int32_t nqt, int32_t nkt, int32_t tnq, int32_t tnk);
+                               int32_t dv, int32_t nqt, int32_t nkt, int32_t tnq, int32_t tnk);
 
 struct BwdParams {
   const void *q, *k, *v, *o, *dout;
@@ -154,7 +160,7 @@ struct BwdParams {
   float *lse2, *dsum;                  // [B, Tq, Hq], dense
   const uint32_t *list;                // dQ pass: per query tile, key tiles (| partial bit)
   const int32_t *count;
-  const uint32_t *tlist;               // dK/dV pass: per 128-key tile, 32-query tiles
+  const uint32_t *tlist;               // dK/dV pass: per key tile, 32-query tiles
   const int32_t *tcount;
   void *kvpack, *qpack;
   int64_t q_bs, kv_bs, o_bs, do_bs, lse_bs, qm_bs, km_bs, dq_bs, dkv_bs;
@@ -162,19 +168,22 @@ struct BwdParams {
   int64_t v_bs, v_ts;                  // V's strides, also dv's
   int32_t batch, tq, tk, hq, hkv, group;
   int32_t nqt, nkt;                    // dQ schedule tiles
-  int32_t tnk, tnq;                    // dK/dV schedule: key tiles (128), query tiles (32)
+  int32_t tnk, tnq;                    // dK/dV schedule: key tiles, 32-query tiles
   float scale, scale_log2;
   MaskParams mask;
 };
-// rowsum(dO * O) and LSE * log2(e) (+inf for a row without visible key).
-hipError_t launch_bwd_prep(const BwdParams &p, int32_t head_dim, bool o_bf16, hipStream_t stream);
-// Packed tiles of both passes.
-hipError_t launch_bwd_pack(const BwdParams &p, int32_t head_dim, hipStream_t stream);
-// dQ pass (workgroups shaped like the forward's: nt token sub-tiles) and dK/dV pass.
-hipError_t launch_bwd_dq(const BwdParams &p, int32_t head_dim, int32_t nt, bool out_bf16,
-                         hipStream_t stream);
-hipError_t launch_bwd_dkdv(const BwdParams &p, int32_t head_dim, bool out_bf16,
+// rowsum(dO * O) and LSE * log2(e) (+inf for a row without visible key);
+// v_head_dim is the width of O and dO.
+hipError_t launch_bwd_prep(const BwdParams &p, int32_t v_head_dim, bool o_bf16,
                            hipStream_t stream);
+// Packed tiles of both passes.
+hipError_t launch_bwd_pack(const BwdParams &p, int32_t head_dim, int32_t v_head_dim,
+                           hipStream_t stream);
+// dQ pass (workgroups shaped like the forward's: nt token sub-tiles) and dK/dV pass.
+hipError_t launch_bwd_dq(const BwdParams &p, int32_t head_dim, int32_t v_head_dim, int32_t nt,
+                         bool out_bf16, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdParams &p, int32_t head_dim, int32_t v_head_dim,
+                           bool out_bf16, hipStream_t stream);
 
 // Heads per bf16 workgroup for a GQA group size, and the token sub-tiles.
 inline int32_t bf16_heads_per_wg(int32_t group) {

@@ -322,10 +322,11 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
              dk=None, dv=None, workspace=None):
     """Gradients ``(dq, dk, dv)`` of the masked GQA attention forward.
 
-    q ``[B,Tq,Hq,D]``, k/v ``[B,Tk,Hkv,D]`` bf16; ``o``/``lse`` the forward's
-    outputs for the same inputs and mask (o bf16 or fp32); ``dout`` bf16 with
-    o's shape and strides.  Gradients are ``grad_dtype`` (float32 or
-    bfloat16) with the shapes and strides of q and k; given buffers are
+    q ``[B,Tq,Hq,D]``, k ``[B,Tk,Hkv,D]``, v ``[B,Tk,Hkv,Dv]`` bf16 (Dv = D, or
+    the MLA pair D = 192, Dv = 128); ``o``/``lse`` the forward's outputs for
+    the same inputs and mask (o ``[B,Tq,Hq,Dv]``, bf16 or fp32); ``dout`` bf16
+    with o's shape and strides.  Gradients are ``grad_dtype`` (float32 or
+    bfloat16) with the shapes and strides of q, k and v; given buffers are
     overwritten.
     """
     _require_gpu(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, o, lse, dout)
@@ -333,10 +334,11 @@ def attn_bwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
         raise TypeError("the backward needs bfloat16 q, k and v")
     if dout.dtype != torch.bfloat16:
         raise TypeError("dout must be bfloat16")
-    if k.shape != v.shape:
-        raise ValueError("k and v must have the same shape (the backward needs Dv == D)")
-    if o.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != tuple(q.shape[:3]):
-        raise ValueError("o and dout must have q's shape, lse [B,Tq,Hq]")
+    if k.shape[:3] != v.shape[:3]:
+        raise ValueError("k and v must have the same batch, length and heads")
+    o_shape = tuple(q.shape[:3]) + (v.shape[3],)
+    if tuple(o.shape) != o_shape or tuple(dout.shape) != o_shape or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("o and dout must be [B,Tq,Hq,Dv], lse [B,Tq,Hq]")
     if _bt_strides(dout) != _bt_strides(o):
         raise ValueError("dout must have o's batch and token strides")
     _check_meta(q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos)

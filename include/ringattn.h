@@ -91,7 +91,7 @@ enum { RA_TILE_SKIP = 0, RA_TILE_PARTIAL = 1, RA_TILE_FULL = 2 };
  * MLA head dimensions ([TUT] "Next steps", single-GPU attention): v and o may have their own
  * head dim Dv (v [B,Tk,Hkv,Dv], o [B,Tq,Hq,Dv]); the scale stays the caller's
  * (head_dim^-1/2 of q and k in [TUT] s3).  Supported (head_dim, Dv) pairs: (64, 64),
- * (128, 128) and, for the bf16 forward, (192, 128).
+ * (128, 128) and, in bf16 (forward and backward), (192, 128).
  * The (batch, token) rows of each tensor must nest without overlap: with
  * L = H*D, either token stride >= L and batch stride >= (T-1)*token stride + L,
  * or batch stride >= L and token stride >= (B-1)*batch stride + L.
@@ -268,10 +268,11 @@ ra_status ra_attn_merge(const ra_merge_desc *desc, const void *o_a, const float 
  * boundary tiles are masked, in both passes: dq over the forward's tile lists,
  * dk/dv over lists built with the roles of keys and queries swapped.
  *
- * Inputs:  q, k, v bf16 (qkv_dtype must be RA_BF16); o [B,Tq,Hq,D] out_dtype
+ * Inputs:  q, k, v bf16 (qkv_dtype must be RA_BF16); o [B,Tq,Hq,Dv] out_dtype
  *          with o_batch_stride; lse [B,Tq,Hq] fp32 with lse_batch_stride;
- *          dout [B,Tq,Hq,D] bf16 with o_batch_stride (in its own elements).
- * Outputs: dq like q (q_batch_stride), dk and dv like k (kv_batch_stride), all
+ *          dout [B,Tq,Hq,Dv] bf16 with o_batch_stride (in its own elements).
+ * Outputs: dq like q (q_batch_stride), dk like k (kv_batch_stride), dv like v
+ *          (v's strides, [B,Tk,Hkv,Dv]), all
  *          of dtype grad_dtype (RA_BF16 or RA_F32), fully overwritten: rows no
  *          visible pair reaches (padding, masked keys) get 0.  Each key's
  *          dk/dv is accumulated in registers over its whole query-head group
@@ -283,8 +284,9 @@ ra_status ra_attn_merge(const ra_merge_desc *desc, const void *o_a, const float 
  * ra_attn_bwd_workspace_size() bytes, 256-byte aligned, owned by the caller,
  * overwritten (both passes' tile lists, rowsum(dout*o), and packed copies of
  * q/dout and k/v tiles in the layouts the kernels read); calls that share a
- * workspace must be ordered on one stream.  Supported: D in {64, 128}, any
- * GQA group, Tq up to 2^20 and Tk up to 2^21 tokens per call.
+ * workspace must be ordered on one stream.  Supported: (head_dim, Dv) of
+ * (64, 64), (128, 128) or MLA's (192, 128), any GQA group, Tq up to 2^20 and
+ * Tk up to 2^21 tokens per call.
  */
 ra_status ra_attn_bwd_workspace_size(const ra_attn_desc *desc, size_t *bytes);
 

@@ -353,6 +353,20 @@ def test_bwd_packed_gradients_are_not_aliases(lib):
                 dv=_p(base + 512 * 4)) == ALIAS
 
 
+def test_bwd_mla_alias_spans(lib):
+    """With MLA head dims V, O, dO and dV rows are 128 wide per head: separate
+    buffers pass, and dk and dv side by side in one packed K/V gradient buffer
+    (rows of 2 x (192 + 128) elements) pass unless they overlap."""
+    d = _desc(head_dim=192, v_head_dim=128, kv_len=300)
+    assert _bwd(lib, d, ws=None) == WS
+    row = 2 * (192 + 128)
+    dp = _desc(head_dim=192, v_head_dim=128, kv_len=300, kv_token_stride=row,
+               kv_batch_stride=300 * row, v_token_stride=row, v_batch_stride=300 * row)
+    base = 12 << 32
+    assert _bwd(lib, dp, ws=None, dk=_p(base), dv=_p(base + 2 * 192 * 4)) == WS
+    assert _bwd(lib, dp, ws=None, dk=_p(base), dv=_p(base + 2 * 192 * 4 - 16)) == ALIAS
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=192, v_head_dim=128), OK),
     (dict(head_dim=128, v_head_dim=128), OK),
@@ -368,8 +382,13 @@ def test_value_head_dim_support(lib, kw, status):
     assert ra.check_support(_desc(**kw)) == status
 
 
-def test_mla_workspace_and_backward_rejected(lib):
+def test_mla_workspaces(lib):
+    """MLA head dims (192 / 128) are accepted by the forward and the backward
+    (bf16); their workspaces are larger than at 128 / 128; fp32 is refused."""
     d = _desc(head_dim=192, v_head_dim=128)
     assert ra.workspace_size(d) > ra.workspace_size(_desc())
+    assert ra.bwd_workspace_size(d) > ra.bwd_workspace_size(_desc())
     with pytest.raises(ra.RingAttnError, match="RA_ERR_UNSUPPORTED"):
-        ra.bwd_workspace_size(d)
+        ra.bwd_workspace_size(_desc(head_dim=192, v_head_dim=128, qkv_dtype=ra.RA_F32))
+    with pytest.raises(ra.RingAttnError, match="RA_ERR_UNSUPPORTED"):
+        ra.bwd_workspace_size(_desc(head_dim=128, v_head_dim=64))

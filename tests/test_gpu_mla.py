@@ -124,3 +124,68 @@ def test_mla_workload_zero_queries_every_row():
     err_o = (o.double() - vm).abs().max().item()                     # Hq == Hkv here
     print(f"MLA Q=0: max|dLSE|={err_l:.2e} max|dO|={err_o:.2e}")
     assert err_o <= 2e-2, err_o
+
+
+# ----------------------------------------------------------------------------- backward
+
+def _mla_bwd(q, k, v, qi, qp, ki, kp, do, causal, window, grad_dtype=torch.float32):
+    o, lse = bosf.attn_fwd(q, k, v, qi, qp, ki, kp, causal=causal, window=window)
+    return bosf.attn_bwd(q, k, v, qi, qp, ki, kp, o, lse, do, causal=causal, window=window,
+                         grad_dtype=grad_dtype)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_cid(c) for c in SMALL])
+def test_mla_backward_small(case):
+    """dQ (192 wide), dK (192) and dV (128) of the MLA head dims against the
+    fp64 backward oracle, element by element; rows and keys that no visible
+    pair reaches must be exactly 0."""
+    from test_gpu_bwd import _unreached
+    from _parity import compare_grads
+    causal, window = case[5], case[6]
+    q, k, v, qi, qp, ki, kp = _small(case, case[1] * 7 + case[2])
+    do = random_qkv(case[0], case[1], 1, case[3], 1, DV, "bf16", seed=case[1] + 91)[0]
+    dq, dk, dv = _mla_bwd(*_dev(q, k, v, qi, qp, ki, kp, do), causal, window)
+    torch.cuda.synchronize()
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+    rq, rk, rv = oracle.attention_backward(q, k, v, do, qi, qp, ki, kp, causal=causal, window=window)
+    zq, zk = _unreached(qi.numpy(), qp.numpy(), ki.numpy(), kp.numpy(), causal, window)
+    what = f"MLA {_cid(case)}"
+    compare_grads(dq, rq, what + " dq", exact_zero=np.broadcast_to(zq[:, :, None, None], rq.shape))
+    compare_grads(dk, rk, what + " dk", exact_zero=np.broadcast_to(zk[:, :, None, None], rk.shape))
+    compare_grads(dv, rv, what + " dv", exact_zero=np.broadcast_to(zk[:, :, None, None], rv.shape))
+
+
+def test_mla_backward_bf16_gradients_and_determinism():
+    from _parity import compare_grads
+    case = SMALL[2]
+    causal, window = case[5], case[6]
+    q, k, v, qi, qp, ki, kp = _small(case, 5)
+    do = random_qkv(case[0], case[1], 1, case[3], 1, DV, "bf16", seed=6)[0]
+    args = _dev(q, k, v, qi, qp, ki, kp, do)
+    g1 = _mla_bwd(*args, causal, window, grad_dtype=torch.bfloat16)
+    g2 = _mla_bwd(*args, causal, window, grad_dtype=torch.bfloat16)
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+    refs = oracle.attention_backward(q, k, v, do, qi, qp, ki, kp, causal=causal, window=window)
+    for got, ref, n in zip(g1, refs, ("dq", "dk", "dv")):
+        assert got.dtype == torch.bfloat16
+        compare_grads(got, ref, f"MLA bf16 {n}")
+
+
+def test_mla_backward_workload_sampled_and_identities():
+    """The MLA workload (2 x 8192 tokens, 128 heads, causal) at full size:
+    sampled query rows and keys against the oracle, and per segment the keys'
+    dK summing to 0 and their dV to the summed dO."""
+    from test_gpu_bwd import _device_do, _sampled_check, _segment_identities
+    w = get(6)
+    q, k, v, ids, pos = device_inputs(w)
+    do = _device_do(w, q.shape[:3] + (w.dv,))
+    dq, dk, dv = _mla_bwd(q, k, v, ids, pos, ids, pos, do, w.causal, w.window)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(61)
+    rows = sorted({(int(rng.integers(0, w.batch)), int(t)) for t in rng.integers(0, w.seq_len, 6)} |
+                  {(0, 0), (1, w.seq_len - 1), (0, 4095)})
+    keys = sorted({(b, t) for b in range(w.batch) for t in (w.seq_len - 1, w.seq_len - 2,
+                                                           w.seq_len - 40)})
+    e = _sampled_check(w, q, k, v, ids, pos, ids, pos, do, dq, dk, dv, rows, keys, "MLA")
+    ident = _segment_identities(dk, dv, do, ids, ids, w.group, "MLA")
+    print("MLA backward sampled:", e, "identities:", ident)
