@@ -111,8 +111,12 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, ids, pos, budget_s):
-    """Oracle (fp64, host) on a bounded random row sample of the same inputs."""
+def cpu_baseline(w, q, k, v, ids, pos, budget_s, o=None, lse=None):
+    """Oracle (fp64, host) on a bounded random row sample of the same inputs.
+
+    With the step's output (``o``, ``lse`` in token order), the oracle rows it
+    computes are also compared with the GPU's: returns the baseline and the
+    sample's max |O| and |LSE| differences and -inf mismatch count (or None)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -123,11 +127,11 @@ def cpu_baseline(w, q, k, v, ids, pos, budget_s):
     rng = np.random.default_rng(0)
     valid = np.argwhere(idc.numpy() != 0)
     order = rng.permutation(len(valid))
-    rows, pairs, t0 = [], 0, time.perf_counter()
+    rows, refs, pairs, t0 = [], [], 0, time.perf_counter()
     for j in order:
         b, i = int(valid[j][0]), int(valid[j][1])
-        oracle.attention_rows(q, kc, vc, idc, posc, idc, posc, [(b, i)], causal=w.causal,
-                              window=w.window)
+        refs.append(oracle.attention_rows(q, kc, vc, idc, posc, idc, posc, [(b, i)],
+                                          causal=w.causal, window=w.window))
         n = int(oracle.visible(idc[b, i:i + 1], posc[b, i:i + 1], idc[b], posc[b], w.causal,
                                w.window).sum())
         rows.append((b, i))
@@ -136,9 +140,25 @@ def cpu_baseline(w, q, k, v, ids, pos, budget_s):
             break
     dt = time.perf_counter() - t0
     flops = 2.0 * (w.head_dim + w.dv) * w.num_q_heads * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(rows)} random valid query rows x all {w.num_q_heads} heads "
                       f"({pairs} visible pairs, {flops / 1e9:.1f} GFLOP fp64) in {dt:.1f} s"}
+    check = None
+    if o is not None and rows:
+        o_err = l_err = 0.0
+        mism = 0
+        for (b, i), (ro, rl) in zip(rows, refs):
+            go = o[b, i].to("cpu", torch.float64).numpy()
+            gl = lse[b, i].to("cpu", torch.float64).numpy()
+            ei, er = np.isneginf(gl), np.isneginf(rl[0])
+            mism += int((ei != er).sum())
+            live = ~(ei | er)
+            o_err = max(o_err, float(np.abs(go - ro[0]).max()))
+            if live.any():
+                l_err = max(l_err, float(np.abs(gl[live] - rl[0][live]).max()))
+        check = {"rows": len(rows), "heads": w.num_q_heads, "max_abs_o": o_err,
+                 "max_abs_lse": l_err, "lse_neg_inf_mismatches": mism}
+    return base, check
 
 
 def main():
@@ -203,13 +223,15 @@ def main():
     log(f"visible pairs {visible}, {flops / 1e12:.3f} TFLOP per step")
 
     ev = EventLog()
+    out = {}
     if allgather:
         bufs = bosf.RingBuffers.like(q, k, ids, w.cp_size, partials=False)
 
         def step():
-            bosf.allgather_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe,
-                                   causal=w.causal, window=w.window, bufs=bufs,
-                                   step_hook=ev.hook)
+            out.clear()   # the previous step's output is not held across the next
+            out["o"], out["lse"] = bosf.allgather_forward(
+                q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe, causal=w.causal,
+                window=w.window, bufs=bufs, step_hook=ev.hook)
     elif w.cp_size > 1:
         bufs = bosf.RingBuffers.like(q, k, ids, w.cp_size)
         # The ring schedule of this segment layout (visible pairs per rank and
@@ -224,9 +246,10 @@ def main():
             log(f"ring plan (visible pairs per rank x step): {plan.tolist()}")
 
         def step():
-            bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe, causal=w.causal,
-                              window=w.window, bufs=bufs, step_hook=ev.hook,
-                              fused=not args.unfused, plan=plan)
+            out.clear()   # the previous step's output is not held across the next
+            out["o"], out["lse"] = bosf.ring_forward(
+                q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe, causal=w.causal,
+                window=w.window, bufs=bufs, step_hook=ev.hook, fused=not args.unfused, plan=plan)
     else:
         o = torch.empty(q.shape[:3] + (w.dv,), dtype=q.dtype, device=dev)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
@@ -240,6 +263,7 @@ def main():
             bosf.attn_fwd(q, k, v, ids, pos, ids, pos, causal=w.causal, window=w.window, out=o,
                           lse=lse, workspace=wsp)
             ev.hook("attn_fwd", 0, 0, False)
+            out["o"], out["lse"] = o, lse
 
     for i in range(args.warmup):
         step()
@@ -331,10 +355,11 @@ def main():
         detail["copy_probe_bytes_each_way"] = n_el * 4
         del src, dst
 
-    cpu = None
+    cpu = check = None
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a host row sample")
-        cpu = cpu_baseline(w, q, k, v, ids, pos, args.cpu_seconds)
+        cpu, check = cpu_baseline(w, q, k, v, ids, pos, args.cpu_seconds, out.get("o"),
+                                  out.get("lse"))
 
     line = {
         "metric": METRIC,
@@ -358,15 +383,18 @@ def main():
                    "stripe": w.stripe, "strategy": "allgather" if allgather else "ring"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "sample_parity": check,
         "detail": detail,
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline_bwd(w, q, k, v, do, q_ids, q_pos, kv_ids, kv_pos, budget_s):
+def cpu_baseline_bwd(w, q, k, v, do, q_ids, q_pos, kv_ids, kv_pos, budget_s, dq=None):
     """Backward oracle (fp64, host) on a bounded random sample of one shard's
     query rows: dQ of each row over all heads (products S, dP, dQ: 2*(2D+Dv)*Hq
-    flops per visible pair, 6*D*Hq when D = Dv)."""
+    flops per visible pair, 6*D*Hq when D = Dv).  With the shard's dQ from the
+    GPU, the sampled rows are also compared: relative Frobenius error and max
+    error over max |dQ| of the sample (or None)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -378,22 +406,31 @@ def cpu_baseline_bwd(w, q, k, v, do, q_ids, q_pos, kv_ids, kv_pos, budget_s):
     rng = np.random.default_rng(1)
     valid = np.argwhere(iq.numpy() != 0)
     order = rng.permutation(len(valid))
-    rows, pairs, t0 = 0, 0, time.perf_counter()
+    rows, refs, pairs, t0 = [], [], 0, time.perf_counter()
     for j in order:
         b, i = int(valid[j][0]), int(valid[j][1])
-        oracle.backward_query_rows(qc, kc, vc, dc, iq, pq, ik, pk, [(b, i)], causal=w.causal,
-                                   window=w.window)
+        refs.append(oracle.backward_query_rows(qc, kc, vc, dc, iq, pq, ik, pk, [(b, i)],
+                                               causal=w.causal, window=w.window)[0])
         pairs += int(oracle.visible(iq[b, i:i + 1], pq[b, i:i + 1], ik[b], pk[b], w.causal,
                                     w.window).sum())
-        rows += 1
+        rows.append((b, i))
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     flops = 2.0 * (2 * w.head_dim + w.dv) * w.num_q_heads * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"dQ of {rows} random valid query rows of shard 0 x all {w.num_q_heads} heads "
-                      f"({pairs} visible pairs, {flops / 1e9:.1f} GFLOP fp64 at 2*(2D+Dv)*Hq per pair) "
-                      f"in {dt:.1f} s"}
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"dQ of {len(rows)} random valid query rows of shard 0 x all "
+                      f"{w.num_q_heads} heads ({pairs} visible pairs, {flops / 1e9:.1f} GFLOP fp64 "
+                      f"at 2*(2D+Dv)*Hq per pair) in {dt:.1f} s"}
+    check = None
+    if dq is not None and rows:
+        ref = np.stack(refs)
+        got = np.stack([dq[b, i].to("cpu", torch.float64).numpy() for b, i in rows])
+        err = got - ref
+        check = {"rows": len(rows), "heads": w.num_q_heads,
+                 "dq_rel_fro": float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300)),
+                 "dq_max_err_over_max_abs": float(np.abs(err).max() / max(np.abs(ref).max(), 1e-300))}
+    return base, check
 
 
 BWD_METRIC = "attention bwd TFLOP/s (visible pairs, 2*(3D+2Dv)*Hq per pair) + % of bf16 MFMA peak, 1 MI355X"
@@ -475,11 +512,12 @@ def bench_backward(args, w, dev):
     call_ms = float(np.mean(calls))
     achieved = flops / cp / (call_ms / 1000.0) / 1e12
     log(f"{ms_step:.3f} ms/step, {value:.1f} TFLOP/s; attn_bwd {call_ms:.3f} ms per call")
-    cpu = None
+    cpu = check = None
     if not args.no_cpu_baseline:
         log("timing the fp64 backward oracle on a host row sample")
         qs, ds, iq, pq = shards[0][:4]
-        cpu = cpu_baseline_bwd(w, qs, k, v, ds, iq, pq, ids, pos, args.cpu_seconds)
+        cpu, check = cpu_baseline_bwd(w, qs, k, v, ds, iq, pq, ids, pos, args.cpu_seconds,
+                                      dq=shards[0][6])
     line = {
         "metric": BWD_METRIC,
         "value": value,
@@ -505,6 +543,7 @@ def bench_backward(args, w, dev):
                                "dk/dv passes)",
                      "per_launch_flops": flops / cp},
         "cpu_baseline": cpu,
+        "sample_parity": check,
         "detail": {"attn_bwd_calls_per_step": cp, "attn_bwd_avg_ms_per_call": call_ms,
                    "visible_pairs_per_step": visible,
                    "workspace_bytes": int(wsp.numel())},
