@@ -81,12 +81,16 @@ class EventLog:
                 bosf.profile_next_kernel(*pair)
                 self.open["attn_kernel"] = pair
         else:
-            self.done.setdefault(name, []).append((self.open.pop(name), ev))
+            self.done.setdefault(name, []).append((self.open.pop(name), ev, rank))
             if name == "attn_fwd":
-                self.done.setdefault("attn_kernel", []).append(self.open.pop("attn_kernel"))
+                self.done.setdefault("attn_kernel", []).append(self.open.pop("attn_kernel")
+                                                               + (rank,))
 
     def ms(self, name):
-        return [a.elapsed_time(b) for a, b in self.done.get(name, [])]
+        return [a.elapsed_time(b) for a, b, _ in self.done.get(name, [])]
+
+    def ranks(self, name):
+        return [r for _, _, r in self.done.get(name, [])]
 
 
 def measured_traffic():
@@ -286,8 +290,12 @@ def main():
     kern_total_ms = float(sum(kern_ms))
     per_launch_flops = flops * args.steps / n_attn
     achieved = flops * args.steps / (kern_total_ms / 1000.0) / 1e12
-    detail = {"attn_fwd_launches_per_step": n_attn // args.steps,
+    per_step = n_attn // args.steps
+    step_kern = [sum(kern_ms[i * per_step:(i + 1) * per_step]) for i in range(args.steps)]
+    detail = {"attn_fwd_launches_per_step": per_step,
               "attn_kernel_ms_per_step": kern_total_ms / args.steps,
+              "attn_kernel_ms_per_step_median": float(np.median(step_kern)),
+              "attn_kernel_ms_per_step_min": float(min(step_kern)),
               "attn_kernel_avg_ms_per_launch": kern_total_ms / n_attn,
               "attn_fwd_call_ms_per_step": attn_total_ms / args.steps,
               "attn_fwd_call_avg_ms_per_launch": attn_total_ms / n_attn,
@@ -295,6 +303,18 @@ def main():
               "visible_pairs_per_step": visible,
               "pct_of_bf16_peak_whole_step": 100.0 * value / PEAK_BF16_TFLOPS}
     if w.cp_size > 1:
+        # per rank: the attention kernel time of its share per step and, with
+        # the ring plan's pair counts, its own rate (the headline aggregates
+        # all ranks' flops over their summed kernel time)
+        rk = ev.ranks("attn_kernel")
+        rank_ms = [sum(m for m, r in zip(kern_ms, rk) if r == rr) / args.steps
+                   for rr in range(w.cp_size)]
+        detail["attn_kernel_ms_per_step_by_rank"] = rank_ms
+        if not allgather and plan is not None:
+            rank_tf = [2.0 * (w.head_dim + w.dv) * w.num_q_heads * float(plan[rr].sum())
+                       / (rank_ms[rr] / 1000.0) / 1e12 for rr in range(w.cp_size)]
+            detail["attn_kernel_TFLOPs_by_rank"] = rank_tf
+            detail["attn_kernel_TFLOPs_min_rank"] = min(rank_tf)
         b, t, hq, d = q.shape
         n = t // w.cp_size
         reorder_ms = sum(ev.ms("reorder")) / args.steps
