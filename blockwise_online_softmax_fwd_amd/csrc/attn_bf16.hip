@@ -421,6 +421,9 @@ attn_fwd_bf16_kernel(AttnParams p) {
   // O = e^(LSE - L) U / z + e^(L_a - L) O_a.
   // The wave's O^T fragment goes through LDS in two 64-column halves so that
   // every global access of O and O_a is a contiguous 16-byte piece of a row.
+  // O is stored with the non-temporal hint: it is not read again by this
+  // launch, and streaming it keeps the L2 for the K/V tiles that neighbouring
+  // workgroups share.
   const float zt = pair_sum(z);
   const bool live = zt > 0.0f;
   const float l_own = live ? p.scale * m + logf(zt) : -INFINITY;
@@ -499,9 +502,9 @@ attn_fwd_bf16_kernel(AttnParams p) {
           hv[1] = (bf16)val[1];
           hv[2] = (bf16)val[2];
           hv[3] = (bf16)val[3];
-          *(bf16x4 *)((bf16 *)p.o + b * p.o_bs + rel) = hv;
+          __builtin_nontemporal_store(hv, (bf16x4 *)((bf16 *)p.o + b * p.o_bs + rel));
         } else {
-          *(f32x4 *)((float *)p.o + b * p.o_bs + rel) = val;
+          __builtin_nontemporal_store(val, (f32x4 *)((float *)p.o + b * p.o_bs + rel));
         }
       }
     }
