@@ -8,9 +8,12 @@ of the 4 shards, 4 ring steps -- attn_fwd for the shard's own chunk, then
 attn_fwd_accumulate for the 3 chunks that arrive next, each folding its block
 into the running fp32 partial in its epilogue (the merge of the ring update,
 fused; ``--unfused`` runs attn_fwd + attn_merge instead); inverse reorder of O
-and LSE.  All four shards are computed, so a step is the complete forward of
-B=2 x 65536 tokens; FLOPs count only visible pairs (4 * head_dim * Hq per pair).
-attn_merge is also timed on its own at the shard partials' shape.
+and LSE, folded into each rank's last ring step (a dual-chunk shard is two
+contiguous stripes of the sequence, so that step runs once per stripe and
+writes to the original positions).  All four shards are computed, so a step
+is the complete forward of B=2 x 65536 tokens; FLOPs count only visible pairs
+(4 * head_dim * Hq per pair).  attn_merge and the inverse reorder kernel are
+also timed on their own at the step's shapes.
 
 Prints one JSON line.  ``roofline`` is measured live with HIP events that the
 library records on its stream right before and after the attention kernel of
@@ -93,14 +96,15 @@ class EventLog:
         return [r for _, _, r in self.done.get(name, [])]
 
 
-def measured_traffic():
+def measured_traffic(launches_per_step):
     """HBM bytes per attn_fwd launch from the committed rocprofv3 counter runs.
 
     ``profiles/attn_fwd_longctx_ring4_traffic.json`` records FETCH_SIZE and
     WRITE_SIZE summed over the forward's launches of one step, already scaled
     by the factors a plain copy kernel of known size gave, together with the
-    SHA-256 of the forward kernel's source at the time; if the kernel has
-    changed since, the figure no longer applies and None is returned.
+    SHA-256 of the forward kernel's source at the time and the number of
+    launches per step; if the kernel or the launch structure has changed
+    since, the figure no longer applies and None is returned.
     """
     import hashlib
     path = os.path.join(ROOT, "profiles", "attn_fwd_longctx_ring4_traffic.json")
@@ -110,7 +114,7 @@ def measured_traffic():
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_source_sha256") != sha or rec.get("launches_per_step") != launches_per_step:
         return None
     return rec.get("bytes_per_launch")
 
@@ -175,6 +179,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="ring steps write separate partials folded by attn_merge")
+    ap.add_argument("--separate-inverse", action="store_true",
+                    help="ring: run the inverse reorder of O and LSE as its own pass instead of "
+                         "folding it into each rank's last ring step")
     ap.add_argument("--no-plan", action="store_true",
                     help="launch every ring step, also those whose blocks hold no visible pair")
     ap.add_argument("--strategy", choices=("ring", "allgather"), default="ring",
@@ -253,7 +260,8 @@ def main():
             out.clear()   # the previous step's output is not held across the next
             out["o"], out["lse"] = bosf.ring_forward(
                 q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe, causal=w.causal,
-                window=w.window, bufs=bufs, step_hook=ev.hook, fused=not args.unfused, plan=plan)
+                window=w.window, bufs=bufs, step_hook=ev.hook, fused=not args.unfused, plan=plan,
+                fuse_inverse=not args.separate_inverse)
     else:
         o = torch.empty(q.shape[:3] + (w.dv,), dtype=q.dtype, device=dev)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
@@ -329,9 +337,29 @@ def main():
                                  else "steps without visible pairs skipped")),
             "reorder_ms_per_step": reorder_ms,
             "reorder_GBs": fwd_bytes / (reorder_ms / 1000.0) / 1e9,
-            "inverse_reorder_ms_per_step": inv_ms,
-            "inverse_reorder_GBs": inv_bytes / (inv_ms / 1000.0) / 1e9,
         })
+        if ev.ms("inverse_reorder"):
+            detail.update({"inverse_reorder_ms_per_step": inv_ms,
+                           "inverse_reorder_GBs": inv_bytes / (inv_ms / 1000.0) / 1e9})
+        else:
+            detail["inverse_reorder"] = ("folded into each rank's last ring step: it runs once "
+                                         "per dual-chunk stripe and writes O and the LSE at "
+                                         "their original positions")
+            # the inverse reorder kernel on its own, on the step's O and LSE
+            # (outside the step), for its HBM rate
+            o_s, l_s = out["o"], out["lse"]
+            for _ in range(2):
+                bosf.inverse_reorder(o_s, w.cp_size, w.reorder, w.stripe)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                bosf.inverse_reorder(o_s, w.cp_size, w.reorder, w.stripe)
+                bosf.inverse_reorder(l_s, w.cp_size, w.reorder, w.stripe)
+            e1.record()
+            torch.cuda.synchronize()
+            ims = e0.elapsed_time(e1) / 5
+            detail.update({"inverse_reorder_standalone_ms": ims,
+                           "inverse_reorder_standalone_GBs": inv_bytes / (ims / 1000.0) / 1e9})
         if args.unfused:
             merges = ev.ms("attn_merge")
             detail["attn_merge_ms_per_step"] = sum(merges) / args.steps
@@ -359,7 +387,7 @@ def main():
         del pa, pb, la, lb, outm, outl
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": (measured_traffic() if args.workload == 5 and not allgather
+                "traffic": (measured_traffic(per_step) if args.workload == 5 and not allgather
                             and not args.unfused and not args.no_plan else None),
                 "kernel": "attn_fwd_bf16_kernel (events recorded by the library around the "
                           "kernel alone)",

@@ -77,16 +77,20 @@ def reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs: RingBuff
 
 
 def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, window=(-1, -1),
-               step_hook=None, fused=True, steps=None):
+               step_hook=None, fused=True, steps=None, final=None):
     """Rank ``rank``'s R ring steps on the reordered buffers; the merged result
     lands in rank's shard of ``bufs.o`` / ``bufs.lse`` (reordered order).
 
     ``fused``: each step after the first folds its block into the running
     partial inside the forward's epilogue (``attn_fwd_accumulate``, in place in
     the fp32 partial, the last step writing the final output); otherwise every
-    step writes its own partial and ``attn_merge`` folds it in."""
+    step writes its own partial and ``attn_merge`` folds it in.  ``final``
+    (fused only): ``[(rows, o_view, lse_view), ...]`` -- the last step writes
+    the shard's rows ``rows`` straight into those views instead of ``bufs.o``
+    (how the dual-chunk inverse reorder is folded into the last step)."""
     if fused:
-        return _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, steps)
+        return _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, steps,
+                                 final)
     t = bufs.q.shape[1]
     n = t // cp_size
     rows = slice(rank * n, (rank + 1) * n)
@@ -119,30 +123,37 @@ def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, win
             step_hook("attn_merge", rank, s, False)
 
 
-def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, steps=None):
+def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, steps=None,
+                      final=None):
     t = bufs.q.shape[1]
     n = t // cp_size
     rows = slice(rank * n, (rank + 1) * n)
     q_r, id_r, pos_r = bufs.q[:, rows], bufs.ids[:, rows], bufs.pos[:, rows]
-    o_r, lse_r = bufs.o[:, rows], bufs.lse[:, rows]
+    if final is None:
+        final = [(slice(0, n), bufs.o[:, rows], bufs.lse[:, rows])]
     steps = list(range(cp_size)) if steps is None else steps
     for i, s in enumerate(steps):
         c = (rank - s) % cp_size
         cols = slice(c * n, (c + 1) * n)
-        args = (q_r, bufs.k[:, cols], bufs.v[:, cols], id_r, pos_r, bufs.ids[:, cols],
-                bufs.pos[:, cols])
+        kv = (bufs.k[:, cols], bufs.v[:, cols])
+        kmeta = (bufs.ids[:, cols], bufs.pos[:, cols])
         last = i == len(steps) - 1
-        dst, dst_lse = (o_r, lse_r) if last else (bufs.acc, bufs.acc_lse)
-        if step_hook:
-            step_hook("attn_fwd", rank, s, True)
-        if i == 0:
-            ra.attn_fwd(*args, scale=scale, causal=causal, window=window, out_dtype=dst.dtype,
-                        out=dst, lse=dst_lse, workspace=bufs.workspace)
-        else:
-            ra.attn_fwd_accumulate(*args, bufs.acc, bufs.acc_lse, scale=scale, causal=causal,
-                                   window=window, out=dst, lse=dst_lse, workspace=bufs.workspace)
-        if step_hook:
-            step_hook("attn_fwd", rank, s, False)
+        # (query rows of the shard, output, lse): the running partial, or the
+        # final destinations at the last step
+        dsts = final if last else [(slice(0, n), bufs.acc, bufs.acc_lse)]
+        for qr, dst, dst_lse in dsts:
+            args = (q_r[:, qr], *kv, id_r[:, qr], pos_r[:, qr], *kmeta)
+            if step_hook:
+                step_hook("attn_fwd", rank, s, True)
+            if i == 0:
+                ra.attn_fwd(*args, scale=scale, causal=causal, window=window,
+                            out_dtype=dst.dtype, out=dst, lse=dst_lse, workspace=bufs.workspace)
+            else:
+                ra.attn_fwd_accumulate(*args, bufs.acc[:, qr], bufs.acc_lse[:, qr], scale=scale,
+                                       causal=causal, window=window, out=dst, lse=dst_lse,
+                                       workspace=bufs.workspace)
+            if step_hook:
+                step_hook("attn_fwd", rank, s, False)
 
 
 def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_heads, num_kv_heads,
@@ -178,7 +189,7 @@ def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_head
 def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, scale=None,
                  causal=True, window=(-1, -1), ranks=None, bufs: RingBuffers | None = None,
                  partial_dtype=torch.float32, out_dtype=None, step_hook=None, fused=True,
-                 plan=None):
+                 plan=None, fuse_inverse=True):
     """Ring-decomposed attention forward of self-attention inputs on one GPU.
 
     q ``[B,T,Hq,D]``, k/v ``[B,T,Hkv,D]``, ids/pos ``int32 [B,T]`` in the
@@ -187,6 +198,13 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     (the others are left as they were in ``bufs``).  With ``plan`` (from
     :func:`ring_plan` on the same layout and mask) the fused path runs only
     the steps whose blocks hold visible pairs.
+
+    With the dual-chunk reorder, the fused path and every rank run
+    (``fuse_inverse``), the inverse reorder is folded into each rank's last
+    step: a dual-chunk shard is two contiguous stripes of the original
+    sequence (stripes r and 2R-1-r), so the last step runs once per stripe,
+    writing O and the LSE straight to their original positions; no separate
+    inverse-reorder pass is made.  The result is bit-identical.
     """
     if q.shape[1] != k.shape[1]:
         raise ValueError("the ring driver runs self-attention (Tq == Tk)")
@@ -205,12 +223,27 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs)
     if step_hook:
         step_hook("reorder", -1, -1, False)
+    direct = (fuse_inverse and fused and ranks is None and cp_size > 1
+              and ra._kind_code(kind) == ra.DUAL_CHUNK)
+    if direct:
+        o = torch.empty_like(bufs.o)
+        lse = torch.empty_like(bufs.lse)
+    n = q.shape[1] // cp_size
+    h = n // 2
     for r in (range(cp_size) if ranks is None else ranks):
         steps = None
         if plan is not None and fused:
             steps = [s for s in range(cp_size) if int(plan[r, s]) > 0] or [cp_size - 1]
+        final = None
+        if direct:
+            # shard rows [0, h) are stripe r, rows [h, 2h) stripe 2R-1-r
+            final = [(slice(0, h), o[:, r * h:(r + 1) * h], lse[:, r * h:(r + 1) * h]),
+                     (slice(h, n), o[:, (2 * cp_size - 1 - r) * h:(2 * cp_size - r) * h],
+                      lse[:, (2 * cp_size - 1 - r) * h:(2 * cp_size - r) * h])]
         rank_steps(r, cp_size, bufs, scale=scale, causal=causal, window=window, step_hook=step_hook,
-                   fused=fused, steps=steps)
+                   fused=fused, steps=steps, final=final)
+    if direct:
+        return o, lse
     if step_hook:
         step_hook("inverse_reorder", -1, -1, True)
     o = ra.inverse_reorder(bufs.o, cp_size, kind, stripe_size)

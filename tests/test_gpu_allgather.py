@@ -161,3 +161,27 @@ def test_ring_with_plan_is_bit_identical():
     o2, l2 = bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe,
                                causal=w.causal, window=w.window, plan=plan)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("cp,window,dtype", [(4, (2048, 0), "bf16"), (2, (-1, -1), "bf16"),
+                                             (8, (300, 0), "bf16"), (4, (500, 0), "f32")])
+def test_ring_inverse_folded_into_last_step_is_bit_identical(cp, window, dtype):
+    """The dual-chunk inverse reorder folded into each rank's last ring step
+    (one launch per stripe, writing O and the LSE at their original positions)
+    gives the same bits as the separate inverse-reorder pass, with and without
+    the plan of steps."""
+    b, t, hq, hkv = 2, 4096, 8, 2
+    ids, pos = packed_metadata(b, t, 2, 1500)
+    q, k, v = _dev(*random_qkv(b, t, t, hq, hkv, 64, dtype, seed=cp * 7 + 1))
+    ids, pos = _dev(ids, pos)
+    kw = dict(causal=True, window=window)
+    o_a, l_a = bosf.ring_forward(q, k, v, ids, pos, cp, "dual_chunk", 1, fuse_inverse=False, **kw)
+    o_b, l_b = bosf.ring_forward(q, k, v, ids, pos, cp, "dual_chunk", 1, **kw)
+    plan = bosf.ring_plan(ids, pos, cp, "dual_chunk", 1, num_q_heads=hq, num_kv_heads=hkv,
+                          head_dim=64, dtype=q.dtype, **kw)
+    o_c, l_c = bosf.ring_forward(q, k, v, ids, pos, cp, "dual_chunk", 1, plan=plan, **kw)
+    assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
+    assert torch.equal(o_a, o_c) and torch.equal(l_a, l_c)
+    ro, rl = oracle.attention(q.cpu(), k.cpu(), v.cpu(), ids.cpu(), pos.cpu(), ids.cpu(),
+                              pos.cpu(), **kw)
+    compare(o_b, l_b, ro, rl, dtype, f"folded inverse cp={cp}")
