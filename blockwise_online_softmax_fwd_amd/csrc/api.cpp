@@ -43,6 +43,8 @@ struct Resolved {
   int64_t v_bs, v_ts;         // V's strides
   int32_t dv;                 // head dim of V and O
   int32_t bm, bn, nqt, nkt, nt;
+  int32_t split;              // split row of o / lse (0: none)
+  int64_t o_soff, lse_soff;   // their extra offsets (elements)
 };
 
 int64_t pick(int64_t given, int64_t dense) { return given == 0 ? dense : given; }
@@ -73,7 +75,6 @@ ra_status check_desc(const ra_attn_desc *d, Resolved *r) {
   if (!dtype_ok(d->qkv_dtype)) return fail(RA_ERR_DTYPE, "unknown qkv_dtype %d", d->qkv_dtype);
   if (!dtype_ok(d->out_dtype)) return fail(RA_ERR_DTYPE, "unknown out_dtype %d", d->out_dtype);
   if (d->v_head_dim < 0) return fail(RA_ERR_SHAPE, "v_head_dim must be >= 0");
-  if (d->reserved != 0) return fail(RA_ERR_SHAPE, "reserved must be 0");
   r->dv = d->v_head_dim ? d->v_head_dim : d->head_dim;
   {
     const bool same = r->dv == d->head_dim && (d->head_dim == 64 || d->head_dim == 128);
@@ -115,6 +116,22 @@ ra_status check_desc(const ra_attn_desc *d, Resolved *r) {
     return fail(RA_ERR_SHAPE, "q, k, v or o strides let two (batch, token) rows overlap");
   if (B > 1 && (r->lse_bs < Tq * Hq || r->qm_bs < Tq || r->km_bs < Tk))
     return fail(RA_ERR_SHAPE, "a batch stride is smaller than one batch row");
+  if (d->o_split_row < 0 || d->o_split_offset < 0 || d->lse_split_offset < 0)
+    return fail(RA_ERR_SHAPE, "o_split_row and the split offsets must be >= 0");
+  r->split = d->o_split_row;
+  r->o_soff = d->o_split_offset;
+  r->lse_soff = d->lse_split_offset;
+  if (r->split == 0 && (r->o_soff != 0 || r->lse_soff != 0))
+    return fail(RA_ERR_SHAPE, "split offsets given without o_split_row");
+  if (r->split > 0) {
+    if (r->split >= Tq)
+      return fail(RA_ERR_SHAPE, "o_split_row %d must be below q_len %d", r->split, d->q_len);
+    if (r->o_ts < Hq * DV)
+      return fail(RA_ERR_SHAPE, "a split output needs an o token stride of at least Hq*Dv");
+    if (B > 1 && (r->o_bs < (Tq - 1) * r->o_ts + r->o_soff + Hq * DV ||
+                  r->lse_bs < Tq * Hq + r->lse_soff))
+      return fail(RA_ERR_SHAPE, "a split output's batch row extends past its batch stride");
+  }
   if (d->qkv_dtype == RA_BF16) {
     r->nt = ra::bf16_token_subtiles(d->num_q_heads / d->num_kv_heads);
     r->bm = 32 * r->nt;
@@ -317,8 +334,12 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
   const size_t q_span = span_bytes2(B, Tq, Lq, r.q_bs, r.q_ts, es);
   const size_t kv_span = span_bytes2(B, Tk, Lk, r.kv_bs, r.kv_ts, es);
   const size_t v_span = span_bytes2(B, Tk, Lv, r.v_bs, r.v_ts, es);
-  const size_t o_span = span_bytes2(B, Tq, Lo, r.o_bs, r.o_ts, os);
-  const size_t l_span = span_bytes(d->batch, r.lse_bs, (int64_t)d->q_len * d->num_q_heads, 4);
+  // a split output's extent includes the gap before its moved rows
+  const size_t o_span = span_bytes2(B, Tq, Lo, r.o_bs, r.o_ts, os) + (size_t)r.o_soff * os;
+  const size_t l_span = span_bytes(d->batch, r.lse_bs, (int64_t)d->q_len * d->num_q_heads, 4) +
+                        (size_t)r.lse_soff * 4;
+  if (r.split > 0 && (r.o_soff * (int64_t)os) % 16)
+    return fail(RA_ERR_ALIGN, "o_split_offset must be a multiple of 16 bytes");
   if (overlaps(o, o_span, q, q_span) || overlaps(o, o_span, k, kv_span) ||
       overlaps(o, o_span, v, v_span) || overlaps(lse, l_span, o, o_span) ||
       overlaps(lse, l_span, q, q_span) || overlaps(lse, l_span, k, kv_span) ||
@@ -343,7 +364,7 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
     const size_t al_span = span_bytes(d->batch, acc_lse_bs, rows, 4);
     const bool same_o = acc->o == o && acc->dtype == d->out_dtype && acc_o_bs == r.o_bs;
     const bool same_l = acc->lse == lse && acc_lse_bs == r.lse_bs;
-    in_place = same_o && same_l;
+    in_place = same_o && same_l && r.split == 0;
     if (!in_place && (overlaps(o, o_span, acc->o, a_span) || overlaps(lse, l_span, acc->lse, al_span) ||
                       overlaps(o, o_span, acc->lse, al_span) || overlaps(lse, l_span, acc->o, a_span)))
       return fail(RA_ERR_ALIAS, "o / lse overlap the partial without being it");
@@ -398,6 +419,9 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
   p.acc_lse_bs = acc_lse_bs;
   p.acc_mode = acc ? (acc->dtype == RA_BF16 ? 2 : 1) : 0;
   p.acc_in_place = in_place ? 1 : 0;
+  p.o_split = r.split > 0 ? r.split : INT32_MAX;
+  p.o_split_off = r.o_soff;
+  p.lse_split_off = r.lse_soff;
   p.kpack = (char *)workspace + L.kpack;
   p.vpack = (char *)workspace + L.vpack;
   p.mpack = (const int32_t *)((char *)workspace + L.mpack);
@@ -475,6 +499,7 @@ ra_status ra_classify_tiles(const ra_attn_desc *d, const int32_t *qid, const int
   Resolved r;
   ra_status st = check_desc(d, &r);
   if (st != RA_OK) return st;
+  if (r.split != 0) return fail(RA_ERR_UNSUPPORTED, "o_split_row applies to the forward's output only");
   st = check_meta(d, r, qid, qpos, kid, kpos);
   if (st != RA_OK) return st;
   if (!aligned(visible_pairs, 8)) return fail(RA_ERR_ALIGN, "visible_pairs must be 8-byte aligned");
@@ -577,6 +602,7 @@ struct BwdShape {
 ra_status check_bwd_desc(const ra_attn_desc *d, Resolved *r, BwdShape *bs) {
   ra_status st = check_desc(d, r);
   if (st != RA_OK) return st;
+  if (r->split != 0) return fail(RA_ERR_UNSUPPORTED, "o_split_row applies to the forward's output only");
   if (d->qkv_dtype != RA_BF16)
     return fail(RA_ERR_UNSUPPORTED, "the backward needs bf16 q, k and v");
   // check_desc admits only the head-dim pairs the kernels have: equal, or MLA's 192 / 128

@@ -434,7 +434,8 @@ attn_fwd_bf16_kernel(AttnParams p) {
     w_acc = lse_weight(la, l_out);
     w_own = live ? lse_weight(l_own, l_out) / zt : 0.0f;
   }
-  if (qvalid && half == 0) p.lse[b * p.lse_bs + (int64_t)tq * p.hq + h] = l_out;
+  if (qvalid && half == 0)
+    p.lse[b * p.lse_bs + (int64_t)tq * p.hq + h + (tq >= p.o_split ? p.lse_split_off : 0)] = l_out;
   if (half == 0) stage_w[wave][col] = w_acc;
 
   const int tq0 = qt * BM + (wave / NH) * 32;   // first query token of this wave
@@ -494,6 +495,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
       f32x4 val = *(const f32x4 *)&stage[wave][qrow][c4];
       if (t < p.tq) {
         const int64_t rel = (int64_t)t * p.o_ts + (int64_t)h * DVH + 64 * hd + c4;
+        const int64_t orel = rel + (t >= p.o_split ? p.o_split_off : 0);   // split output
         const float wa = stage_w[wave][qrow];
         if (wa != 0.0f) val += wa * acc[hd][pass];
         if (OUT_BF16) {
@@ -502,9 +504,9 @@ attn_fwd_bf16_kernel(AttnParams p) {
           hv[1] = (bf16)val[1];
           hv[2] = (bf16)val[2];
           hv[3] = (bf16)val[3];
-          __builtin_nontemporal_store(hv, (bf16x4 *)((bf16 *)p.o + b * p.o_bs + rel));
+          __builtin_nontemporal_store(hv, (bf16x4 *)((bf16 *)p.o + b * p.o_bs + orel));
         } else {
-          __builtin_nontemporal_store(val, (f32x4 *)((float *)p.o + b * p.o_bs + rel));
+          __builtin_nontemporal_store(val, (f32x4 *)((float *)p.o + b * p.o_bs + orel));
         }
       }
     }

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
     w_acc = lse_weight(la, l_out);
     w_own = live ? lse_weight(l_own, l_out) / z : 0.0f;
   }
-  const int64_t obase = b * p.o_bs + rel;
+  const int64_t obase = b * p.o_bs + rel + (tq >= p.o_split ? p.o_split_off : 0);  // split output
   const int64_t abase = b * p.acc_o_bs + rel;
   for (int d = 0; d < DH; ++d) {
     float val = o[d] * w_own;
@@ -134,7 +134,8 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
     else
       ((float *)p.o)[obase + d] = val;
   }
-  if (half == 0) p.lse[b * p.lse_bs + (int64_t)tq * p.hq + h] = l_out;
+  if (half == 0)
+    p.lse[b * p.lse_bs + (int64_t)tq * p.hq + h + (tq >= p.o_split ? p.lse_split_off : 0)] = l_out;
 }
 
 template <int D>

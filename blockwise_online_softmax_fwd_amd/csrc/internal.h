@@ -87,6 +87,10 @@ struct AttnParams {
   int64_t acc_o_bs, acc_lse_bs;
   int32_t acc_mode;      // 0 none, 1 fp32 partial, 2 bf16 partial
   int32_t acc_in_place;  // o/lse are the partial itself: untouched tiles are skipped
+  // Split output: query rows >= o_split (INT32_MAX: none) are written
+  // o_split_off / lse_split_off elements further on in o / lse.
+  int32_t o_split;
+  int64_t o_split_off, lse_split_off;
 };
 
 // Launchers (return the launch's hipError_t).

@@ -85,9 +85,9 @@ def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, win
     partial inside the forward's epilogue (``attn_fwd_accumulate``, in place in
     the fp32 partial, the last step writing the final output); otherwise every
     step writes its own partial and ``attn_merge`` folds it in.  ``final``
-    (fused only): ``[(rows, o_view, lse_view), ...]`` -- the last step writes
-    the shard's rows ``rows`` straight into those views instead of ``bufs.o``
-    (how the dual-chunk inverse reorder is folded into the last step)."""
+    (fused only): ``(o_lo, lse_lo, split)`` -- the last step writes its output
+    there instead of ``bufs.o``, ``split`` as in ``attn_fwd`` (how the
+    dual-chunk inverse reorder is folded into the last step)."""
     if fused:
         return _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, steps,
                                  final)
@@ -130,30 +130,26 @@ def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, ste
     rows = slice(rank * n, (rank + 1) * n)
     q_r, id_r, pos_r = bufs.q[:, rows], bufs.ids[:, rows], bufs.pos[:, rows]
     if final is None:
-        final = [(slice(0, n), bufs.o[:, rows], bufs.lse[:, rows])]
+        final = (bufs.o[:, rows], bufs.lse[:, rows], None)
     steps = list(range(cp_size)) if steps is None else steps
     for i, s in enumerate(steps):
         c = (rank - s) % cp_size
         cols = slice(c * n, (c + 1) * n)
-        kv = (bufs.k[:, cols], bufs.v[:, cols])
-        kmeta = (bufs.ids[:, cols], bufs.pos[:, cols])
+        args = (q_r, bufs.k[:, cols], bufs.v[:, cols], id_r, pos_r, bufs.ids[:, cols],
+                bufs.pos[:, cols])
         last = i == len(steps) - 1
-        # (query rows of the shard, output, lse): the running partial, or the
-        # final destinations at the last step
-        dsts = final if last else [(slice(0, n), bufs.acc, bufs.acc_lse)]
-        for qr, dst, dst_lse in dsts:
-            args = (q_r[:, qr], *kv, id_r[:, qr], pos_r[:, qr], *kmeta)
-            if step_hook:
-                step_hook("attn_fwd", rank, s, True)
-            if i == 0:
-                ra.attn_fwd(*args, scale=scale, causal=causal, window=window,
-                            out_dtype=dst.dtype, out=dst, lse=dst_lse, workspace=bufs.workspace)
-            else:
-                ra.attn_fwd_accumulate(*args, bufs.acc[:, qr], bufs.acc_lse[:, qr], scale=scale,
-                                       causal=causal, window=window, out=dst, lse=dst_lse,
-                                       workspace=bufs.workspace)
-            if step_hook:
-                step_hook("attn_fwd", rank, s, False)
+        dst, dst_lse, split = final if last else (bufs.acc, bufs.acc_lse, None)
+        if step_hook:
+            step_hook("attn_fwd", rank, s, True)
+        if i == 0:
+            ra.attn_fwd(*args, scale=scale, causal=causal, window=window, out_dtype=dst.dtype,
+                        out=dst, lse=dst_lse, workspace=bufs.workspace, split=split)
+        else:
+            ra.attn_fwd_accumulate(*args, bufs.acc, bufs.acc_lse, scale=scale, causal=causal,
+                                   window=window, out=dst, lse=dst_lse, workspace=bufs.workspace,
+                                   split=split)
+        if step_hook:
+            step_hook("attn_fwd", rank, s, False)
 
 
 def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_heads, num_kv_heads,
@@ -202,9 +198,10 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     With the dual-chunk reorder, the fused path and every rank run
     (``fuse_inverse``), the inverse reorder is folded into each rank's last
     step: a dual-chunk shard is two contiguous stripes of the original
-    sequence (stripes r and 2R-1-r), so the last step runs once per stripe,
-    writing O and the LSE straight to their original positions; no separate
-    inverse-reorder pass is made.  The result is bit-identical.
+    sequence (stripes r and 2R-1-r), so the last step writes its output with a
+    split at the second stripe (``split`` of ``attn_fwd``), O and the LSE going
+    straight to their original positions; no separate inverse-reorder pass is
+    made.  The result is bit-identical.
     """
     if q.shape[1] != k.shape[1]:
         raise ValueError("the ring driver runs self-attention (Tq == Tk)")
@@ -237,9 +234,8 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
         final = None
         if direct:
             # shard rows [0, h) are stripe r, rows [h, 2h) stripe 2R-1-r
-            final = [(slice(0, h), o[:, r * h:(r + 1) * h], lse[:, r * h:(r + 1) * h]),
-                     (slice(h, n), o[:, (2 * cp_size - 1 - r) * h:(2 * cp_size - r) * h],
-                      lse[:, (2 * cp_size - 1 - r) * h:(2 * cp_size - r) * h])]
+            hi = slice((2 * cp_size - 1 - r) * h, (2 * cp_size - r) * h)
+            final = (o[:, r * h:(r + 1) * h], lse[:, r * h:(r + 1) * h], (h, o[:, hi], lse[:, hi]))
         rank_steps(r, cp_size, bufs, scale=scale, causal=causal, window=window, step_hook=step_hook,
                    fused=fused, steps=steps, final=final)
     if direct:

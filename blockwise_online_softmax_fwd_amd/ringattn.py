@@ -46,9 +46,11 @@ class AttnDesc(ctypes.Structure):
         (n, ctypes.c_int64) for n in (
             "q_batch_stride", "kv_batch_stride", "o_batch_stride", "lse_batch_stride",
             "q_meta_batch_stride", "kv_meta_batch_stride", "q_token_stride", "kv_token_stride",
-            "o_token_stride")] + [("v_head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32),
+            "o_token_stride")] + [("v_head_dim", ctypes.c_int32), ("o_split_row", ctypes.c_int32),
                                   ("v_batch_stride", ctypes.c_int64),
-                                  ("v_token_stride", ctypes.c_int64)]
+                                  ("v_token_stride", ctypes.c_int64),
+                                  ("o_split_offset", ctypes.c_int64),
+                                  ("lse_split_offset", ctypes.c_int64)]
 
 
 class Partial(ctypes.Structure):
@@ -233,14 +235,39 @@ def _attn_desc(q, k, q_ids, kv_ids, scale, causal, window, out_dtype, o, lse, v=
                      window, strides)
 
 
+def _apply_split(desc, out, lse, split, tq):
+    """Split output: rows >= ``row`` of the call go to ``out_hi`` / ``lse_hi``
+    (views with out's and lse's strides) instead of following ``out`` / ``lse``."""
+    row, out_hi, lse_hi = split
+    if not 0 < row < tq:
+        raise ValueError("the split row must lie inside the query rows")
+    if (out.shape[1] != row or lse.shape[1] != row or out_hi.shape[1] != tq - row
+            or lse_hi.shape[1] != tq - row):
+        raise ValueError("out/lse hold the rows below the split, out_hi/lse_hi the rest")
+    if out_hi.dtype != out.dtype or _bt_strides(out_hi) != _bt_strides(out) or lse_hi.stride() != lse.stride():
+        raise ValueError("the split halves must share dtype and strides")
+    ots = _bt_strides(out)[1]
+    o_off = out_hi.data_ptr() - out.data_ptr() - row * ots * out.element_size()
+    l_off = lse_hi.data_ptr() - lse.data_ptr() - row * lse.shape[2] * 4
+    if o_off < 0 or l_off < 0 or o_off % out.element_size() or l_off % 4:
+        raise ValueError("the rows above the split must lie after those below it")
+    desc.o_split_row = row
+    desc.o_split_offset = o_off // out.element_size()
+    desc.lse_split_offset = l_off // 4
+
+
 def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, *, scale=None,
-             causal=True, window=(-1, -1), out_dtype=None, out=None, lse=None, workspace=None):
+             causal=True, window=(-1, -1), out_dtype=None, out=None, lse=None, workspace=None,
+             split=None):
     """Masked GQA attention forward.  Returns ``(o, lse)``.
 
     q ``[B,Tq,Hq,D]``, k ``[B,Tk,Hkv,D]``, v ``[B,Tk,Hkv,Dv]`` (bf16 or fp32,
     same dtype; Dv = D, or D = 192 with Dv = 128 for MLA head dims in bf16),
     ids/pos int32 ``[B,T]``.  O is ``[B,Tq,Hq,Dv]``.  ``out``/``lse`` may be
     given (views into larger or packed buffers); otherwise they are allocated.
+    ``split=(row, out_hi, lse_hi)``: query rows >= row are written to
+    ``out_hi``/``lse_hi`` (placed after ``out``/``lse`` in the same buffers, which
+    then hold rows [0, row) only) -- a split output.
     """
     _require_gpu(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos)
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -257,6 +284,8 @@ def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
     if lse is None:
         lse = torch.empty((b, tq, hq), dtype=torch.float32, device=q.device)
     desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window, oc, out, lse, v)
+    if split is not None:
+        _apply_split(desc, out, lse, split, tq)
     ws_bytes = workspace_size(desc)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
@@ -269,11 +298,12 @@ def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
 
 def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos,
                         partial_o, partial_lse, *, scale=None, causal=True, window=(-1, -1),
-                        out_dtype=None, out=None, lse=None, workspace=None):
+                        out_dtype=None, out=None, lse=None, workspace=None, split=None):
     """Attention forward merged with a running partial ``(partial_o, partial_lse)``
     over other key sets.  ``out``/``lse`` default to the partial itself (in-place
     update); query tiles with no visible pair in this call are then untouched.
-    Returns ``(out, lse)``."""
+    ``split`` as in :func:`attn_fwd` (``out``/``lse`` must then be given and be
+    separate from the partial).  Returns ``(out, lse)``."""
     _require_gpu(q, k, v, partial_o, partial_lse)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
@@ -293,6 +323,8 @@ def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, k
     if _dtype_code(out.dtype) != oc:
         raise TypeError("out has the wrong dtype")
     desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window, oc, out, lse, v)
+    if split is not None:
+        _apply_split(desc, out, lse, split, tq)
     part = Partial()
     part.o, part.lse = partial_o.data_ptr(), partial_lse.data_ptr()
     part.dtype = _dtype_code(partial_o.dtype)

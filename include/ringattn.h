@@ -95,6 +95,18 @@ enum { RA_TILE_SKIP = 0, RA_TILE_PARTIAL = 1, RA_TILE_FULL = 2 };
  * The (batch, token) rows of each tensor must nest without overlap: with
  * L = H*D, either token stride >= L and batch stride >= (T-1)*token stride + L,
  * or batch stride >= L and token stride >= (B-1)*batch stride + L.
+ *
+ * Split output (ra_attn_fwd and ra_attn_fwd_accumulate only; every other entry
+ * point requires o_split_row = 0): with 0 < o_split_row < Tq, query row t >=
+ * o_split_row of batch row b is written at o + b*o_batch_stride +
+ * t*o_token_stride + o_split_offset, and its LSE at lse + b*lse_batch_stride +
+ * t*Hq + lse_split_offset.  A dual-chunk shard ([RA] "Load balance") is two
+ * stripes of the sequence, so its result can go straight to the stripes'
+ * original positions: the inverse reorder folded into the call.  Needs token
+ * stride >= L; the offsets are >= 0, o_split_offset keeps o 16-byte aligned,
+ * and with B > 1 each batch row's extent (gap included) fits in its batch
+ * stride.  That extent must not overlap any input, and an accumulating call's
+ * partial must then be a separate buffer (no in-place update).
  */
 typedef struct ra_attn_desc {
   int32_t batch;          /* B  >= 0                                           */
@@ -119,9 +131,11 @@ typedef struct ra_attn_desc {
   int64_t kv_token_stride;  /* the same for k and v (one value for both); 0 = Hkv*D         */
   int64_t o_token_stride;   /* the same for o (and a running partial, dout); 0 = Hq*Dv     */
   int32_t v_head_dim;       /* Dv, head dim of v and o; 0 = head_dim (see below)           */
-  int32_t reserved;         /* 0                                                           */
+  int32_t o_split_row;      /* 0, or a split row of the output (see below)                 */
   int64_t v_batch_stride;   /* v's strides; 0 = k's when Dv == head_dim, else dense        */
   int64_t v_token_stride;   /*   (Tk*Hkv*Dv and Hkv*Dv)                                    */
+  int64_t o_split_offset;   /* elements: extra offset of o rows >= o_split_row (>= 0)      */
+  int64_t lse_split_offset; /* elements: the same for lse (>= 0)                           */
 } ra_attn_desc;
 
 /* Library identification and diagnostics.  The returned strings are static

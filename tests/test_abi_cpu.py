@@ -208,6 +208,46 @@ def test_accumulate_validation(lib):
     assert call(ctypes.byref(part), o=_p(10 << 32), lse=_p(11 << 32)) == ALIAS
 
 
+def test_split_output_validation(lib):
+    """A split output (rows >= o_split_row moved o_split_offset / lse_split_offset
+    further on) is checked before any launch: its row inside the query rows, the
+    offsets >= 0 and aligned, each batch row's extent inside its batch stride,
+    no overlap of the extent with an input, no in-place partial, and only the
+    forward outputs may be split."""
+    L = 16 * 128                                    # one o row (elements), q_len 100
+    ok = dict(o_split_row=50, o_split_offset=300 * L, lse_split_offset=300 * 16,
+              o_batch_stride=1000 * L, lse_batch_stride=1000 * 16)
+    assert ra.check_support(_desc(**ok)) == OK
+    for bad, st in [(dict(o_split_row=100), SHAPE), (dict(o_split_row=-1), SHAPE),
+                    (dict(o_split_row=0), SHAPE),                    # offsets without a row
+                    (dict(o_split_offset=-L), SHAPE),
+                    (dict(o_batch_stride=300 * L), SHAPE),          # extent past the batch stride
+                    (dict(lse_batch_stride=300 * 16), SHAPE),
+                    (dict(o_token_stride=L // 2, o_batch_stride=L // 2 * 100), SHAPE)]:
+        assert ra.check_support(_desc(**{**ok, **bad})) == st, bad
+    assert _fwd(lib, _desc(**{**ok, "o_split_offset": 300 * L + 4})) == ALIGN   # 8 bytes in bf16
+    # q sits in the gap between o's rows below the split (200 KB) and those
+    # moved 300 rows further on
+    assert _fwd(lib, _desc(**ok), o=_p(-(512 << 10))) == ALIAS
+    # in place is refused with a split
+    d = _desc(**ok)
+    d.out_dtype = ra.RA_F32
+    part = ra.Partial()
+    part.o, part.lse, part.dtype = FAKE + (7 << 32), FAKE + (8 << 32), ra.RA_F32
+    part.o_batch_stride, part.lse_batch_stride = 1000 * L, 1000 * 16
+    assert lib.ra_attn_fwd_accumulate(ctypes.byref(d), _p(0), _p(1 << 32), _p(2 << 32),
+                                      _p(3 << 32), _p(4 << 32), _p(5 << 32), _p(6 << 32),
+                                      ctypes.byref(part), _p(7 << 32), _p(8 << 32), _p(9 << 32),
+                                      ctypes.c_size_t(1 << 30), None) == ALIAS
+    # only the forward's output can be split
+    assert _bwd(lib, _desc(**ok)) == UNSUP
+    c = (ctypes.c_int8 * 8)()
+    n = (ctypes.c_int64 * 2)()
+    assert lib.ra_classify_tiles(ctypes.byref(_desc(**ok)), _p(3 << 32), _p(4 << 32), _p(5 << 32),
+                                 _p(6 << 32), c, n, _p(9 << 32), ctypes.c_size_t(1 << 30),
+                                 None) == UNSUP
+
+
 def _merge(lib, md, **over):
     args = dict(oa=_p(0), la=_p(1 << 32), ob=_p(2 << 32), lb=_p(3 << 32), oo=_p(4 << 32),
                 lo=_p(5 << 32))
@@ -375,7 +415,7 @@ def test_bwd_mla_alias_spans(lib):
     (dict(head_dim=128, v_head_dim=64), UNSUP),
     (dict(head_dim=192, v_head_dim=128, qkv_dtype=ra.RA_F32), UNSUP),
     (dict(v_head_dim=-1), SHAPE),
-    (dict(reserved=1), SHAPE),
+    (dict(o_split_row=100), SHAPE),                    # split row must be below q_len
     (dict(head_dim=192, v_head_dim=128, v_token_stride=2 * 128 - 8), SHAPE),
 ])
 def test_value_head_dim_support(lib, kw, status):

@@ -185,3 +185,42 @@ def test_ring_inverse_folded_into_last_step_is_bit_identical(cp, window, dtype):
     ro, rl = oracle.attention(q.cpu(), k.cpu(), v.cpu(), ids.cpu(), pos.cpu(), ids.cpu(),
                               pos.cpu(), **kw)
     compare(o_b, l_b, ro, rl, dtype, f"folded inverse cp={cp}")
+
+
+@pytest.mark.parametrize("dtype,out_dtype", [("bf16", torch.bfloat16), ("bf16", torch.float32),
+                                             ("f32", torch.float32)])
+def test_split_output_places_rows_and_leaves_the_gap(dtype, out_dtype):
+    """attn_fwd and attn_fwd_accumulate with a split output write rows below the
+    split at ``out`` and the rest ``o_split_offset`` further on, bit-identical to
+    the unsplit call; the gap between them keeps its contents."""
+    b, tq, tk, hq, hkv, d, row, gap = 2, 300, 260, 8, 2, 64, 97, 41
+    rng = np.random.default_rng(3)
+    from workloads import random_layout
+    qi, qp = random_layout(rng, b, tq, max_segments=3, pad_prob=0.2, pos_offset_max=5)
+    ki, kp = random_layout(rng, b, tk, max_segments=3, pad_prob=0.2, pos_offset_max=40)
+    q, k, v = _dev(*random_qkv(b, tq, tk, hq, hkv, d, dtype, seed=11))
+    qi, qp, ki, kp = _dev(qi, qp, ki, kp)
+    kw = dict(causal=True, window=(120, 0), out_dtype=out_dtype)
+    o_ref, l_ref = bosf.attn_fwd(q, k, v, qi, qp, ki, kp, **kw)
+    big_o = torch.full((b, tq + gap, hq, d), 7.0, dtype=out_dtype, device=DEV)
+    big_l = torch.full((b, tq + gap, hq), 7.0, dtype=torch.float32, device=DEV)
+    bosf.attn_fwd(q, k, v, qi, qp, ki, kp, out=big_o[:, :row], lse=big_l[:, :row],
+                  split=(row, big_o[:, row + gap:], big_l[:, row + gap:]), **kw)
+    assert torch.equal(big_o[:, :row], o_ref[:, :row]) and torch.equal(big_o[:, row + gap:], o_ref[:, row:])
+    assert torch.equal(big_l[:, :row], l_ref[:, :row]) and torch.equal(big_l[:, row + gap:], l_ref[:, row:])
+    assert (big_o[:, row:row + gap] == 7.0).all() and (big_l[:, row:row + gap] == 7.0).all()
+    # accumulate: fold the second half of the keys into the first half's partial
+    h = tk // 2
+    po, pl = bosf.attn_fwd(q, k[:, :h], v[:, :h], qi, qp, ki[:, :h], kp[:, :h], causal=True,
+                           window=(120, 0), out_dtype=torch.float32)
+    ref_o, ref_l = bosf.attn_fwd_accumulate(q, k[:, h:], v[:, h:], qi, qp, ki[:, h:], kp[:, h:],
+                                            po.clone(), pl.clone(), causal=True, window=(120, 0),
+                                            out=torch.empty_like(o_ref), lse=torch.empty_like(l_ref))
+    big_o.fill_(7.0)
+    big_l.fill_(7.0)
+    bosf.attn_fwd_accumulate(q, k[:, h:], v[:, h:], qi, qp, ki[:, h:], kp[:, h:], po, pl,
+                             causal=True, window=(120, 0), out=big_o[:, :row], lse=big_l[:, :row],
+                             split=(row, big_o[:, row + gap:], big_l[:, row + gap:]))
+    assert torch.equal(big_o[:, :row], ref_o[:, :row]) and torch.equal(big_o[:, row + gap:], ref_o[:, row:])
+    assert torch.equal(big_l[:, :row], ref_l[:, :row]) and torch.equal(big_l[:, row + gap:], ref_l[:, row:])
+    assert (big_o[:, row:row + gap] == 7.0).all() and (big_l[:, row:row + gap] == 7.0).all()
