@@ -182,6 +182,9 @@ def main():
     ap.add_argument("--separate-inverse", action="store_true",
                     help="ring: run the inverse reorder of O and LSE as its own pass instead of "
                          "folding it into each rank's last ring step")
+    ap.add_argument("--plan-by-rank", action="store_true",
+                    help="ring: plan steps per rank only (both stripes of a shard finish at the "
+                         "rank's last step with work)")
     ap.add_argument("--no-plan", action="store_true",
                     help="launch every ring step, also those whose blocks hold no visible pair")
     ap.add_argument("--strategy", choices=("ring", "allgather"), default="ring",
@@ -245,15 +248,18 @@ def main():
                 window=w.window, bufs=bufs, step_hook=ev.hook)
     elif w.cp_size > 1:
         bufs = bosf.RingBuffers.like(q, k, ids, w.cp_size)
-        # The ring schedule of this segment layout (visible pairs per rank and
-        # step), computed once outside the timed region like the layout itself;
-        # steps whose blocks hold no visible pair are then not launched.
+        # The ring schedule of this segment layout (visible pairs per rank,
+        # dual-chunk stripe and step), computed once outside the timed region
+        # like the layout itself; steps whose blocks hold no visible pair are
+        # then not launched, and each stripe is finished at its own last step
+        # with work.
         plan = None
         if not args.no_plan and not args.unfused:
             plan = bosf.ring_plan(ids, pos, w.cp_size, w.reorder, w.stripe,
                                   num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                                   head_dim=w.head_dim, dtype=q.dtype, causal=w.causal,
-                                  window=w.window)
+                                  window=w.window,
+                                  halves=w.reorder == "dual_chunk" and not args.plan_by_rank)
             log(f"ring plan (visible pairs per rank x step): {plan.tolist()}")
 
         def step():

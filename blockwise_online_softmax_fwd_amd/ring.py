@@ -153,7 +153,8 @@ def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, ste
 
 
 def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_heads, num_kv_heads,
-              head_dim=128, dtype=torch.bfloat16, causal=True, window=(-1, -1), v_head_dim=None):
+              head_dim=128, dtype=torch.bfloat16, causal=True, window=(-1, -1), v_head_dim=None,
+              halves=False):
     """Visible pairs of every ring step on this segment layout, ``int64 [R, R]``
     on the host (rank, step), from the library's tile classification.
 
@@ -162,24 +163,83 @@ def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_head
     contributes nothing to its rank's softmax ("Causal attention": such blocks
     are skipped), so :func:`ring_forward` given the plan runs only the steps
     with work and lets the last of them write the final output.
+
+    ``halves`` (dual chunk): ``int64 [R, 2, R]`` (rank, stripe, step), the
+    counts of each of the shard's two stripes apart; summed over the stripe
+    axis it is the plain plan.  With it :func:`ring_forward` also finishes each
+    stripe at its own last step with work.
     """
     b, t = ids.shape
     n = t // cp_size
     ids_r = ra.reorder(ids, cp_size, kind, stripe_size)
     pos_r = ra.reorder(pos, cp_size, kind, stripe_size)
-    plan = torch.zeros((cp_size, cp_size), dtype=torch.int64)
+    parts = [slice(0, n // 2), slice(n // 2, n)] if halves else [slice(0, n)]
+    plan = torch.zeros((cp_size, len(parts), cp_size), dtype=torch.int64)
     for r in range(cp_size):
-        rows = slice(r * n, (r + 1) * n)
-        for s in range(cp_size):
-            c = (r - s) % cp_size
-            cols = slice(c * n, (c + 1) * n)
-            _, pairs = ra.classify_tiles(ids_r[:, rows], pos_r[:, rows], ids_r[:, cols],
-                                         pos_r[:, cols], num_q_heads=num_q_heads,
-                                         num_kv_heads=num_kv_heads, head_dim=head_dim,
-                                         dtype=dtype, causal=causal, window=window,
-                                         v_head_dim=v_head_dim)
-            plan[r, s] = int(pairs.sum().item())
-    return plan
+        for j, part in enumerate(parts):
+            rows = slice(r * n + part.start, r * n + part.stop)
+            for s in range(cp_size):
+                c = (r - s) % cp_size
+                cols = slice(c * n, (c + 1) * n)
+                _, pairs = ra.classify_tiles(ids_r[:, rows], pos_r[:, rows], ids_r[:, cols],
+                                             pos_r[:, cols], num_q_heads=num_q_heads,
+                                             num_kv_heads=num_kv_heads, head_dim=head_dim,
+                                             dtype=dtype, causal=causal, window=window,
+                                             v_head_dim=v_head_dim)
+                plan[r, j, s] = int(pairs.sum().item())
+    return plan if halves else plan[:, 0]
+
+
+def _rank_steps_stripes(rank, cp_size, bufs, hplan, o, lse, scale, causal, window, step_hook):
+    """Rank ``rank``'s ring steps on a dual-chunk layout with a per-stripe plan
+    ``hplan [2, R]``: each of the shard's two stripes starts at its first step
+    with work and is finished (written to its original positions in ``o`` /
+    ``lse``) at its last one, so a stripe with no work left costs nothing; at a
+    step where both stripes play the same part one call covers them (a split
+    output at the second stripe when that part is the last)."""
+    t = bufs.q.shape[1]
+    n = t // cp_size
+    h = n // 2
+    rows = slice(rank * n, (rank + 1) * n)
+    q_r, id_r, pos_r = bufs.q[:, rows], bufs.ids[:, rows], bufs.pos[:, rows]
+    halves = [slice(0, h), slice(h, n)]
+    outs = [(o[:, rank * h:(rank + 1) * h], lse[:, rank * h:(rank + 1) * h]),
+            (o[:, (2 * cp_size - 1 - rank) * h:(2 * cp_size - rank) * h],
+             lse[:, (2 * cp_size - 1 - rank) * h:(2 * cp_size - rank) * h])]
+    steps = [[s for s in range(cp_size) if int(hplan[j, s]) > 0] or [cp_size - 1] for j in (0, 1)]
+    for s in range(cp_size):
+        roles = {}
+        for j in (0, 1):
+            if s in steps[j]:
+                roles.setdefault((s == steps[j][0], s == steps[j][-1]), []).append(j)
+        c = (rank - s) % cp_size
+        cols = slice(c * n, (c + 1) * n)
+        kv = (bufs.k[:, cols], bufs.v[:, cols])
+        kmeta = (bufs.ids[:, cols], bufs.pos[:, cols])
+        for (first, last), js in roles.items():
+            qr = slice(0, n) if len(js) == 2 else halves[js[0]]
+            args = (q_r[:, qr], *kv, id_r[:, qr], pos_r[:, qr], *kmeta)
+            split = None
+            if last and len(js) == 2:
+                dst, dst_lse = outs[0]
+                split = (h, outs[1][0], outs[1][1])
+            elif last:
+                dst, dst_lse = outs[js[0]]
+            else:
+                dst, dst_lse = bufs.acc[:, qr], bufs.acc_lse[:, qr]
+            if step_hook:
+                step_hook("attn_fwd", rank, s, True)
+            if first:
+                ra.attn_fwd(*args, scale=scale, causal=causal, window=window, out_dtype=dst.dtype,
+                            out=dst, lse=dst_lse, workspace=bufs.workspace, split=split)
+            else:
+                ra.attn_fwd_accumulate(*args, bufs.acc[:, qr], bufs.acc_lse[:, qr], scale=scale,
+                                       causal=causal, window=window,
+                                       out=None if not last else dst,
+                                       lse=None if not last else dst_lse,
+                                       workspace=bufs.workspace, split=split)
+            if step_hook:
+                step_hook("attn_fwd", rank, s, False)
 
 
 def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, scale=None,
@@ -193,7 +253,9 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     ``ranks`` a subset of ranks, only those shards of the output are computed
     (the others are left as they were in ``bufs``).  With ``plan`` (from
     :func:`ring_plan` on the same layout and mask) the fused path runs only
-    the steps whose blocks hold visible pairs.
+    the steps whose blocks hold visible pairs; a per-stripe plan
+    (``halves=True``) also lets each of a dual-chunk shard's two stripes stop
+    at its own last step with work.
 
     With the dual-chunk reorder, the fused path and every rank run
     (``fuse_inverse``), the inverse reorder is folded into each rank's last
@@ -227,7 +289,15 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
         lse = torch.empty_like(bufs.lse)
     n = q.shape[1] // cp_size
     h = n // 2
+    stripes = plan is not None and plan.dim() == 3
+    if stripes and not direct:
+        plan = plan.sum(1)          # per-stripe counts folded back into the plain plan
+        stripes = False
     for r in (range(cp_size) if ranks is None else ranks):
+        if stripes:
+            _rank_steps_stripes(r, cp_size, bufs, plan[r], o, lse, scale, causal, window,
+                                step_hook)
+            continue
         steps = None
         if plan is not None and fused:
             steps = [s for s in range(cp_size) if int(plan[r, s]) > 0] or [cp_size - 1]

@@ -167,9 +167,10 @@ def test_ring_with_plan_is_bit_identical():
                                              (8, (300, 0), "bf16"), (4, (500, 0), "f32")])
 def test_ring_inverse_folded_into_last_step_is_bit_identical(cp, window, dtype):
     """The dual-chunk inverse reorder folded into each rank's last ring step
-    (one launch per stripe, writing O and the LSE at their original positions)
-    gives the same bits as the separate inverse-reorder pass, with and without
-    the plan of steps."""
+    (a split output writing O and the LSE at their original positions) gives
+    the same bits as the separate inverse-reorder pass, with and without the
+    plan of steps, and with the per-stripe plan (each stripe finished at its
+    own last step with work)."""
     b, t, hq, hkv = 2, 4096, 8, 2
     ids, pos = packed_metadata(b, t, 2, 1500)
     q, k, v = _dev(*random_qkv(b, t, t, hq, hkv, 64, dtype, seed=cp * 7 + 1))
@@ -180,8 +181,13 @@ def test_ring_inverse_folded_into_last_step_is_bit_identical(cp, window, dtype):
     plan = bosf.ring_plan(ids, pos, cp, "dual_chunk", 1, num_q_heads=hq, num_kv_heads=hkv,
                           head_dim=64, dtype=q.dtype, **kw)
     o_c, l_c = bosf.ring_forward(q, k, v, ids, pos, cp, "dual_chunk", 1, plan=plan, **kw)
+    hplan = bosf.ring_plan(ids, pos, cp, "dual_chunk", 1, num_q_heads=hq, num_kv_heads=hkv,
+                           head_dim=64, dtype=q.dtype, halves=True, **kw)
+    assert torch.equal(hplan.sum(1), plan)
+    o_d, l_d = bosf.ring_forward(q, k, v, ids, pos, cp, "dual_chunk", 1, plan=hplan, **kw)
     assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
     assert torch.equal(o_a, o_c) and torch.equal(l_a, l_c)
+    assert torch.equal(o_a, o_d) and torch.equal(l_a, l_d)
     ro, rl = oracle.attention(q.cpu(), k.cpu(), v.cpu(), ids.cpu(), pos.cpu(), ids.cpu(),
                               pos.cpu(), **kw)
     compare(o_b, l_b, ro, rl, dtype, f"folded inverse cp={cp}")
