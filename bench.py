@@ -8,9 +8,12 @@ of the 4 shards, 4 ring steps -- attn_fwd for the shard's own chunk, then
 attn_fwd_accumulate for the 3 chunks that arrive next, each folding its block
 into the running fp32 partial in its epilogue (the merge of the ring update,
 fused; ``--unfused`` runs attn_fwd + attn_merge instead); inverse reorder of O
-and LSE, folded into each rank's last ring step (a dual-chunk shard is two
-contiguous stripes of the sequence, so that step runs once per stripe and
-writes to the original positions).  All four shards are computed, so a step
+and LSE, folded into the forward's stores (a dual-chunk shard is two
+contiguous stripes of the sequence, written with a split output at their
+original positions).  A plan computed once per layout skips the ring steps
+whose blocks hold no visible pair and finishes each stripe at its own last
+step with work (``--plan-by-rank``, ``--no-plan`` for the coarser schedules).
+All four shards are computed, so a step
 is the complete forward of B=2 x 65536 tokens; FLOPs count only visible pairs
 (4 * head_dim * Hq per pair).  attn_merge and the inverse reorder kernel are
 also timed on their own at the step's shapes.
