@@ -336,7 +336,13 @@ def main():
         n = t // w.cp_size
         reorder_ms = sum(ev.ms("reorder")) / args.steps
         inv_ms = sum(ev.ms("inverse_reorder")) / args.steps
-        fwd_bytes = 2 * (q.numel() * 2 + 2 * k.numel() * 2 + 2 * ids.numel() * 4)
+        # Q is read in place (no reordered copy) when the per-stripe plan never
+        # runs both stripes of a shard in one call
+        q_moved = (allgather or args.unfused or args.separate_inverse or plan is None
+                   or bosf.needs_reordered_q(plan, w.cp_size))
+        fwd_bytes = 2 * ((q.numel() * 2 if q_moved else 0) + 2 * k.numel() * 2
+                         + 2 * ids.numel() * 4)
+        detail["q_reordered"] = bool(q_moved)
         inv_bytes = 2 * (q.numel() * 2 + b * t * hq * 4)
         detail.update({
             "strategy": ("all-gather: each shard against the whole K/V, no merge" if allgather
@@ -351,9 +357,9 @@ def main():
             detail.update({"inverse_reorder_ms_per_step": inv_ms,
                            "inverse_reorder_GBs": inv_bytes / (inv_ms / 1000.0) / 1e9})
         else:
-            detail["inverse_reorder"] = ("folded into each rank's last ring step: it runs once "
-                                         "per dual-chunk stripe and writes O and the LSE at "
-                                         "their original positions")
+            detail["inverse_reorder"] = ("folded into the forward's stores: each dual-chunk "
+                                         "stripe's O and LSE are written at their original "
+                                         "positions (split output)")
             # the inverse reorder kernel on its own, on the step's O and LSE
             # (outside the step), for its HBM rate
             o_s, l_s = out["o"], out["lse"]

@@ -29,4 +29,5 @@ from .ringattn import (  # noqa: F401
     version,
     workspace_size,
 )
-from .ring import RingBuffers, allgather_forward, ring_forward, ring_plan  # noqa: F401
+from .ring import (RingBuffers, allgather_forward, needs_reordered_q, ring_forward,  # noqa: F401
+                   ring_plan)

@@ -68,8 +68,9 @@ class RingBuffers:
         )
 
 
-def reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs: RingBuffers):
-    ra.reorder(q, cp_size, kind, stripe_size, out=bufs.q)
+def reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs: RingBuffers, with_q=True):
+    if with_q:
+        ra.reorder(q, cp_size, kind, stripe_size, out=bufs.q)
     ra.reorder(k, cp_size, kind, stripe_size, out=bufs.k)
     ra.reorder(v, cp_size, kind, stripe_size, out=bufs.v)
     ra.reorder(ids, cp_size, kind, stripe_size, out=bufs.ids)
@@ -190,7 +191,34 @@ def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_head
     return plan if halves else plan[:, 0]
 
 
-def _rank_steps_stripes(rank, cp_size, bufs, hplan, o, lse, scale, causal, window, step_hook):
+def _stripe_schedule(hplan_r, cp_size):
+    """Per ring step, the launches of one rank under a per-stripe plan
+    ``[2, R]``: ``{(first, last): [stripes]}`` -- a stripe starts at its first
+    step with work and finishes at its last (the last step if it has none)."""
+    steps = [[s for s in range(cp_size) if int(hplan_r[j, s]) > 0] or [cp_size - 1]
+             for j in (0, 1)]
+    out = []
+    for s in range(cp_size):
+        roles = {}
+        for j in (0, 1):
+            if s in steps[j]:
+                roles.setdefault((s == steps[j][0], s == steps[j][-1]), []).append(j)
+        out.append(roles)
+    return out
+
+
+def needs_reordered_q(plan, cp_size):
+    """False when a per-stripe plan ``[R, 2, R]`` never runs both stripes of a
+    shard in one call: every call then reads one stripe, a contiguous range
+    of the original sequence, and Q needs no reordered copy."""
+    if plan is None or plan.dim() != 3:
+        return True
+    return any(len(js) == 2 for r in range(cp_size)
+               for roles in _stripe_schedule(plan[r], cp_size) for js in roles.values())
+
+
+def _rank_steps_stripes(rank, cp_size, bufs, hplan, o, lse, scale, causal, window, step_hook,
+                        q_orig=None):
     """Rank ``rank``'s ring steps on a dual-chunk layout with a per-stripe plan
     ``hplan [2, R]``: each of the shard's two stripes starts at its first step
     with work and is finished (written to its original positions in ``o`` /
@@ -203,22 +231,20 @@ def _rank_steps_stripes(rank, cp_size, bufs, hplan, o, lse, scale, causal, windo
     rows = slice(rank * n, (rank + 1) * n)
     q_r, id_r, pos_r = bufs.q[:, rows], bufs.ids[:, rows], bufs.pos[:, rows]
     halves = [slice(0, h), slice(h, n)]
-    outs = [(o[:, rank * h:(rank + 1) * h], lse[:, rank * h:(rank + 1) * h]),
-            (o[:, (2 * cp_size - 1 - rank) * h:(2 * cp_size - rank) * h],
-             lse[:, (2 * cp_size - 1 - rank) * h:(2 * cp_size - rank) * h])]
-    steps = [[s for s in range(cp_size) if int(hplan[j, s]) > 0] or [cp_size - 1] for j in (0, 1)]
-    for s in range(cp_size):
-        roles = {}
-        for j in (0, 1):
-            if s in steps[j]:
-                roles.setdefault((s == steps[j][0], s == steps[j][-1]), []).append(j)
+    # the shard's stripes in the original order: stripe r, then stripe 2R-1-r
+    orig = [slice(rank * h, (rank + 1) * h),
+            slice((2 * cp_size - 1 - rank) * h, (2 * cp_size - rank) * h)]
+    outs = [(o[:, orig[0]], lse[:, orig[0]]), (o[:, orig[1]], lse[:, orig[1]])]
+    for s, roles in enumerate(_stripe_schedule(hplan, cp_size)):
         c = (rank - s) % cp_size
         cols = slice(c * n, (c + 1) * n)
         kv = (bufs.k[:, cols], bufs.v[:, cols])
         kmeta = (bufs.ids[:, cols], bufs.pos[:, cols])
         for (first, last), js in roles.items():
             qr = slice(0, n) if len(js) == 2 else halves[js[0]]
-            args = (q_r[:, qr], *kv, id_r[:, qr], pos_r[:, qr], *kmeta)
+            # one stripe: its Q rows read in place from the original order
+            qx = q_orig[:, orig[js[0]]] if q_orig is not None and len(js) == 1 else q_r[:, qr]
+            args = (qx, *kv, id_r[:, qr], pos_r[:, qr], *kmeta)
             split = None
             if last and len(js) == 2:
                 dst, dst_lse = outs[0]
@@ -277,13 +303,17 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
                             {"v_head_dim": v.shape[3]})
         bufs.workspace = torch.empty(max(1, ra.workspace_size(desc)), dtype=torch.uint8,
                                      device=q.device)
-    if step_hook:
-        step_hook("reorder", -1, -1, True)
-    reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs)
-    if step_hook:
-        step_hook("reorder", -1, -1, False)
     direct = (fuse_inverse and fused and ranks is None and cp_size > 1
               and ra._kind_code(kind) == ra.DUAL_CHUNK)
+    # With a per-stripe plan whose calls each read one stripe, Q is read in
+    # place (the reordered copy of Q is never made).
+    q_in_place = direct and plan is not None and plan.dim() == 3 and not needs_reordered_q(
+        plan, cp_size)
+    if step_hook:
+        step_hook("reorder", -1, -1, True)
+    reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs, with_q=not q_in_place)
+    if step_hook:
+        step_hook("reorder", -1, -1, False)
     if direct:
         o = torch.empty_like(bufs.o)
         lse = torch.empty_like(bufs.lse)
@@ -296,7 +326,7 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     for r in (range(cp_size) if ranks is None else ranks):
         if stripes:
             _rank_steps_stripes(r, cp_size, bufs, plan[r], o, lse, scale, causal, window,
-                                step_hook)
+                                step_hook, q if q_in_place else None)
             continue
         steps = None
         if plan is not None and fused:
