@@ -249,8 +249,14 @@ def test_accumulate_in_place_leaves_untouched_tiles_bit_exact():
 
 def _run_workload(w, q, k, v, ids, pos):
     if w.cp_size > 1:
+        # the benchmark's schedule: per-stripe plan (Q read in place when every
+        # call covers one stripe), inverse reorder folded into the stores
+        plan = bosf.ring_plan(ids, pos, w.cp_size, w.reorder, w.stripe,
+                              num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                              head_dim=w.head_dim, dtype=q.dtype, causal=w.causal,
+                              window=w.window, halves=w.reorder == "dual_chunk")
         return bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe,
-                                 causal=w.causal, window=w.window)
+                                 causal=w.causal, window=w.window, plan=plan)
     return bosf.attn_fwd(q, k, v, ids, pos, ids, pos, causal=w.causal, window=w.window)
 
 
