@@ -257,7 +257,7 @@ ra_status run_schedule(const ra_attn_desc *d, const Resolved &r, const ra::Sched
 
 extern "C" {
 
-const char *ra_version(void) { return "libringattn 0.1.0 (gfx950)"; }
+const char *ra_version(void) { return "libringattn 0.2.0 (gfx950)"; }
 
 const char *ra_status_string(ra_status s) {
   switch (s) {
