@@ -194,6 +194,31 @@ bool rows_overlap(const void *a, int64_t Ta, int64_t la, const void *b, int64_t 
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// A buffer and its extent in bytes, for the overlap checks.
+struct Span {
+  const void *p;
+  size_t n;
+};
+
+// True if any of the n spans overlaps [x, x + xn).
+bool overlaps_any(const void *x, size_t xn, const Span *spans, int n) {
+  for (int i = 0; i < n; ++i)
+    if (overlaps(x, xn, spans[i].p, spans[i].n)) return true;
+  return false;
+}
+
+// Extents of the four int32 metadata buffers [B, T] at their batch strides.
+struct MetaSpans {
+  Span s[4];
+};
+MetaSpans meta_spans(const ra_attn_desc *d, const int64_t qm_bs, const int64_t km_bs,
+                     const int32_t *qid, const int32_t *qpos, const int32_t *kid,
+                     const int32_t *kpos) {
+  const size_t qn = span_bytes(d->batch, qm_bs, d->q_len, 4);
+  const size_t kn = span_bytes(d->batch, km_bs, d->kv_len, 4);
+  return MetaSpans{{{qid, qn}, {qpos, qn}, {kid, kn}, {kpos, kn}}};
+}
+
 ra_status check_meta(const ra_attn_desc *d, const Resolved &r, const int32_t *qid,
                      const int32_t *qpos, const int32_t *kid, const int32_t *kpos) {
   if (d->batch > 0 && d->q_len > 0 && (!qid || !qpos))
@@ -347,6 +372,7 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
     return fail(RA_ERR_ALIAS, "o / lse overlap an input or each other");
   int64_t acc_o_bs = 0, acc_lse_bs = 0;
   bool in_place = false;
+  Span acc_span{nullptr, 0}, acc_lspan{nullptr, 0};
   if (acc) {
     if (!dtype_ok(acc->dtype)) return fail(RA_ERR_DTYPE, "unknown partial dtype %d", acc->dtype);
     if (acc->o_batch_stride < 0 || acc->lse_batch_stride < 0)
@@ -368,10 +394,21 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
     if (!in_place && (overlaps(o, o_span, acc->o, a_span) || overlaps(lse, l_span, acc->lse, al_span) ||
                       overlaps(o, o_span, acc->lse, al_span) || overlaps(lse, l_span, acc->o, a_span)))
       return fail(RA_ERR_ALIAS, "o / lse overlap the partial without being it");
+    acc_span = Span{acc->o, a_span};
+    acc_lspan = Span{acc->lse, al_span};
   }
+  const MetaSpans ms = meta_spans(d, r.qm_bs, r.km_bs, qid, qpos, kid, kpos);
+  if (overlaps_any(o, o_span, ms.s, 4) || overlaps_any(lse, l_span, ms.s, 4))
+    return fail(RA_ERR_ALIAS, "o / lse overlap the segment ids or positions");
   if (!has_q) return RA_OK;
   st = check_workspace(d, r, workspace, workspace_bytes);
   if (st != RA_OK) return st;
+  {
+    const Span used[11] = {{q, q_span}, {k, kv_span}, {v, v_span}, {o, o_span}, {lse, l_span},
+                           acc_span, acc_lspan, ms.s[0], ms.s[1], ms.s[2], ms.s[3]};
+    if (overlaps_any(workspace, layout_of(d, r).total, used, 11))
+      return fail(RA_ERR_ALIAS, "the workspace overlaps an input or output");
+  }
 
   hipStream_t s = (hipStream_t)stream;
   const ra::WorkspaceLayout L = layout_of(d, r);
@@ -506,6 +543,16 @@ ra_status ra_classify_tiles(const ra_attn_desc *d, const int32_t *qid, const int
   if (d->batch == 0) return RA_OK;
   st = check_workspace(d, r, workspace, workspace_bytes);
   if (st != RA_OK) return st;
+  {
+    const MetaSpans ms = meta_spans(d, r.qm_bs, r.km_bs, qid, qpos, kid, kpos);
+    const size_t cn = (size_t)d->batch * r.nqt * r.nkt, pn = (size_t)d->batch * 8;
+    if (overlaps_any(classes, cn, ms.s, 4) || overlaps_any(visible_pairs, pn, ms.s, 4) ||
+        overlaps(classes, cn, visible_pairs, pn))
+      return fail(RA_ERR_ALIAS, "classes / visible_pairs overlap the metadata or each other");
+    const Span used[6] = {{classes, cn}, {visible_pairs, pn}, ms.s[0], ms.s[1], ms.s[2], ms.s[3]};
+    if (overlaps_any(workspace, layout_of(d, r).total, used, 6))
+      return fail(RA_ERR_ALIAS, "the workspace overlaps an input or output");
+  }
   hipStream_t s = (hipStream_t)stream;
   const ra::Schedule sch = carve(workspace, layout_of(d, r));
   st = run_schedule(d, r, sch, qid, qpos, kid, kpos, classes, s);
@@ -715,6 +762,10 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   if (qv_same ? rows_overlap(dq, Tq, Lq * g, dv, Tk, Lv * g, B, r.q_bs * g, r.q_ts * g)
               : overlaps(dq, dq_span, dv, dvv_span))
     return fail(RA_ERR_ALIAS, "dq overlaps dv");
+  const MetaSpans ms = meta_spans(d, r.qm_bs, r.km_bs, qid, qpos, kid, kpos);
+  for (int i = 0; i < 3; ++i)
+    if (overlaps_any(outs[i], out_span[i], ms.s, 4))
+      return fail(RA_ERR_ALIAS, "a gradient buffer overlaps the segment ids or positions");
   if (!has_q && !has_k) return RA_OK;
   const ra::BwdLayout L = bwd_layout_of(d, r, bs);
   if (L.total > 0 && !workspace)
@@ -722,6 +773,14 @@ ra_status ra_attn_bwd(const ra_attn_desc *d, const void *q, const void *k, const
   if (workspace_bytes < L.total)
     return fail(RA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
   if (!aligned(workspace, 256)) return fail(RA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  {
+    const Span used[13] = {{q, q_span},   {k, kv_span},   {v, v_span},     {o, o_span},
+                           {lse, l_span}, {dout, do_span}, {dq, dq_span},  {dk, dkv_span},
+                           {dv, dvv_span}, ms.s[0],        ms.s[1],        ms.s[2],
+                           ms.s[3]};
+    if (overlaps_any(workspace, L.total, used, 13))
+      return fail(RA_ERR_ALIAS, "the workspace overlaps an input or output");
+  }
 
   hipStream_t s = (hipStream_t)stream;
   char *ws = (char *)workspace;

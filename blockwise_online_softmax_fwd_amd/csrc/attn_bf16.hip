@@ -124,9 +124,6 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(PackParams p) {
 
 // ----------------------------------------------------------------------------- forward
 
-// Branch-free visibility test of one key against the lane's query.  With
-// non-negative ids and positions, the pair is visible iff kid == qkey (qkey is
-// -1 for a padding query) and lo <= qpos - kpos <= hi.
 // Largest of x over lanes l and l ^ 32 (the two halves of a query's keys),
 // exchanged with v_permlane32_swap rather than through LDS.
 __device__ __forceinline__ float pair_max(float x) {
@@ -142,6 +139,11 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
 }
 
+// Branch-free visibility test of one key against the lane's query: the pair
+// is visible iff kid == qkey and lo <= qpos - kpos <= hi.  A padding query
+// (id 0) gets the empty range lo = 1 > hi = 0, so it sees no key whatever the
+// ids; a padding key (id 0) never equals a non-padding query's id.  Positions
+// are non-negative, so qpos - kpos cannot overflow.
 struct LaneMask {
   int qkey, qpos, lo, hi;
   __device__ __forceinline__ bool operator()(int kid, int kpos) const {
@@ -277,11 +279,15 @@ attn_fwd_bf16_kernel(AttnParams p) {
   LaneMask lm;
   {
     const int my_qid = qvalid ? p.qid[b * p.qm_bs + tq] : 0;
-    lm.qkey = my_qid != 0 ? my_qid : -1;
+    lm.qkey = my_qid;
     lm.qpos = qvalid ? p.qpos[b * p.qm_bs + tq] : 0;
     lm.lo = p.mask.causal ? 0 : INT_MIN;
     if (p.mask.wr >= 0) lm.lo = max(lm.lo, -p.mask.wr);
     lm.hi = p.mask.wl >= 0 ? p.mask.wl : INT_MAX;
+    if (my_qid == 0) {   // padding (or out-of-range) query: empty window
+      lm.lo = 1;
+      lm.hi = 0;
+    }
   }
   const bool ragged = (p.tk % BN) != 0;
   auto entry_tile = [&](int it) { return (int)(lst[it] & 0x7fffffffu); };

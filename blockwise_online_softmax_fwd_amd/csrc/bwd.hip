@@ -240,8 +240,9 @@ __global__ __launch_bounds__(256) void bwd_pack_q_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------------------- masks
 
-// Visibility of one key against the lane's query (dQ pass): kid == qkey (-1
-// for a padding query) and lo <= qpos - kpos <= hi.
+// Visibility of one key against the lane's query (dQ pass): kid == qkey and
+// lo <= qpos - kpos <= hi; a padding query gets the empty range lo > hi, so
+// it sees no key whatever the ids.
 struct LaneMask {
   int qkey, qpos, lo, hi;
   __device__ __forceinline__ bool operator()(int kid, int kpos) const {
@@ -250,8 +251,9 @@ struct LaneMask {
   }
 };
 
-// Visibility of one query against the lane's key (dK/dV pass): qid == kkey (-1
-// for a padding or missing key) and lo <= qpos - kpos <= hi.
+// Visibility of one query against the lane's key (dK/dV pass): qid == kkey
+// and lo <= qpos - kpos <= hi; a padding or missing key gets the empty range
+// lo > hi, so no query sees it whatever the ids.
 struct KeyMask {
   int kkey, kpos, lo, hi;
   __device__ __forceinline__ bool operator()(int qid, int qpos) const {
@@ -349,9 +351,13 @@ bwd_dq_kernel(BwdParams p) {
   LaneMask lm;
   {
     const int my_qid = qvalid ? p.qid[b * p.qm_bs + tq] : 0;
-    lm.qkey = my_qid != 0 ? my_qid : -1;
+    lm.qkey = my_qid;
     lm.qpos = qvalid ? p.qpos[b * p.qm_bs + tq] : 0;
     mask_bounds(p.mask, lm.lo, lm.hi);
+    if (my_qid == 0) {   // padding (or out-of-range) query: empty window
+      lm.lo = 1;
+      lm.hi = 0;
+    }
   }
   const bool ragged = (p.tk % BN) != 0;
   auto entry_tile = [&](int it) { return (int)(lst[it] & 0x7fffffffu); };
@@ -567,9 +573,13 @@ bwd_dkdv_kernel(BwdParams p) {
   KeyMask km;
   {
     const int my_kid = kvalid ? p.kid[b * p.km_bs + key] : 0;
-    km.kkey = my_kid != 0 ? my_kid : -1;
+    km.kkey = my_kid;
     km.kpos = kvalid ? p.kpos[b * p.km_bs + key] : 0;
     mask_bounds(p.mask, km.lo, km.hi);
+    if (my_kid == 0) {   // padding (or out-of-range) key: empty window
+      km.lo = 1;
+      km.hi = 0;
+    }
   }
   const float c2 = p.scale_log2;
 

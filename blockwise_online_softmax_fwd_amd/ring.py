@@ -153,11 +153,69 @@ def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, ste
             step_hook("attn_fwd", rank, s, False)
 
 
+def _layout_fingerprint(ids, pos):
+    """Two 64-bit position-weighted sums of the segment ids and positions
+    (computed where the tensors live; wrapping int64 arithmetic), to tell one
+    segment layout from another."""
+    t = ids.shape[1]
+    w = torch.arange(1, t + 1, device=ids.device, dtype=torch.int64)
+    a = ids.to(torch.int64) * 1000003 + pos.to(torch.int64) * 7919 + 1
+    h1 = (a * (w * 2654435761 + 97)).sum(dim=1)
+    h2 = ((a ^ (a >> 7)) * (w * w + 31337)).sum(dim=1)
+    return tuple(int(x) for x in torch.stack([h1, h2], 1).flatten().tolist())
+
+
+class RingPlan:
+    """The ring schedule of one segment layout and mask (see :func:`ring_plan`).
+
+    ``counts``: host ``int64 [R, R]`` (rank, step), or ``[R, 2, R]`` (rank,
+    dual-chunk stripe, step) -- the visible pairs of every block.  The plan
+    records what it was computed from (shape, shard count, reorder, mask and a
+    fingerprint of the ids and positions); :func:`ring_forward` refuses a plan
+    made for anything else, since it would skip blocks that hold visible
+    pairs.  Tensors already checked (same storage, unmodified since) are not
+    fingerprinted again, so the steady state adds no device synchronisation.
+    """
+
+    def __init__(self, counts, ids, pos, cp_size, kind, stripe_size, causal, window):
+        self.counts = counts
+        self.meta = (tuple(ids.shape), int(cp_size), ra._kind_code(kind),
+                     int(stripe_size) if ra._kind_code(kind) == ra.STRIPED else 1,
+                     bool(causal), (int(window[0]), int(window[1])))
+        self.fingerprint = _layout_fingerprint(ids, pos)
+        self._seen = {self._token(ids, pos)}
+
+    @staticmethod
+    def _token(ids, pos):
+        return (ids.data_ptr(), ids._version, tuple(ids.stride()), pos.data_ptr(), pos._version,
+                tuple(pos.stride()), str(ids.device))
+
+    def check(self, ids, pos, cp_size, kind, stripe_size, causal, window):
+        """Raise ValueError unless the plan was made for this layout and mask."""
+        meta = (tuple(ids.shape), int(cp_size), ra._kind_code(kind),
+                int(stripe_size) if ra._kind_code(kind) == ra.STRIPED else 1,
+                bool(causal), (int(window[0]), int(window[1])))
+        if meta != self.meta:
+            raise ValueError(f"ring plan made for {self.meta} (shape, shards, reorder, stripe, "
+                             f"causal, window), used with {meta}")
+        tok = self._token(ids, pos)
+        if tok in self._seen:
+            return
+        if _layout_fingerprint(ids, pos) != self.fingerprint:
+            raise ValueError("ring plan made for other segment ids / positions")
+        self._seen.add(tok)
+
+    def dim(self):
+        return self.counts.dim()
+
+
 def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_heads, num_kv_heads,
               head_dim=128, dtype=torch.bfloat16, causal=True, window=(-1, -1), v_head_dim=None,
               halves=False):
-    """Visible pairs of every ring step on this segment layout, ``int64 [R, R]``
-    on the host (rank, step), from the library's tile classification.
+    """The ring schedule of this segment layout: visible pairs of every ring
+    step, ``counts int64 [R, R]`` on the host (rank, step), from the library's
+    tile classification, wrapped in a :class:`RingPlan` that remembers the
+    layout and mask it belongs to.
 
     The counts depend only on the segment ids and positions, so one plan
     serves every forward on the same layout.  A block with no visible pair
@@ -165,9 +223,9 @@ def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_head
     are skipped), so :func:`ring_forward` given the plan runs only the steps
     with work and lets the last of them write the final output.
 
-    ``halves`` (dual chunk): ``int64 [R, 2, R]`` (rank, stripe, step), the
-    counts of each of the shard's two stripes apart; summed over the stripe
-    axis it is the plain plan.  With it :func:`ring_forward` also finishes each
+    ``halves`` (dual chunk): counts ``int64 [R, 2, R]`` (rank, stripe, step),
+    each of the shard's two stripes apart; summed over the stripe axis they
+    are the plain plan.  With it :func:`ring_forward` also finishes each
     stripe at its own last step with work.
     """
     b, t = ids.shape
@@ -188,7 +246,8 @@ def ring_plan(ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, num_q_head
                                              dtype=dtype, causal=causal, window=window,
                                              v_head_dim=v_head_dim)
                 plan[r, j, s] = int(pairs.sum().item())
-    return plan if halves else plan[:, 0]
+    return RingPlan(plan if halves else plan[:, 0], ids, pos, cp_size, kind, stripe_size, causal,
+                    window)
 
 
 def _stripe_schedule(hplan_r, cp_size):
@@ -211,6 +270,8 @@ def needs_reordered_q(plan, cp_size):
     """False when a per-stripe plan ``[R, 2, R]`` never runs both stripes of a
     shard in one call: every call then reads one stripe, a contiguous range
     of the original sequence, and Q needs no reordered copy."""
+    if isinstance(plan, RingPlan):
+        plan = plan.counts
     if plan is None or plan.dim() != 3:
         return True
     return any(len(js) == 2 for r in range(cp_size)
@@ -293,6 +354,11 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     """
     if q.shape[1] != k.shape[1]:
         raise ValueError("the ring driver runs self-attention (Tq == Tk)")
+    if plan is not None:
+        if not isinstance(plan, RingPlan):
+            raise TypeError("plan must come from ring_plan()")
+        plan.check(ids, pos, cp_size, kind, stripe_size, causal, window)
+        plan = plan.counts
     if bufs is None:
         bufs = RingBuffers.like(q, k, ids, cp_size, partial_dtype, out_dtype, v=v)
     if bufs.workspace is None:

@@ -114,7 +114,7 @@ typedef struct ra_attn_desc {
   int32_t kv_len;         /* Tk >= 0                                           */
   int32_t num_q_heads;    /* Hq >= 1                                           */
   int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0                           */
-  int32_t head_dim;       /* D: 64 or 128                                      */
+  int32_t head_dim;       /* D of q and k: 64, 128, or 192 with v_head_dim 128 */
   int32_t qkv_dtype;      /* ra_dtype of q, k and v                            */
   int32_t out_dtype;      /* ra_dtype of o                                     */
   float scale;            /* score scale, finite and > 0; head_dim^-1/2 in [TUT] s3 */
@@ -148,9 +148,11 @@ const char *ra_last_error(void);
  * Host-only support query (the role of FusedAttnHelper's backend query in
  * [CPP]): RA_OK if ra_attn_fwd implements this description, otherwise the
  * status it would return.  Supported: bf16 q/k/v (MFMA path) or fp32 q/k/v,
- * D in {64, 128}, bf16 or fp32 output, any Hq/Hkv group size, any lengths up to
- * 2^21 key tokens per call (2^20 for fp32), and the (head_dim, v_head_dim)
- * pairs above.  Segment ids and positions must be non-negative.  Makes no HIP call.
+ * (head_dim, v_head_dim) of (64, 64) or (128, 128), and in bf16 also (192, 128),
+ * bf16 or fp32 output, any Hq/Hkv group size, any lengths up to 2^21 key tokens
+ * per call (2^20 for fp32).  Segment ids may be any int32 value (0 marks
+ * padding; ids compare only within one batch row); positions must be
+ * non-negative (the device does not check them).  Makes no HIP call.
  */
 ra_status ra_check_support(const ra_attn_desc *desc);
 
@@ -176,10 +178,12 @@ ra_status ra_attn_fwd_workspace_size(const ra_attn_desc *desc, size_t *bytes);
  *                               scores; a query with no visible key gets
  *                               o = 0 and lse = -inf.
  * Both are fully overwritten.  q, k, v, o: 16-byte aligned, batch strides a
- * multiple of 16 bytes; metadata and lse 4-byte aligned.  o must not overlap
- * q, k or v.  workspace: device memory of at least
- * ra_attn_fwd_workspace_size() bytes, 256-byte aligned, owned by the caller,
- * overwritten; calls that share a workspace must be ordered on one stream.
+ * multiple of 16 bytes; metadata and lse 4-byte aligned.  o and lse must not
+ * overlap q, k, v, the segment ids or positions, or each other.  workspace:
+ * device memory of at least ra_attn_fwd_workspace_size() bytes, 256-byte
+ * aligned, owned by the caller, overwritten, overlapping no other argument;
+ * calls that share a workspace must be ordered on one stream.  Every overlap
+ * named here is RA_ERR_ALIAS.
  */
 ra_status ra_attn_fwd(const ra_attn_desc *desc, const void *q, const void *k, const void *v,
                       const int32_t *q_segment_ids, const int32_t *q_segment_pos,
@@ -236,7 +240,8 @@ ra_status ra_profile_next_kernel(ra_event_t start, ra_event_t stop);
  * ceil(Tk/bn)] with RA_TILE_* values (a tile's class is decided over its
  * in-range pairs only); visible_pairs: int64 [B].  Either output may be NULL.
  * Only the metadata fields of desc matter (dtypes and head_dim select the tile
- * shape).  Same workspace rules as ra_attn_fwd.
+ * shape).  Same workspace rules as ra_attn_fwd; classes and visible_pairs
+ * must not overlap the metadata, the workspace or each other (RA_ERR_ALIAS).
  */
 ra_status ra_classify_tiles(const ra_attn_desc *desc, const int32_t *q_segment_ids,
                             const int32_t *q_segment_pos, const int32_t *kv_segment_ids,
@@ -294,7 +299,8 @@ ra_status ra_attn_merge(const ra_merge_desc *desc, const void *o_a, const float 
  *          scheduling.
  * q, k, v, o, dout, dq, dk, dv: 16-byte aligned, batch strides multiples of 16
  * bytes; lse and metadata 4-byte aligned.  dq, dk and dv must not overlap each
- * other or any input (RA_ERR_ALIAS).  workspace: device memory of at least
+ * other or any input, metadata included, and the workspace must overlap no
+ * argument (RA_ERR_ALIAS).  workspace: device memory of at least
  * ra_attn_bwd_workspace_size() bytes, 256-byte aligned, owned by the caller,
  * overwritten (both passes' tile lists, rowsum(dout*o), and packed copies of
  * q/dout and k/v tiles in the layouts the kernels read); calls that share a

@@ -148,31 +148,34 @@ def _take_keys(x, b, cand, g):
     return f64(np.asarray(x)[b, cand, g, :])
 
 
-def attention_rows(q, k, v, qid, qpos, kid, kpos, rows, scale=None, causal=True,
-                   window=(-1, -1)):
-    """Exact attention for selected query rows only.
+def _gather_rows(x, rows):
+    """fp64 ``[len(rows), H, D]``: the (batch, token) rows of a [B, T, H, D] array-like."""
+    if hasattr(x, "detach"):
+        import torch
+        bi = torch.tensor([r[0] for r in rows], dtype=torch.int64, device=x.device)
+        ti = torch.tensor([r[1] for r in rows], dtype=torch.int64, device=x.device)
+        return f64(x[bi, ti])
+    a = np.asarray(x)
+    return f64(a[[r[0] for r in rows], [r[1] for r in rows]])
 
-    ``rows`` is a sequence of (batch, token) pairs.  Returns fp64 O
-    ``[n, Hq, D]`` and LSE ``[n, Hq]`` for those rows, every head.  Used where
-    the full output is too large for the oracle; K and V may be any array-like
-    (they are only indexed, then widened).
+
+def _rows_forward(qrows, k, v, qid, qpos, kid, kpos, rows, scale, causal=True, window=(-1, -1)):
+    """Exact attention of single query rows, one plain softmax per row and head.
+
+    ``qrows[n]`` ``[Hq, D]`` is the query at ``rows[n] = (b, i)``; the metadata
+    are int64 arrays ``[B, T]``; k, v are indexable ``[B, Tk, Hkv, D(v)]``.
     """
-    hq, d = q.shape[2], q.shape[3]
+    n_rows, hq = qrows.shape[0], qrows.shape[1]
     hkv = k.shape[2]
     grp = hq // hkv
-    if scale is None:
-        scale = d ** -0.5
-    kid_all, kpos_all = i64(kid), i64(kpos)
-    qid_all, qpos_all = i64(qid), i64(qpos)
-    o = np.zeros((len(rows), hq, v.shape[3]))
-    lse = np.full((len(rows), hq), -np.inf)
+    o = np.zeros((n_rows, hq, v.shape[3]))
+    lse = np.full((n_rows, hq), -np.inf)
     for n, (b, i) in enumerate(rows):
-        vis = visible(qid_all[b, i:i + 1], qpos_all[b, i:i + 1], kid_all[b], kpos_all[b],
-                      causal, window)
+        vis = visible(qid[b, i:i + 1], qpos[b, i:i + 1], kid[b], kpos[b], causal, window)
         cand = np.nonzero(vis[0])[0]
         if cand.size == 0:
             continue
-        qrow = f64(q[b, i])                       # [Hq, D]
+        qrow = f64(qrows[n])                      # [Hq, D]
         for g in range(hkv):
             kc = _take_keys(k, b, cand, g)
             vc = _take_keys(v, b, cand, g)
@@ -181,3 +184,31 @@ def attention_rows(q, k, v, qid, qpos, kid, kpos, rows, scale=None, causal=True,
             o[n, g * grp:(g + 1) * grp] = og[0]
             lse[n, g * grp:(g + 1) * grp] = lg[0]
     return o, lse
+
+
+def attention_rows(q, k, v, qid, qpos, kid, kpos, rows, scale=None, causal=True,
+                   window=(-1, -1), workers=None):
+    """Exact attention for selected query rows only.
+
+    ``rows`` is a sequence of (batch, token) pairs.  Returns fp64 O
+    ``[n, Hq, Dv]`` and LSE ``[n, Hq]`` for those rows, every head.  Used where
+    the full output is too large for the oracle; K and V may be any array-like
+    (they are only indexed, then widened).  Rows are independent, so a large
+    sample is spread over worker processes (``workers``; default: the host
+    cores for 32 rows or more, else this process) that run the same row
+    function on shared copies of K, V and the metadata.
+    """
+    rows = [(int(b), int(i)) for b, i in rows]
+    d = q.shape[3]
+    if scale is None:
+        scale = d ** -0.5
+    qrows = _gather_rows(q, rows) if rows else np.zeros((0, q.shape[2], d))
+    if workers is None:
+        from .pool import pool_workers
+        workers = pool_workers() if len(rows) >= 32 else 1
+    if workers > 1 and len(rows) > 1:
+        from .pool import RowPool
+        with RowPool(k, v, qid, qpos, kid, kpos, workers) as pool:
+            return pool.forward(qrows, rows, scale=scale, causal=causal, window=window)
+    return _rows_forward(qrows, k, v, i64(qid), i64(qpos), i64(kid), i64(kpos), rows, scale,
+                         causal, window)

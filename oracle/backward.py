@@ -27,7 +27,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 from ._arrays import f64, i64
-from .attention import _default_workers, visible
+from .attention import _default_workers, _take_keys, visible
 
 
 def _row_softmax(s, vis):
@@ -99,34 +99,57 @@ def attention_backward(q, k, v, do, qid, qpos, kid, kpos, scale=None, causal=Tru
     return dq, dk, dv
 
 
-def backward_query_rows(q, k, v, do, qid, qpos, kid, kpos, rows, scale=None, causal=True,
-                        window=(-1, -1)):
-    """dQ of selected query rows ``[(b, t), ...]``: ``[len(rows), Hq, D]``.
-
-    dQ of a row depends only on that row and the keys it sees, so full-size
-    problems can be checked on a sample.
-    """
-    b_, tq, hq, d = q.shape
+def _rows_dq(qrows, dorows, k, v, qid, qpos, kid, kpos, rows, scale, causal=True,
+             window=(-1, -1)):
+    """dQ ``[n, Hq, D]`` of single query rows: ``qrows[n]`` and ``dorows[n]``
+    (``[Hq, D]``, ``[Hq, Dv]``) are the query and output gradient at
+    ``rows[n] = (b, t)``; metadata int64 ``[B, T]``; k, v indexable."""
+    n_rows, hq, d = qrows.shape
     hkv = k.shape[2]
     grp = hq // hkv
-    if scale is None:
-        scale = d ** -0.5
-    out = np.zeros((len(rows), hq, d))
+    out = np.zeros((n_rows, hq, d))
     for n, (b, t) in enumerate(rows):
-        vis = visible(i64(qid[b, t:t + 1]), i64(qpos[b, t:t + 1]), i64(kid[b]), i64(kpos[b]),
-                      causal, window)[0]
+        vis = visible(qid[b, t:t + 1], qpos[b, t:t + 1], kid[b], kpos[b], causal, window)[0]
         cand = np.nonzero(vis)[0]
         if cand.size == 0:
             continue
         for g in range(hkv):
-            kc, vc = f64(k[b, cand, g, :]), f64(v[b, cand, g, :])
+            kc, vc = _take_keys(k, b, cand, g), _take_keys(v, b, cand, g)
             for h in range(g * grp, (g + 1) * grp):
-                qh, doh = f64(q[b, t, h, :]), f64(do[b, t, h, :])
+                qh, doh = f64(qrows[n, h]), f64(dorows[n, h])
                 p = _row_softmax(scale * (kc @ qh)[None, :], np.ones((1, cand.size), bool))[0]
                 dp = vc @ doh
                 ds = p * (dp - (p * dp).sum())
                 out[n, h] = scale * (ds @ kc)
     return out
+
+
+def backward_query_rows(q, k, v, do, qid, qpos, kid, kpos, rows, scale=None, causal=True,
+                        window=(-1, -1), workers=None):
+    """dQ of selected query rows ``[(b, t), ...]``: ``[len(rows), Hq, D]``.
+
+    dQ of a row depends only on that row and the keys it sees, so full-size
+    problems can be checked on a sample; a large sample is spread over worker
+    processes running this same row function (``workers``, as in
+    ``attention_rows``).
+    """
+    from .attention import _gather_rows
+    rows = [(int(b), int(t)) for b, t in rows]
+    d = q.shape[3]
+    if scale is None:
+        scale = d ** -0.5
+    if not rows:
+        return np.zeros((0, q.shape[2], d))
+    qrows, dorows = _gather_rows(q, rows), _gather_rows(do, rows)
+    if workers is None:
+        from .pool import pool_workers
+        workers = pool_workers() if len(rows) >= 32 else 1
+    if workers > 1 and len(rows) > 1:
+        from .pool import RowPool
+        with RowPool(k, v, qid, qpos, kid, kpos, workers) as pool:
+            return pool.dq(qrows, dorows, rows, scale=scale, causal=causal, window=window)
+    return _rows_dq(qrows, dorows, k, v, i64(qid), i64(qpos), i64(kid), i64(kpos), rows,
+                    scale, causal, window)
 
 
 def backward_key_rows(q, k, v, do, qid, qpos, kid, kpos, keys, scale=None, causal=True,

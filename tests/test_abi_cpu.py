@@ -183,6 +183,46 @@ def test_fwd_rejects_aliasing(lib):
     assert _fwd(lib, d, lse=_p((7 << 32) + 4096)) == ALIAS  # lse inside o
 
 
+def test_workspace_and_metadata_aliasing(lib):
+    """The workspace (overwritten by the classification and packing kernels)
+    must not overlap any argument, and the outputs must not overlap the
+    segment ids or positions: each such call is refused before any HIP call."""
+    d = _desc()
+    need = ra.workspace_size(d)
+    for name in ("q", "k", "v", "qid", "qpos", "kid", "kpos", "o", "lse"):
+        base = {"q": 0, "k": 1, "v": 2, "qid": 3, "qpos": 4, "kid": 5, "kpos": 6, "o": 7,
+                "lse": 8}[name]
+        assert _fwd(lib, d, ws=_p(base << 32), ws_bytes=need) == ALIAS, name
+    # the workspace's whole extent counts: one starting below lse and reaching into it
+    assert _fwd(lib, d, ws=_p((8 << 32) - 256), ws_bytes=need) == ALIAS
+    assert _fwd(lib, d, o=_p(3 << 32)) == ALIAS          # o over the query ids
+    assert _fwd(lib, d, lse=_p(6 << 32)) == ALIAS        # lse over the key positions
+    # accumulate: the workspace over the partial
+    part = ra.Partial()
+    part.o, part.lse, part.dtype = FAKE + (10 << 32), FAKE + (11 << 32), ra.RA_F32
+    for ws in (10, 11):
+        assert lib.ra_attn_fwd_accumulate(ctypes.byref(d), _p(0), _p(1 << 32), _p(2 << 32),
+                                          _p(3 << 32), _p(4 << 32), _p(5 << 32), _p(6 << 32),
+                                          ctypes.byref(part), _p(7 << 32), _p(8 << 32),
+                                          _p(ws << 32), ctypes.c_size_t(need), None) == ALIAS
+    # classification: outputs over the metadata, workspace over an output
+    c = ctypes.c_void_p(FAKE + (12 << 32))
+    n = ctypes.c_void_p(FAKE + (13 << 32))
+
+    def classify(classes, pairs, ws):
+        return lib.ra_classify_tiles(ctypes.byref(d), _p(3 << 32), _p(4 << 32), _p(5 << 32),
+                                     _p(6 << 32), classes, pairs, ws, ctypes.c_size_t(need), None)
+    assert classify(_p(3 << 32), n, _p(9 << 32)) == ALIAS
+    assert classify(c, _p(6 << 32), _p(9 << 32)) == ALIAS
+    assert classify(c, n, _p(12 << 32)) == ALIAS
+    assert classify(c, c, _p(9 << 32)) == ALIAS
+    # backward: gradients over the metadata, workspace over a gradient or input
+    assert _bwd(lib, d, dq=_p(3 << 32)) == ALIAS
+    assert _bwd(lib, d, dk=_p(5 << 32)) == ALIAS
+    for base in (0, 7, 10, 11, 12, 13, 4):
+        assert _bwd(lib, d, ws=_p(base << 32)) == ALIAS, base
+
+
 def test_accumulate_validation(lib):
     d = _desc()
     part = ra.Partial()

@@ -8,6 +8,8 @@ dims, both input dtypes, masked and unmasked, windows at their edges,
 cross-attention with unrelated layouts, and empty inputs.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -15,7 +17,8 @@ import torch
 import blockwise_online_softmax_fwd_amd as bosf
 import oracle
 from _parity import compare, to64
-from _workload_io import closed_form_counts, device_inputs, sample_rows
+from _workload_io import (closed_form_counts, device_inputs, sample_rows, stratified_rows,
+                          tiles_covered)
 from workloads import get, packed_metadata, random_layout, random_qkv
 
 pytestmark = pytest.mark.gpu
@@ -78,6 +81,27 @@ def test_small_random_layouts(case, out):
     torch.cuda.synchronize()
     ro, rl = oracle.attention(q, k, v, q_ids, q_pos, kv_ids, kv_pos, causal=causal, window=window)
     compare(o, lse, ro, rl, dt, _case_id(case))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_negative_segment_ids(dt, causal):
+    """Segment ids of either sign (0 still marks padding): padding queries see
+    nothing, also next to keys whose id is -1, on boundary tiles as well as
+    skipped and full ones."""
+    rng = np.random.default_rng(71 if causal else 72)
+    q_ids, q_pos = random_layout(rng, 2, 333, max_segments=6, pad_prob=0.4, pos_offset_max=3)
+    sign = torch.from_numpy(np.where(rng.random(q_ids.shape) < 0.5, -1, 1).astype(np.int32))
+    # every segment id negated (-1, -2, ...), then a few segments made positive again
+    q_ids = torch.where(q_ids != 0, -q_ids, q_ids)
+    q_ids = torch.where((q_ids < -3) & (sign > 0), -q_ids, q_ids)
+    q, k, v = random_qkv(2, 333, 333, 16, 2, 128 if dt == "bf16" else 64, dt, seed=73)
+    o, lse = bosf.attn_fwd(*_dev(q, k, v, q_ids, q_pos, q_ids, q_pos), causal=causal,
+                           window=(70, 0) if causal else (60, 60))
+    ro, rl = oracle.attention(q, k, v, q_ids, q_pos, q_ids, q_pos, causal=causal,
+                              window=(70, 0) if causal else (60, 60))
+    assert (q_ids == -1).any() and (q_ids == 0).any()
+    compare(o, lse, ro, rl, dt, f"negative ids {dt} causal={causal}")
 
 
 def test_packed_layout_scale_and_window_edges():
@@ -260,41 +284,73 @@ def _run_workload(w, q, k, v, ids, pos):
     return bosf.attn_fwd(q, k, v, ids, pos, ids, pos, causal=w.causal, window=w.window)
 
 
-@pytest.mark.parametrize("cfg", [4, 5])
-def test_workload_full_size_sampled(cfg):
-    """Full-size run in the configuration the benchmark times; sampled rows
-    (segment starts, window edges, padding, shard boundaries, random) against
-    the oracle, every head."""
-    w = get(cfg)
-    q, k, v, ids, pos = device_inputs(w)
-    o, lse = _run_workload(w, q, k, v, ids, pos)
+@pytest.fixture(scope="module")
+def full_size_oracle():
+    """Per workload (4 or 5): the full-size inputs on the device, a row sample
+    holding one row of every 32-token query tile of every launch (unsplit,
+    dual-chunk and striped(1) rings alike) plus segment starts, window edges,
+    padding and shard boundaries, and the oracle's O and LSE on those rows,
+    every head.  One workload is held at a time."""
+    cache = {}
+
+    def case(cfg):
+        if cfg not in cache:
+            cache.clear()
+            w = get(cfg)
+            inputs = device_inputs(w)
+            rng = np.random.default_rng(cfg)
+            left = w.window[0]
+            edges = [0, 1, 2, 31, 32, 63, 64, left - 1, left, left + 1, left + 2,
+                     w.valid_per_slot - 1, w.valid_per_slot, w.slot_len - 1]
+            rows = set(stratified_rows(w, rng)) | set(sample_rows(w, rng, edges, n_random=0))
+            n = w.seq_len // 4
+            for kind in ("dual_chunk", "striped"):   # both sides of every shard boundary
+                m = oracle.reorder_map(w.seq_len, 4, kind, 1)
+                for r in range(1, 4):
+                    for p in (r * n - 1, r * n, r * n + n // 2 - 1, r * n + n // 2):
+                        rows.add((0, int(m[p])))
+            rows = sorted(rows)
+            q, k, v, ids, pos = inputs
+            ro, rl = oracle.attention_rows(q, k, v, ids, pos, ids, pos, rows, causal=w.causal,
+                                           window=w.window)
+            cache[cfg] = (w, inputs, rows, ro, rl)
+        return cache[cfg]
+
+    yield case
+    cache.clear()
+
+
+@pytest.mark.parametrize("cfg,kind", [(4, None), (5, "dual_chunk"), (5, "striped")])
+def test_workload_full_size_stratified(full_size_oracle, cfg, kind):
+    """Full-size run in the benchmark's configuration (workload 5 also under
+    the tutorial's ring layout, striped with stripe 1), compared with the
+    oracle on at least one row of every 32-token query tile of every launch,
+    every head."""
+    w, inputs, rows, ro, rl = full_size_oracle(cfg)
+    if kind is not None:
+        w = dataclasses.replace(w, reorder=kind, stripe=1)
+        order = oracle.reorder_map(w.seq_len, w.cp_size, kind, 1)
+    else:
+        order = np.arange(w.seq_len)
+    bm = bosf.tile_shape(bosf.make_desc(1, 1, 1, w.num_q_heads, w.num_kv_heads, w.head_dim))[0]
+    assert bm == 32
+    assert len(tiles_covered(rows, order, bm)) == w.batch * w.seq_len // bm
+    o, lse = _run_workload(w, *inputs)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(cfg)
-    left = w.window[0]
-    edges = [0, 1, 2, 31, 32, 63, 64, left - 1, left, left + 1, left + 2,
-             w.valid_per_slot - 1, w.valid_per_slot, w.slot_len - 1]
-    rows = sample_rows(w, rng, edges)
-    if w.cp_size > 1:  # rows on both sides of every shard boundary after reordering
-        m = oracle.reorder_map(w.seq_len, w.cp_size, w.reorder, w.stripe)
-        n = w.seq_len // w.cp_size
-        for r in range(1, w.cp_size):
-            for p in (r * n - 1, r * n, r * n + n // 2 - 1, r * n + n // 2):
-                rows.append((0, int(m[p])))
-    kc, vc = k.cpu(), v.cpu()
-    ro, rl = oracle.attention_rows(q, kc, vc, ids.cpu(), pos.cpu(), ids.cpu(), pos.cpu(), rows,
-                                   causal=w.causal, window=w.window)
     bi = torch.tensor([r[0] for r in rows])
     ti = torch.tensor([r[1] for r in rows])
-    e = compare(o[bi, ti], lse[bi, ti], ro, rl, "bf16", w.name)
-    print(f"{w.name}: {len(rows)} rows x {w.num_q_heads} heads: max|dO|={e[0]:.2e} "
+    e = compare(o[bi, ti], lse[bi, ti], ro, rl, "bf16", f"{w.name} {kind}")
+    print(f"{w.name} {kind or ''}: {len(rows)} rows x {w.num_q_heads} heads: max|dO|={e[0]:.2e} "
           f"max|dLSE|={e[1]:.2e}")
 
 
-@pytest.mark.parametrize("cfg", [2, 4, 5])
-def test_workload_zero_queries_every_row(cfg):
+@pytest.mark.parametrize("cfg,kind", [(2, None), (4, None), (5, None), (5, "striped")])
+def test_workload_zero_queries_every_row(cfg, kind):
     """Q = 0: every row's LSE is ln(visible keys), known in closed form for
     every row at full size; padding rows are -inf."""
     w = get(cfg)
+    if kind is not None:
+        w = dataclasses.replace(w, reorder=kind, stripe=1)
     q, k, v, ids, pos = device_inputs(w, zero_q=True)
     o, lse = _run_workload(w, q, k, v, ids, pos)
     n = closed_form_counts(w, pos, ids)                 # [B, T]
@@ -307,10 +363,12 @@ def test_workload_zero_queries_every_row(cfg):
     assert (o[~live] == 0).all()
 
 
-@pytest.mark.parametrize("cfg", [4, 5])
-def test_workload_uniform_v_every_row(cfg):
+@pytest.mark.parametrize("cfg,kind", [(4, None), (5, None), (5, "striped")])
+def test_workload_uniform_v_every_row(cfg, kind):
     """v[b, j, g, :] = c_g: every live row's output is c_g of its head's group."""
     w = get(cfg)
+    if kind is not None:
+        w = dataclasses.replace(w, reorder=kind, stripe=1)
     c = torch.randn((w.num_kv_heads, w.head_dim), generator=torch.Generator().manual_seed(1))
     c = c.to(torch.bfloat16)
     q, k, v, ids, pos = device_inputs(w, uniform_v=c)

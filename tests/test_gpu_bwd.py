@@ -96,6 +96,27 @@ def _small_inputs(case):
     return q, k, v, do, qi, qp, ki, kp
 
 
+def test_negative_segment_ids():
+    """Segment ids of either sign (0 marks padding): a padding query never sees
+    a key of id -1 and no query sees a padding key, in both passes."""
+    rng = np.random.default_rng(74)
+    ids, pos = random_layout(rng, 2, 300, max_segments=6, pad_prob=0.4, pos_offset_max=3)
+    ids = torch.where(ids != 0, -ids, ids)
+    assert (ids == -1).any() and (ids == 0).any()
+    q, k, v = random_qkv(2, 300, 300, 16, 2, 128, "bf16", seed=75)
+    do = random_qkv(2, 300, 1, 16, 1, 128, "bf16", seed=76)[0]
+    for causal, window in ((True, (50, 0)), (False, (-1, -1))):
+        dq, dk, dv = _fwd_bwd(*_dev(q, k, v, ids, pos, ids, pos, do), causal, window)
+        torch.cuda.synchronize()
+        refs = oracle.attention_backward(q, k, v, do, ids, pos, ids, pos, causal=causal,
+                                         window=window)
+        zq, zk = _unreached(ids.numpy(), pos.numpy(), ids.numpy(), pos.numpy(), causal, window)
+        for got, ref, z, name in ((dq, refs[0], zq, "dq"), (dk, refs[1], zk, "dk"),
+                                  (dv, refs[2], zk, "dv")):
+            compare_grads(got, ref, f"negative ids causal={causal} {name}",
+                          exact_zero=np.broadcast_to(z[:, :, None, None], ref.shape))
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[_case_id(c) for c in SMALL])
 @pytest.mark.parametrize("o_dtype", ["bf16", "f32"])
 def test_small_random_layouts(case, o_dtype):

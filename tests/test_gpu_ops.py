@@ -153,34 +153,49 @@ def test_classify_workloads(cfg):
     assert np.array_equal(pairs, ref_pairs)
 
 
-@pytest.mark.parametrize("cfg,ranks", [(3, (0, 1, 2, 3)), (5, (0, 1))])
-def test_classify_ring_steps(cfg, ranks):
+@pytest.mark.parametrize("cfg,kind", [(3, "dual_chunk"), (5, "dual_chunk"), (5, "striped")])
+def test_classify_ring_steps(cfg, kind):
     """Every (rank, ring step) of the reordered workloads, batch row 0 (rows are
-    identical), against the oracle on its own reordered metadata."""
+    identical), against the oracle on its own reordered metadata: the
+    dual-chunk layout the benchmark times and the tutorial's ring layout
+    (striped, stripe 1), all four ranks."""
+    from concurrent.futures import ThreadPoolExecutor
     w = get(cfg)
+    stripe = 1
     ids, pos = packed_metadata(1, w.seq_len, w.slots, w.valid_per_slot)
-    m = oracle.reorder_map(w.seq_len, w.cp_size, w.reorder, w.stripe)
+    m = oracle.reorder_map(w.seq_len, w.cp_size, kind, stripe)
     ids_o, pos_o = oracle.apply_map(ids.numpy(), m), oracle.apply_map(pos.numpy(), m)
-    ids_g = bosf.reorder(ids.to(DEV), w.cp_size, w.reorder, w.stripe)
-    pos_g = bosf.reorder(pos.to(DEV), w.cp_size, w.reorder, w.stripe)
+    ids_g = bosf.reorder(ids.to(DEV), w.cp_size, kind, stripe)
+    pos_g = bosf.reorder(pos.to(DEV), w.cp_size, kind, stripe)
     assert np.array_equal(ids_g.cpu().numpy(), ids_o)
     n = w.seq_len // w.cp_size
-    total = 0
-    for r in ranks:
+    desc = bosf.make_desc(1, n, n, w.num_q_heads, w.num_kv_heads, w.head_dim)
+    bm, bn = bosf.tile_shape(desc)
+    steps = [(r, s) for r in range(w.cp_size) for s in range(w.cp_size)]
+    got, total = {}, 0
+    for r, s in steps:
         rq = slice(r * n, (r + 1) * n)
-        for s in range(w.cp_size):
-            c = (r - s) % w.cp_size
-            rk = slice(c * n, (c + 1) * n)
-            cls, pairs = bosf.classify_tiles(ids_g[:, rq], pos_g[:, rq], ids_g[:, rk], pos_g[:, rk],
-                                             num_q_heads=w.num_q_heads,
-                                             num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
-                                             causal=w.causal, window=w.window)
-            desc = bosf.make_desc(1, n, n, w.num_q_heads, w.num_kv_heads, w.head_dim)
-            bm, bn = bosf.tile_shape(desc)
-            ref = oracle.classify_tiles_exact(ids_o[:, rq], pos_o[:, rq], ids_o[:, rk],
-                                              pos_o[:, rk], bm, bn, w.causal, w.window)
-            assert np.array_equal(cls.cpu().numpy(), ref), (r, s)
-            total += int(pairs.cpu()[0])
-    if cfg == 5 and ranks == (0, 1):
-        # each rank of the long-context workload sees exactly a quarter of one row's pairs
-        assert total == 2 * (536936448 // 2 // 4)
+        c = (r - s) % w.cp_size
+        rk = slice(c * n, (c + 1) * n)
+        cls, pairs = bosf.classify_tiles(ids_g[:, rq], pos_g[:, rq], ids_g[:, rk], pos_g[:, rk],
+                                         num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                                         head_dim=w.head_dim, causal=w.causal, window=w.window)
+        got[(r, s)] = cls.cpu().numpy()
+        total += int(pairs.cpu()[0])
+
+    def exact(rs):
+        r, s = rs
+        c = (r - s) % w.cp_size
+        rq, rk = slice(r * n, (r + 1) * n), slice(c * n, (c + 1) * n)
+        return oracle.classify_tiles_exact(ids_o[:, rq], pos_o[:, rq], ids_o[:, rk], pos_o[:, rk],
+                                           bm, bn, w.causal, w.window)
+
+    with ThreadPoolExecutor(8) as ex:
+        refs = dict(zip(steps, ex.map(exact, steps)))
+    for rs in steps:
+        assert np.array_equal(got[rs], refs[rs]), rs
+    # the ring covers every visible pair of one batch row exactly once
+    want = int(oracle.visible_pairs(ids, pos, ids, pos, w.causal, w.window)[0])
+    assert total == want
+    if cfg == 5:
+        assert total == 536936448 // 2

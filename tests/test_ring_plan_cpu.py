@@ -2,7 +2,10 @@
 
 import torch
 
-from blockwise_online_softmax_fwd_amd.ring import _stripe_schedule, needs_reordered_q
+import pytest
+
+from blockwise_online_softmax_fwd_amd.ring import RingPlan, _stripe_schedule, needs_reordered_q
+from workloads import packed_metadata
 
 
 def test_stripe_schedule_roles():
@@ -25,3 +28,32 @@ def test_q_in_place_only_without_joint_calls():
     joint = torch.tensor([[[5, 2, 0, 0], [5, 2, 0, 0]], [[1, 0, 0, 0], [0, 0, 0, 1]]] * 2)
     assert needs_reordered_q(joint, 4)
     assert needs_reordered_q(None, 4) and needs_reordered_q(torch.ones(4, 4), 4)
+
+
+def test_plan_refuses_another_layout_or_mask():
+    """A plan records the layout and mask it was computed for; using it with
+    other ids or positions, another shard count, reorder or mask is refused
+    (it would skip blocks that hold visible pairs)."""
+    ids, pos = packed_metadata(2, 4096, 4, 768)
+    counts = torch.ones((4, 4), dtype=torch.int64)
+    plan = RingPlan(counts, ids, pos, 4, "dual_chunk", 1, True, (-1, -1))
+    plan.check(ids, pos, 4, "dual_chunk", 1, True, (-1, -1))
+    plan.check(ids.clone(), pos.clone(), 4, "dual_chunk", 1, True, (-1, -1))   # same values
+    for args in [(8, "dual_chunk", 1, True, (-1, -1)), (4, "striped", 1, True, (-1, -1)),
+                 (4, "dual_chunk", 1, False, (-1, -1)), (4, "dual_chunk", 1, True, (100, 0))]:
+        with pytest.raises(ValueError):
+            plan.check(ids, pos, *args)
+    other_ids, other_pos = packed_metadata(2, 4096, 4, 700)
+    with pytest.raises(ValueError):
+        plan.check(other_ids, other_pos, 4, "dual_chunk", 1, True, (-1, -1))
+    shifted = pos.clone()
+    shifted[1, 5] += 1
+    with pytest.raises(ValueError):
+        plan.check(ids, shifted, 4, "dual_chunk", 1, True, (-1, -1))
+    # an in-place change of checked tensors is seen too
+    ids2 = ids.clone()
+    plan.check(ids2, pos, 4, "dual_chunk", 1, True, (-1, -1))
+    ids2[0, 0] = 9
+    with pytest.raises(ValueError):
+        plan.check(ids2, pos, 4, "dual_chunk", 1, True, (-1, -1))
+    assert needs_reordered_q(plan, 4)
