@@ -139,11 +139,14 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
 }
 
-// Branch-free visibility test of one key against the lane's query: the pair
-// is visible iff kid == qkey and lo <= qpos - kpos <= hi.  A padding query
-// (id 0) gets the empty range lo = 1 > hi = 0, so it sees no key whatever the
-// ids; a padding key (id 0) never equals a non-padding query's id.  Positions
-// are non-negative, so qpos - kpos cannot overflow.
+// Branch-free visibility test of one key against the lane's query on a
+// boundary tile: kid == qkey and lo <= qpos - kpos <= hi (lo and hi depend on
+// the mask only, so they stay in scalar registers; positions are
+// non-negative, so qpos - kpos cannot overflow).  qkey is the query's own
+// segment id, of either sign; a padding key (id 0) never matches a live
+// query.  A padding query (id 0) would match padding keys here, so its row is
+// declared empty in the epilogue whatever it accumulated (a tile holding a
+// padding query is never classified full).
 struct LaneMask {
   int qkey, qpos, lo, hi;
   __device__ __forceinline__ bool operator()(int kid, int kpos) const {
@@ -284,10 +287,6 @@ attn_fwd_bf16_kernel(AttnParams p) {
     lm.lo = p.mask.causal ? 0 : INT_MIN;
     if (p.mask.wr >= 0) lm.lo = max(lm.lo, -p.mask.wr);
     lm.hi = p.mask.wl >= 0 ? p.mask.wl : INT_MAX;
-    if (my_qid == 0) {   // padding (or out-of-range) query: empty window
-      lm.lo = 1;
-      lm.hi = 0;
-    }
   }
   const bool ragged = (p.tk % BN) != 0;
   auto entry_tile = [&](int it) { return (int)(lst[it] & 0x7fffffffu); };
@@ -431,7 +430,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
   // launch, and streaming it keeps the L2 for the K/V tiles that neighbouring
   // workgroups share.
   const float zt = pair_sum(z);
-  const bool live = zt > 0.0f;
+  const bool live = zt > 0.0f && lm.qkey != 0;   // padding queries see nothing
   const float l_own = live ? p.scale * m + logf(zt) : -INFINITY;
   float w_own = live ? 1.0f / zt : 0.0f;
   float w_acc = 0.0f, l_out = l_own;
