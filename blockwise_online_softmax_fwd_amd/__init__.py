@@ -7,6 +7,7 @@ ABI of ``include/ringattn.h``); :mod:`.ringattn` is its ctypes binding and
 
 from .ringattn import (  # noqa: F401
     DUAL_CHUNK,
+    NOALLOC_SCRATCH_BYTES,
     STRIPED,
     TILE_FULL,
     TILE_PARTIAL,
@@ -15,6 +16,7 @@ from .ringattn import (  # noqa: F401
     attn_bwd,
     attn_fwd,
     attn_fwd_accumulate,
+    attn_fwd_noalloc,
     attn_merge,
     bwd_workspace_size,
     check_support,

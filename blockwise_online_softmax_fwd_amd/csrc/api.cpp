@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -329,10 +330,42 @@ ra_status ra_attn_fwd_workspace_size(const ra_attn_desc *desc, size_t *bytes) {
 
 namespace {
 
+// Scratch of the no-allocation forward: one copy per GPU, reserved when the
+// library's code is loaded onto that GPU and held until the process ends.
+// Host code never uses this name as an address (on the host it is only a
+// stand-in); it uses the per-device pointer that hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[RA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device.
+ra_status scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RA_ERR_UNSUPPORTED, "device %d beyond the %d devices the scratch table holds",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p % 256) != 0)
+      return fail(RA_ERR_HIP, "scratch of device %d has no usable address", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return RA_OK;
+}
+
 ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, const void *v,
                         const int32_t *qid, const int32_t *qpos, const int32_t *kid,
                         const int32_t *kpos, const ra_partial *acc, void *o, float *lse,
-                        void *workspace, size_t workspace_bytes, ra_stream_t stream) {
+                        void *workspace, size_t workspace_bytes, ra_stream_t stream,
+                        bool use_scratch = false) {
   // an armed profiling pair belongs to this call, whatever its outcome
   const hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
@@ -401,6 +434,18 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
   if (overlaps_any(o, o_span, ms.s, 4) || overlaps_any(lse, l_span, ms.s, 4))
     return fail(RA_ERR_ALIAS, "o / lse overlap the segment ids or positions");
   if (!has_q) return RA_OK;
+  if (use_scratch) {
+    // the no-allocation entry point: the workspace is this device's scratch
+    const size_t need = layout_of(d, r).total;
+    if (need > RA_NOALLOC_SCRATCH_BYTES)
+      return fail(RA_ERR_WORKSPACE,
+                  "this call needs %zu bytes of scratch; the no-allocation forward holds %zu "
+                  "(use ra_attn_fwd with a caller-owned workspace)",
+                  need, (size_t)RA_NOALLOC_SCRATCH_BYTES);
+    st = scratch_of_current_device(&workspace);
+    if (st != RA_OK) return st;
+    workspace_bytes = RA_NOALLOC_SCRATCH_BYTES;
+  }
   st = check_workspace(d, r, workspace, workspace_bytes);
   if (st != RA_OK) return st;
   {
@@ -519,6 +564,13 @@ ra_status ra_attn_fwd_accumulate(const ra_attn_desc *d, const void *q, const voi
   if (!partial) return fail(RA_ERR_NULL, "partial is NULL");
   return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, partial, o, lse, workspace,
                        workspace_bytes, stream);
+}
+
+ra_status ra_attn_fwd_noalloc(const ra_attn_desc *d, const void *q, const void *k, const void *v,
+                              const int32_t *qid, const int32_t *qpos, const int32_t *kid,
+                              const int32_t *kpos, void *o, float *lse, ra_stream_t stream) {
+  return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, nullptr, o, lse, nullptr, 0, stream,
+                       /*use_scratch=*/true);
 }
 
 ra_status ra_profile_next_kernel(ra_event_t start, ra_event_t stop) {

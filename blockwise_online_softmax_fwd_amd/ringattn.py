@@ -29,7 +29,10 @@ EXPORTS = ["ra_version", "ra_status_string", "ra_last_error", "ra_check_support"
            "ra_attn_fwd_workspace_size", "ra_attn_fwd", "ra_attn_fwd_accumulate",
            "ra_classify_tiles", "ra_attn_merge", "ra_reorder", "ra_inverse_reorder",
            "ra_reorder_index", "ra_attn_bwd_workspace_size", "ra_attn_bwd",
-           "ra_profile_next_kernel"]
+           "ra_profile_next_kernel", "ra_attn_fwd_noalloc"]
+
+# Size of the no-allocation forward's per-GPU scratch (RA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class RingAttnError(RuntimeError):
@@ -98,6 +101,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ra_attn_bwd_workspace_size": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)], I32),
         "ra_attn_bwd": ([ctypes.POINTER(AttnDesc)] + [P] * 10 + [I32] + [P] * 3 + [P, SZ, P], I32),
         "ra_profile_next_kernel": ([P, P], I32),
+        "ra_attn_fwd_noalloc": ([ctypes.POINTER(AttnDesc)] + [P] * 9 + [P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -293,6 +297,26 @@ def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_segment_ids), _ptr(q_segment_pos),
         _ptr(kv_segment_ids), _ptr(kv_segment_pos), _ptr(out), _ptr(lse), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), _stream(q)))
+    return out, lse
+
+
+def attn_fwd_noalloc(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, *,
+                     out, lse, scale=None, causal=True, window=(-1, -1)):
+    """``attn_fwd`` through the entry point that allocates nothing: the caller
+    passes the outputs ``out`` and ``lse``; the tile lists and packed K/V go
+    to the library's per-GPU scratch (``NOALLOC_SCRATCH_BYTES``).  Calls that
+    may overlap in time on one GPU must not be made.  Returns ``(out, lse)``."""
+    _require_gpu(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, out, lse)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape[:3] != v.shape[:3]:
+        raise ValueError("k and v must have the same batch, length and heads")
+    _check_meta(q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos)
+    desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window,
+                      _dtype_code(out.dtype), out, lse, v)
+    _check(load_library().ra_attn_fwd_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_segment_ids), _ptr(q_segment_pos),
+        _ptr(kv_segment_ids), _ptr(kv_segment_pos), _ptr(out), _ptr(lse), _stream(q)))
     return out, lse
 
 

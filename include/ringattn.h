@@ -221,6 +221,31 @@ ra_status ra_attn_fwd_accumulate(const ra_attn_desc *desc, const void *q, const 
                                  ra_stream_t stream);
 
 /*
+ * The forward of ra_attn_fwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid hipMalloc.  Same arguments, rules and results as ra_attn_fwd
+ * (bit-identical outputs), but no workspace argument: the tile lists and the
+ * packed K/V tiles go to a scratch buffer of RA_NOALLOC_SCRATCH_BYTES that
+ * the library holds as a static device array, one per GPU, reserved when the
+ * library is loaded onto that GPU and kept until the process ends.  The call
+ * allocates nothing and uses the current device's scratch (the stream must
+ * belong to the current device).  A description whose
+ * ra_attn_fwd_workspace_size() exceeds RA_NOALLOC_SCRATCH_BYTES is refused
+ * with RA_ERR_WORKSPACE before any HIP call.  Every call on one GPU shares
+ * that GPU's scratch: calls that may overlap in time on one GPU (different
+ * streams, or threads without ordering) race and must not be made; calls
+ * ordered on one stream are safe.  Nothing in the scratch needs to start at
+ * zero: each call writes all it reads.
+ */
+#define RA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+ra_status ra_attn_fwd_noalloc(const ra_attn_desc *desc, const void *q, const void *k,
+                              const void *v, const int32_t *q_segment_ids,
+                              const int32_t *q_segment_pos, const int32_t *kv_segment_ids,
+                              const int32_t *kv_segment_pos, void *o, float *lse,
+                              ra_stream_t stream);
+
+/*
  * Measurement hook (for timing the attention kernel apart from the tile
  * classification and K/V packing that precede it in the same call).  The next
  * ra_attn_fwd or ra_attn_fwd_accumulate call made on the calling thread

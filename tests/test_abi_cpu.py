@@ -223,6 +223,35 @@ def test_workspace_and_metadata_aliasing(lib):
         assert _bwd(lib, d, ws=_p(base << 32)) == ALIAS, base
 
 
+def test_noalloc_scratch_limit_and_validation(lib):
+    """The no-allocation forward's scratch size is the header's, and a call
+    that needs more scratch is refused with a clear error before any HIP
+    call; argument checks are ra_attn_fwd's."""
+    text = open(HEADER).read()
+    m = re.search(r"#define RA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ra.NOALLOC_SCRATCH_BYTES
+
+    def call(d, **over):
+        args = dict(q=_p(0), k=_p(1 << 32), v=_p(2 << 32), qid=_p(3 << 32), qpos=_p(4 << 32),
+                    kid=_p(5 << 32), kpos=_p(6 << 32), o=_p(7 << 32), lse=_p(8 << 32))
+        args.update(over)
+        return lib.ra_attn_fwd_noalloc(ctypes.byref(d), args["q"], args["k"], args["v"],
+                                       args["qid"], args["qpos"], args["kid"], args["kpos"],
+                                       args["o"], args["lse"], None)
+    big = _desc(batch=2, q_len=32768, kv_len=65536, num_q_heads=64, num_kv_heads=8)
+    assert ra.workspace_size(big) > ra.NOALLOC_SCRATCH_BYTES
+    assert call(big) == WS
+    msg = lib.ra_last_error().decode()
+    assert "scratch" in msg and str(ra.NOALLOC_SCRATCH_BYTES) in msg
+    assert lib.ra_attn_fwd_noalloc(None, *([None] * 9), None) == NULL
+    d = _desc()
+    assert ra.workspace_size(d) <= ra.NOALLOC_SCRATCH_BYTES
+    assert call(d, q=None) == NULL
+    assert call(d, o=_p(8)) == ALIGN
+    assert call(d, o=_p(0)) == ALIAS
+    assert call(_desc(head_dim=96)) == UNSUP
+
+
 def test_accumulate_validation(lib):
     d = _desc()
     part = ra.Partial()
