@@ -494,6 +494,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads, the backward call and the standalone "
                          "merge/reorder rates in detail")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the other workloads and the backward call (keep the standalone "
+                         "merge/reorder rates)")
     ap.add_argument("--unfused", action="store_true",
                     help="ring steps write separate partials folded by attn_merge")
     ap.add_argument("--separate-inverse", action="store_true",
@@ -645,7 +648,7 @@ def main():
                                   out.get("lse"))
         log(f"cpu baseline {cpu['value'] * 1000:.2f} GFLOP/s on {cpu['cores']} cores")
 
-    if not args.no_extra and args.workload == 5 and not allgather:
+    if not args.no_extra and not args.no_other_configs and args.workload == 5 and not allgather:
         # the other configurations, measured in this same process
         res["bufs"] = None
         out.clear()
