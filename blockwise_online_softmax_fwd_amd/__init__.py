@@ -7,6 +7,8 @@ ABI of ``include/ringattn.h``); :mod:`.ringattn` is its ctypes binding and
 
 from .ringattn import (  # noqa: F401
     DUAL_CHUNK,
+    FWD_KV_READY,
+    FWD_SCHEDULE_READY,
     NOALLOC_SCRATCH_BYTES,
     STRIPED,
     TILE_FULL,
@@ -29,6 +31,7 @@ from .ringattn import (  # noqa: F401
     reorder_index,
     tile_shape,
     version,
+    workspace_parts,
     workspace_size,
 )
 from .ring import (RingBuffers, allgather_forward, needs_reordered_q, ring_forward,  # noqa: F401

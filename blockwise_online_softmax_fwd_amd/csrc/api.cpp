@@ -361,11 +361,25 @@ ra_status scratch_of_current_device(void **ptr) {
   return RA_OK;
 }
 
+// Where a forward call's workspace comes from: one caller-owned buffer (tile
+// lists followed by the packed K/V), this device's scratch, or the two parts
+// in separate caller-owned buffers (with flags saying which already hold
+// this call's data).
+enum class WsMode { kContiguous, kScratch, kSplit };
+
+struct FwdWorkspace {
+  WsMode mode;
+  void *ws;              // contiguous: the buffer; split: the schedule part
+  size_t bytes;
+  void *kv;              // split: the packed K/V part
+  size_t kv_bytes;
+  uint32_t flags;        // split: RA_FWD_* reuse flags
+};
+
 ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, const void *v,
                         const int32_t *qid, const int32_t *qpos, const int32_t *kid,
                         const int32_t *kpos, const ra_partial *acc, void *o, float *lse,
-                        void *workspace, size_t workspace_bytes, ra_stream_t stream,
-                        bool use_scratch = false) {
+                        FwdWorkspace w, ra_stream_t stream) {
   // an armed profiling pair belongs to this call, whatever its outcome
   const hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
@@ -434,32 +448,64 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
   if (overlaps_any(o, o_span, ms.s, 4) || overlaps_any(lse, l_span, ms.s, 4))
     return fail(RA_ERR_ALIAS, "o / lse overlap the segment ids or positions");
   if (!has_q) return RA_OK;
-  if (use_scratch) {
-    // the no-allocation entry point: the workspace is this device's scratch
-    const size_t need = layout_of(d, r).total;
-    if (need > RA_NOALLOC_SCRATCH_BYTES)
-      return fail(RA_ERR_WORKSPACE,
-                  "this call needs %zu bytes of scratch; the no-allocation forward holds %zu "
-                  "(use ra_attn_fwd with a caller-owned workspace)",
-                  need, (size_t)RA_NOALLOC_SCRATCH_BYTES);
-    st = scratch_of_current_device(&workspace);
+  const ra::WorkspaceLayout L = layout_of(d, r);
+  const size_t sched_need = L.kpack, kv_need = L.total - L.kpack;
+  // sched: tile summaries and lists (offsets of L below kpack); kvp: the
+  // packed K/V tiles (offsets of L from kpack on, shifted to start at 0)
+  char *sched = nullptr, *kvp = nullptr;
+  const Span used[11] = {{q, q_span}, {k, kv_span}, {v, v_span}, {o, o_span}, {lse, l_span},
+                         acc_span, acc_lspan, ms.s[0], ms.s[1], ms.s[2], ms.s[3]};
+  if (w.mode == WsMode::kSplit) {
+    if (sched_need > 0 && !w.ws)
+      return fail(RA_ERR_WORKSPACE, "schedule workspace is NULL (%zu bytes needed)", sched_need);
+    if (w.bytes < sched_need)
+      return fail(RA_ERR_WORKSPACE, "schedule workspace has %zu bytes, %zu needed", w.bytes,
+                  sched_need);
+    if (kv_need > 0 && !w.kv)
+      return fail(RA_ERR_WORKSPACE, "K/V workspace is NULL (%zu bytes needed)", kv_need);
+    if (w.kv_bytes < kv_need)
+      return fail(RA_ERR_WORKSPACE, "K/V workspace has %zu bytes, %zu needed", w.kv_bytes,
+                  kv_need);
+    if (!aligned(w.ws, 256) || !aligned(w.kv, 256))
+      return fail(RA_ERR_ALIGN, "workspaces must be 256-byte aligned");
+    if (w.flags & ~(uint32_t)(RA_FWD_SCHEDULE_READY | RA_FWD_KV_READY))
+      return fail(RA_ERR_SHAPE, "unknown flags 0x%x", w.flags);
+    if (overlaps_any(w.ws, sched_need, used, 11) || overlaps_any(w.kv, kv_need, used, 11))
+      return fail(RA_ERR_ALIAS, "a workspace overlaps an input or output");
+    if (overlaps(w.ws, sched_need, w.kv, kv_need))
+      return fail(RA_ERR_ALIAS, "the schedule and K/V workspaces overlap");
+    sched = (char *)w.ws;
+    kvp = (char *)w.kv;
+  } else {
+    void *workspace = w.ws;
+    size_t workspace_bytes = w.bytes;
+    if (w.mode == WsMode::kScratch) {
+      // the no-allocation entry point: the workspace is this device's scratch
+      if (L.total > RA_NOALLOC_SCRATCH_BYTES)
+        return fail(RA_ERR_WORKSPACE,
+                    "this call needs %zu bytes of scratch; the no-allocation forward holds %zu "
+                    "(use ra_attn_fwd with a caller-owned workspace)",
+                    L.total, (size_t)RA_NOALLOC_SCRATCH_BYTES);
+      st = scratch_of_current_device(&workspace);
+      if (st != RA_OK) return st;
+      workspace_bytes = RA_NOALLOC_SCRATCH_BYTES;
+    }
+    st = check_workspace(d, r, workspace, workspace_bytes);
     if (st != RA_OK) return st;
-    workspace_bytes = RA_NOALLOC_SCRATCH_BYTES;
-  }
-  st = check_workspace(d, r, workspace, workspace_bytes);
-  if (st != RA_OK) return st;
-  {
-    const Span used[11] = {{q, q_span}, {k, kv_span}, {v, v_span}, {o, o_span}, {lse, l_span},
-                           acc_span, acc_lspan, ms.s[0], ms.s[1], ms.s[2], ms.s[3]};
-    if (overlaps_any(workspace, layout_of(d, r).total, used, 11))
+    if (overlaps_any(workspace, L.total, used, 11))
       return fail(RA_ERR_ALIAS, "the workspace overlaps an input or output");
+    sched = (char *)workspace;
+    kvp = (char *)workspace + L.kpack;
   }
+  const bool schedule_ready = w.mode == WsMode::kSplit && (w.flags & RA_FWD_SCHEDULE_READY);
+  const bool kv_ready = w.mode == WsMode::kSplit && (w.flags & RA_FWD_KV_READY);
 
   hipStream_t s = (hipStream_t)stream;
-  const ra::WorkspaceLayout L = layout_of(d, r);
-  const ra::Schedule sch = carve(workspace, L);
-  st = run_schedule(d, r, sch, qid, qpos, kid, kpos, nullptr, s);
-  if (st != RA_OK) return st;
+  const ra::Schedule sch = carve(sched, L);
+  if (!schedule_ready) {
+    st = run_schedule(d, r, sch, qid, qpos, kid, kpos, nullptr, s);
+    if (st != RA_OK) return st;
+  }
 
   ra::AttnParams p;
   p.q = q;
@@ -504,18 +550,18 @@ ra_status attn_fwd_impl(const ra_attn_desc *d, const void *q, const void *k, con
   p.o_split = r.split > 0 ? r.split : INT32_MAX;
   p.o_split_off = r.o_soff;
   p.lse_split_off = r.lse_soff;
-  p.kpack = (char *)workspace + L.kpack;
-  p.vpack = (char *)workspace + L.vpack;
-  p.mpack = (const int32_t *)((char *)workspace + L.mpack);
-  if (d->qkv_dtype == RA_BF16 && d->kv_len > 0) {
+  p.kpack = kvp;
+  p.vpack = kvp + (L.vpack - L.kpack);
+  p.mpack = (const int32_t *)(kvp + (L.mpack - L.kpack));
+  if (d->qkv_dtype == RA_BF16 && d->kv_len > 0 && !kv_ready) {
     ra::PackParams pk;
     pk.k = k;
     pk.v = v;
     pk.kid = kid;
     pk.kpos = kpos;
-    pk.kpack = (char *)workspace + L.kpack;
-    pk.vpack = (char *)workspace + L.vpack;
-    pk.mpack = (int32_t *)((char *)workspace + L.mpack);
+    pk.kpack = kvp;
+    pk.vpack = kvp + (L.vpack - L.kpack);
+    pk.mpack = (int32_t *)(kvp + (L.mpack - L.kpack));
     pk.kv_bs = r.kv_bs;
     pk.kv_ts = r.kv_ts;
     pk.v_bs = r.v_bs;
@@ -552,8 +598,9 @@ ra_status ra_attn_fwd(const ra_attn_desc *d, const void *q, const void *k, const
                       const int32_t *qid, const int32_t *qpos, const int32_t *kid,
                       const int32_t *kpos, void *o, float *lse, void *workspace,
                       size_t workspace_bytes, ra_stream_t stream) {
-  return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, nullptr, o, lse, workspace,
-                       workspace_bytes, stream);
+  return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, nullptr, o, lse,
+                       FwdWorkspace{WsMode::kContiguous, workspace, workspace_bytes, nullptr, 0, 0},
+                       stream);
 }
 
 ra_status ra_attn_fwd_accumulate(const ra_attn_desc *d, const void *q, const void *k,
@@ -562,15 +609,39 @@ ra_status ra_attn_fwd_accumulate(const ra_attn_desc *d, const void *q, const voi
                                  const ra_partial *partial, void *o, float *lse, void *workspace,
                                  size_t workspace_bytes, ra_stream_t stream) {
   if (!partial) return fail(RA_ERR_NULL, "partial is NULL");
-  return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, partial, o, lse, workspace,
-                       workspace_bytes, stream);
+  return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, partial, o, lse,
+                       FwdWorkspace{WsMode::kContiguous, workspace, workspace_bytes, nullptr, 0, 0},
+                       stream);
+}
+
+ra_status ra_attn_fwd_workspace_parts(const ra_attn_desc *desc, size_t *schedule_bytes,
+                                      size_t *kv_bytes) {
+  Resolved r;
+  const ra_status st = check_desc(desc, &r);
+  if (st != RA_OK) return st;
+  if (!schedule_bytes || !kv_bytes) return fail(RA_ERR_NULL, "output pointer is NULL");
+  const ra::WorkspaceLayout L = layout_of(desc, r);
+  *schedule_bytes = L.kpack;
+  *kv_bytes = L.total - L.kpack;
+  return RA_OK;
+}
+
+ra_status ra_attn_fwd_ex(const ra_attn_desc *d, const void *q, const void *k, const void *v,
+                         const int32_t *qid, const int32_t *qpos, const int32_t *kid,
+                         const int32_t *kpos, const ra_partial *partial, void *o, float *lse,
+                         void *schedule_ws, size_t schedule_bytes, void *kv_ws, size_t kv_bytes,
+                         uint32_t flags, ra_stream_t stream) {
+  return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, partial, o, lse,
+                       FwdWorkspace{WsMode::kSplit, schedule_ws, schedule_bytes, kv_ws, kv_bytes,
+                                    flags},
+                       stream);
 }
 
 ra_status ra_attn_fwd_noalloc(const ra_attn_desc *d, const void *q, const void *k, const void *v,
                               const int32_t *qid, const int32_t *qpos, const int32_t *kid,
                               const int32_t *kpos, void *o, float *lse, ra_stream_t stream) {
-  return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, nullptr, o, lse, nullptr, 0, stream,
-                       /*use_scratch=*/true);
+  return attn_fwd_impl(d, q, k, v, qid, qpos, kid, kpos, nullptr, o, lse,
+                       FwdWorkspace{WsMode::kScratch, nullptr, 0, nullptr, 0, 0}, stream);
 }
 
 ra_status ra_profile_next_kernel(ra_event_t start, ra_event_t stop) {

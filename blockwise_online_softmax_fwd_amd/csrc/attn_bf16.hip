@@ -210,7 +210,9 @@ attn_fwd_bf16_kernel(AttnParams p) {
   const bool qvalid = tq < p.tq;
 
   const int64_t row = (int64_t)b * p.nqt + qt;
-  const int n = p.count[row];
+  // clamped so that a stale schedule can only give wrong results, never an
+  // access outside the packed tiles
+  const int n = min(p.count[row], p.nkt);
   // Accumulating in place into a partial: a query tile with nothing visible in
   // this call keeps its partial as it is.
   if (p.acc_in_place && n == 0) return;
@@ -289,7 +291,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
     lm.hi = p.mask.wl >= 0 ? p.mask.wl : INT_MAX;
   }
   const bool ragged = (p.tk % BN) != 0;
-  auto entry_tile = [&](int it) { return (int)(lst[it] & 0x7fffffffu); };
+  auto entry_tile = [&](int it) { return min((int)(lst[it] & 0x7fffffffu), p.nkt - 1); };
   auto entry_masked = [&](int it) {
     const uint32_t e = lst[it];
     return (e >> 31) != 0 || (ragged && (int)(e & 0x7fffffffu) == p.nkt - 1);

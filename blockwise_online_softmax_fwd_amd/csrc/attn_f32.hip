@@ -57,7 +57,9 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
   const int my_qpos = qvalid ? p.qpos[b * p.qm_bs + tq] : 0;
 
   const int64_t row = (int64_t)b * p.nqt + qt;
-  const int n = p.count[row];
+  // clamped so that a stale schedule can only give wrong results, never an
+  // access outside K and V
+  const int n = min(p.count[row], p.nkt);
   if (p.acc_in_place && n == 0) return;  // partial stays as it is
   const uint32_t *lst = p.list + row * p.nkt;
   const float *kb = (const float *)p.k + b * p.kv_bs + (int64_t)g * D;
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(AttnParams p) {
   float m = -INFINITY, z = 0.0f;
   for (int it = 0; it < n; ++it) {
     const uint32_t e = lst[it];
-    const int kt = (int)(e & 0x7fffffffu);
+    const int kt = min((int)(e & 0x7fffffffu), p.nkt - 1);
     const bool masked = (e >> 31) || (ragged && kt == p.nkt - 1);
     __syncthreads();
     for (int u = tid; u < BN * D; u += 128) {

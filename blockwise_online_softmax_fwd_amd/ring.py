@@ -22,7 +22,7 @@ of the keys does not matter).  No partials, no merge.
 
 from __future__ import annotations
 
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 
 import torch
 
@@ -44,6 +44,10 @@ class RingBuffers:
     part: torch.Tensor
     part_lse: torch.Tensor
     workspace: torch.Tensor | None = None
+    # split workspaces (ra_attn_fwd_ex): one packed-K/V buffer per K/V chunk and
+    # a schedule buffer for calls without a plan
+    kv_ws: dict = field(default_factory=dict)
+    sched_ws: torch.Tensor | None = None
 
     @classmethod
     def like(cls, q, k, ids, cp_size, partial_dtype=torch.float32, out_dtype=None, partials=True,
@@ -77,8 +81,61 @@ def reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs: RingBuff
     ra.reorder(pos, cp_size, kind, stripe_size, out=bufs.pos)
 
 
+class _Prepared:
+    """The split workspaces of one driver call (``ra_attn_fwd_ex``).
+
+    Every K/V chunk is packed by the first call that reads it and reused by the
+    others (K/V do not change during the driver call; a new driver call packs
+    again).  Schedules -- tile lists, a function of the layout, the mask and
+    the tile shape only -- live in the plan when there is one, keyed by
+    (rank, step, stripes) and the tile-shape inputs, and are computed once per
+    plan; without a plan every call writes one shared schedule buffer anew.
+    """
+
+    def __init__(self, bufs, plan, desc_full, key_extra):
+        self.bufs, self.plan = bufs, plan
+        self.sched_bytes, self.kv_bytes = ra.workspace_parts(desc_full)
+        self.key_extra = key_extra
+        self.packed = set()
+        dev = bufs.q.device
+        for c in list(bufs.kv_ws):
+            if bufs.kv_ws[c].numel() < self.kv_bytes:
+                del bufs.kv_ws[c]
+        if plan is None and (bufs.sched_ws is None or bufs.sched_ws.numel() < self.sched_bytes):
+            bufs.sched_ws = torch.empty(max(1, self.sched_bytes), dtype=torch.uint8, device=dev)
+        self.dev = dev
+
+    def get(self, key, chunk):
+        """``(schedule_ws, kv_ws, flags)`` for a call on ``chunk``, and a callback
+        that records the call's buffers as written once it has been enqueued."""
+        flags = 0
+        kv = self.bufs.kv_ws.get(chunk)
+        if kv is None:
+            kv = torch.empty(max(1, self.kv_bytes), dtype=torch.uint8, device=self.dev)
+            self.bufs.kv_ws[chunk] = kv
+        if chunk in self.packed:
+            flags |= ra.FWD_KV_READY
+        if self.plan is None:
+            sched = self.bufs.sched_ws
+            skey = None
+        else:
+            skey = (key, self.key_extra, str(self.dev))
+            sched = self.plan.schedules.get(skey)
+            if sched is None:
+                sched = torch.empty(max(1, self.sched_bytes), dtype=torch.uint8, device=self.dev)
+                self.plan.schedules[skey] = sched
+            if skey in self.plan.ready:
+                flags |= ra.FWD_SCHEDULE_READY
+
+        def done():
+            self.packed.add(chunk)
+            if skey is not None:
+                self.plan.ready.add(skey)
+        return (sched, kv, flags), done
+
+
 def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, window=(-1, -1),
-               step_hook=None, fused=True, steps=None, final=None):
+               step_hook=None, fused=True, steps=None, final=None, prep=None):
     """Rank ``rank``'s R ring steps on the reordered buffers; the merged result
     lands in rank's shard of ``bufs.o`` / ``bufs.lse`` (reordered order).
 
@@ -91,7 +148,7 @@ def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, win
     dual-chunk inverse reorder is folded into the last step)."""
     if fused:
         return _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, steps,
-                                 final)
+                                 final, prep)
     t = bufs.q.shape[1]
     n = t // cp_size
     rows = slice(rank * n, (rank + 1) * n)
@@ -106,11 +163,15 @@ def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, win
             dst, dst_lse = bufs.acc, bufs.acc_lse
         else:
             dst, dst_lse = bufs.part, bufs.part_lse
+        prepared, done = prep.get((rank, s, (0, 1)), c) if prep else (None, None)
         if step_hook:
             step_hook("attn_fwd", rank, s, True)
         _, _ = ra.attn_fwd(q_r, bufs.k[:, cols], bufs.v[:, cols], id_r, pos_r, bufs.ids[:, cols],
                            bufs.pos[:, cols], scale=scale, causal=causal, window=window,
-                           out_dtype=dst.dtype, out=dst, lse=dst_lse, workspace=bufs.workspace)
+                           out_dtype=dst.dtype, out=dst, lse=dst_lse, workspace=bufs.workspace,
+                           prepared=prepared)
+        if done:
+            done()
         if step_hook:
             step_hook("attn_fwd", rank, s, False)
         if s == 0:
@@ -125,7 +186,7 @@ def rank_steps(rank, cp_size, bufs: RingBuffers, *, scale=None, causal=True, win
 
 
 def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, steps=None,
-                      final=None):
+                      final=None, prep=None):
     t = bufs.q.shape[1]
     n = t // cp_size
     rows = slice(rank * n, (rank + 1) * n)
@@ -140,15 +201,19 @@ def _rank_steps_fused(rank, cp_size, bufs, scale, causal, window, step_hook, ste
                 bufs.pos[:, cols])
         last = i == len(steps) - 1
         dst, dst_lse, split = final if last else (bufs.acc, bufs.acc_lse, None)
+        prepared, done = prep.get((rank, s, (0, 1)), c) if prep else (None, None)
         if step_hook:
             step_hook("attn_fwd", rank, s, True)
         if i == 0:
             ra.attn_fwd(*args, scale=scale, causal=causal, window=window, out_dtype=dst.dtype,
-                        out=dst, lse=dst_lse, workspace=bufs.workspace, split=split)
+                        out=dst, lse=dst_lse, workspace=bufs.workspace, split=split,
+                        prepared=prepared)
         else:
             ra.attn_fwd_accumulate(*args, bufs.acc, bufs.acc_lse, scale=scale, causal=causal,
                                    window=window, out=dst, lse=dst_lse, workspace=bufs.workspace,
-                                   split=split)
+                                   split=split, prepared=prepared)
+        if done:
+            done()
         if step_hook:
             step_hook("attn_fwd", rank, s, False)
 
@@ -184,6 +249,9 @@ class RingPlan:
                      bool(causal), (int(window[0]), int(window[1])))
         self.fingerprint = _layout_fingerprint(ids, pos)
         self._seen = {self._token(ids, pos)}
+        # device schedules of the ring's calls on this layout (see _Prepared)
+        self.schedules = {}
+        self.ready = set()
 
     @staticmethod
     def _token(ids, pos):
@@ -279,7 +347,7 @@ def needs_reordered_q(plan, cp_size):
 
 
 def _rank_steps_stripes(rank, cp_size, bufs, hplan, o, lse, scale, causal, window, step_hook,
-                        q_orig=None):
+                        q_orig=None, prep=None):
     """Rank ``rank``'s ring steps on a dual-chunk layout with a per-stripe plan
     ``hplan [2, R]``: each of the shard's two stripes starts at its first step
     with work and is finished (written to its original positions in ``o`` /
@@ -314,17 +382,21 @@ def _rank_steps_stripes(rank, cp_size, bufs, hplan, o, lse, scale, causal, windo
                 dst, dst_lse = outs[js[0]]
             else:
                 dst, dst_lse = bufs.acc[:, qr], bufs.acc_lse[:, qr]
+            prepared, done = prep.get((rank, s, tuple(js)), c) if prep else (None, None)
             if step_hook:
                 step_hook("attn_fwd", rank, s, True)
             if first:
                 ra.attn_fwd(*args, scale=scale, causal=causal, window=window, out_dtype=dst.dtype,
-                            out=dst, lse=dst_lse, workspace=bufs.workspace, split=split)
+                            out=dst, lse=dst_lse, workspace=bufs.workspace, split=split,
+                            prepared=prepared)
             else:
                 ra.attn_fwd_accumulate(*args, bufs.acc[:, qr], bufs.acc_lse[:, qr], scale=scale,
                                        causal=causal, window=window,
                                        out=None if not last else dst,
                                        lse=None if not last else dst_lse,
-                                       workspace=bufs.workspace, split=split)
+                                       workspace=bufs.workspace, split=split, prepared=prepared)
+            if done:
+                done()
             if step_hook:
                 step_hook("attn_fwd", rank, s, False)
 
@@ -354,21 +426,21 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     """
     if q.shape[1] != k.shape[1]:
         raise ValueError("the ring driver runs self-attention (Tq == Tk)")
+    plan_obj = None
     if plan is not None:
         if not isinstance(plan, RingPlan):
             raise TypeError("plan must come from ring_plan()")
         plan.check(ids, pos, cp_size, kind, stripe_size, causal, window)
-        plan = plan.counts
+        plan_obj, plan = plan, plan.counts
     if bufs is None:
         bufs = RingBuffers.like(q, k, ids, cp_size, partial_dtype, out_dtype, v=v)
-    if bufs.workspace is None:
-        b, t = ids.shape
-        n = t // cp_size
-        desc = ra.make_desc(b, n, n, q.shape[2], k.shape[2], q.shape[3],
-                            ra._dtype_code(q.dtype), None, scale, causal, window,
-                            {"v_head_dim": v.shape[3]})
-        bufs.workspace = torch.empty(max(1, ra.workspace_size(desc)), dtype=torch.uint8,
-                                     device=q.device)
+    b, t = ids.shape
+    n = t // cp_size
+    # every call of the ring reads at most a whole shard of queries against one chunk
+    desc = ra.make_desc(b, n, n, q.shape[2], k.shape[2], q.shape[3], ra._dtype_code(q.dtype),
+                        None, scale, causal, window, {"v_head_dim": v.shape[3]})
+    prep = _Prepared(bufs, plan_obj, desc, (ra._dtype_code(q.dtype), q.shape[2], k.shape[2],
+                                            q.shape[3], v.shape[3], bool(causal), tuple(window)))
     direct = (fuse_inverse and fused and ranks is None and cp_size > 1
               and ra._kind_code(kind) == ra.DUAL_CHUNK)
     # With a per-stripe plan whose calls each read one stripe, Q is read in
@@ -392,7 +464,7 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     for r in (range(cp_size) if ranks is None else ranks):
         if stripes:
             _rank_steps_stripes(r, cp_size, bufs, plan[r], o, lse, scale, causal, window,
-                                step_hook, q if q_in_place else None)
+                                step_hook, q if q_in_place else None, prep)
             continue
         steps = None
         if plan is not None and fused:
@@ -403,7 +475,7 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
             hi = slice((2 * cp_size - 1 - r) * h, (2 * cp_size - r) * h)
             final = (o[:, r * h:(r + 1) * h], lse[:, r * h:(r + 1) * h], (h, o[:, hi], lse[:, hi]))
         rank_steps(r, cp_size, bufs, scale=scale, causal=causal, window=window, step_hook=step_hook,
-                   fused=fused, steps=steps, final=final)
+                   fused=fused, steps=steps, final=final, prep=prep)
     if direct:
         return o, lse
     if step_hook:
@@ -431,12 +503,10 @@ def allgather_forward(q, k, v, ids, pos, cp_size, kind="striped", stripe_size=51
     n = t // cp_size
     if bufs is None:
         bufs = RingBuffers.like(q, k, ids, cp_size, out_dtype=out_dtype, partials=False, v=v)
-    if bufs.workspace is None:
-        desc = ra.make_desc(b, n, t, q.shape[2], k.shape[2], q.shape[3],
-                            ra._dtype_code(q.dtype), None, scale, causal, window,
-                            {"v_head_dim": v.shape[3]})
-        bufs.workspace = torch.empty(max(1, ra.workspace_size(desc)), dtype=torch.uint8,
-                                     device=q.device)
+    desc = ra.make_desc(b, n, t, q.shape[2], k.shape[2], q.shape[3], ra._dtype_code(q.dtype),
+                        None, scale, causal, window, {"v_head_dim": v.shape[3]})
+    # the whole K/V is packed once, by the first shard's call
+    prep = _Prepared(bufs, None, desc, None)
     if step_hook:
         step_hook("reorder", -1, -1, True)
     reorder_inputs(q, k, v, ids, pos, cp_size, kind, stripe_size, bufs)
@@ -446,10 +516,12 @@ def allgather_forward(q, k, v, ids, pos, cp_size, kind="striped", stripe_size=51
         rows = slice(r * n, (r + 1) * n)
         if step_hook:
             step_hook("attn_fwd", r, 0, True)
+        prepared, done = prep.get(None, 0)
         ra.attn_fwd(bufs.q[:, rows], bufs.k, bufs.v, bufs.ids[:, rows], bufs.pos[:, rows],
                     bufs.ids, bufs.pos, scale=scale, causal=causal, window=window,
                     out_dtype=bufs.o.dtype, out=bufs.o[:, rows], lse=bufs.lse[:, rows],
-                    workspace=bufs.workspace)
+                    prepared=prepared)
+        done()
         if step_hook:
             step_hook("attn_fwd", r, 0, False)
     if step_hook:

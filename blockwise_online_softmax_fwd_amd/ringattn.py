@@ -29,7 +29,11 @@ EXPORTS = ["ra_version", "ra_status_string", "ra_last_error", "ra_check_support"
            "ra_attn_fwd_workspace_size", "ra_attn_fwd", "ra_attn_fwd_accumulate",
            "ra_classify_tiles", "ra_attn_merge", "ra_reorder", "ra_inverse_reorder",
            "ra_reorder_index", "ra_attn_bwd_workspace_size", "ra_attn_bwd",
-           "ra_profile_next_kernel", "ra_attn_fwd_noalloc"]
+           "ra_profile_next_kernel", "ra_attn_fwd_noalloc", "ra_attn_fwd_workspace_parts",
+           "ra_attn_fwd_ex"]
+
+# Flags of ra_attn_fwd_ex: the schedule / packed K/V buffer already holds this call's data.
+FWD_SCHEDULE_READY, FWD_KV_READY = 1, 2
 
 # Size of the no-allocation forward's per-GPU scratch (RA_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 256 << 20
@@ -102,6 +106,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ra_attn_bwd": ([ctypes.POINTER(AttnDesc)] + [P] * 10 + [I32] + [P] * 3 + [P, SZ, P], I32),
         "ra_profile_next_kernel": ([P, P], I32),
         "ra_attn_fwd_noalloc": ([ctypes.POINTER(AttnDesc)] + [P] * 9 + [P], I32),
+        "ra_attn_fwd_workspace_parts": ([ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ),
+                                         ctypes.POINTER(SZ)], I32),
+        "ra_attn_fwd_ex": ([ctypes.POINTER(AttnDesc)] + [P] * 7 + [ctypes.POINTER(Partial)] +
+                           [P, P, P, SZ, P, SZ, ctypes.c_uint32, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -218,6 +226,45 @@ def workspace_size(desc: AttnDesc) -> int:
     return n.value
 
 
+def workspace_parts(desc: AttnDesc):
+    """Bytes of the forward workspace's two parts: ``(schedule, packed K/V)``."""
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().ra_attn_fwd_workspace_parts(ctypes.byref(desc), ctypes.byref(a),
+                                                      ctypes.byref(b)))
+    return a.value, b.value
+
+
+def _run_fwd(desc, q, k, v, qi, qp, ki, kp, part, out, lse, workspace, prepared):
+    """ra_attn_fwd / ra_attn_fwd_accumulate with one workspace, or ra_attn_fwd_ex
+    with ``prepared = (schedule_ws, kv_ws, flags)``."""
+    lib = load_library()
+    pp = ctypes.byref(part) if part is not None else None
+    if prepared is not None:
+        sched, kvw, flags = prepared
+        need_s, need_k = workspace_parts(desc)
+        if sched is None or sched.numel() < need_s or (need_k and (kvw is None or kvw.numel() < need_k)):
+            raise ValueError(f"prepared workspaces need {need_s} and {need_k} bytes")
+        _check(lib.ra_attn_fwd_ex(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(qi), _ptr(qp), _ptr(ki), _ptr(kp),
+            pp, _ptr(out), _ptr(lse), _ptr(sched), ctypes.c_size_t(sched.numel()),
+            _ptr(kvw) if kvw is not None else None,
+            ctypes.c_size_t(kvw.numel() if kvw is not None else 0), ctypes.c_uint32(flags),
+            _stream(q)))
+        return
+    ws_bytes = workspace_size(desc)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if part is None:
+        _check(lib.ra_attn_fwd(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(qi), _ptr(qp), _ptr(ki), _ptr(kp),
+            _ptr(out), _ptr(lse), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(q)))
+    else:
+        _check(lib.ra_attn_fwd_accumulate(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(qi), _ptr(qp), _ptr(ki), _ptr(kp),
+            pp, _ptr(out), _ptr(lse), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+            _stream(q)))
+
+
 def _attn_desc(q, k, q_ids, kv_ids, scale, causal, window, out_dtype, o, lse, v=None):
     b, tq, hq, d = q.shape
     tk, hkv = k.shape[1], k.shape[2]
@@ -262,7 +309,7 @@ def _apply_split(desc, out, lse, split, tq):
 
 def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, *, scale=None,
              causal=True, window=(-1, -1), out_dtype=None, out=None, lse=None, workspace=None,
-             split=None):
+             split=None, prepared=None):
     """Masked GQA attention forward.  Returns ``(o, lse)``.
 
     q ``[B,Tq,Hq,D]``, k ``[B,Tk,Hkv,D]``, v ``[B,Tk,Hkv,Dv]`` (bf16 or fp32,
@@ -272,6 +319,9 @@ def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
     ``split=(row, out_hi, lse_hi)``: query rows >= row are written to
     ``out_hi``/``lse_hi`` (placed after ``out``/``lse`` in the same buffers, which
     then hold rows [0, row) only) -- a split output.
+    ``prepared=(schedule_ws, kv_ws, flags)``: the workspace in two parts
+    (``ra_attn_fwd_ex``; ``flags`` of ``FWD_SCHEDULE_READY`` / ``FWD_KV_READY``
+    skip the classification / packing when the buffers already hold them).
     """
     _require_gpu(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos)
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -290,13 +340,8 @@ def attn_fwd(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_p
     desc = _attn_desc(q, k, q_segment_ids, kv_segment_ids, scale, causal, window, oc, out, lse, v)
     if split is not None:
         _apply_split(desc, out, lse, split, tq)
-    ws_bytes = workspace_size(desc)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    _check(load_library().ra_attn_fwd(
-        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_segment_ids), _ptr(q_segment_pos),
-        _ptr(kv_segment_ids), _ptr(kv_segment_pos), _ptr(out), _ptr(lse), _ptr(workspace),
-        ctypes.c_size_t(workspace.numel()), _stream(q)))
+    _run_fwd(desc, q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, None,
+             out, lse, workspace, prepared)
     return out, lse
 
 
@@ -322,12 +367,14 @@ def attn_fwd_noalloc(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_s
 
 def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos,
                         partial_o, partial_lse, *, scale=None, causal=True, window=(-1, -1),
-                        out_dtype=None, out=None, lse=None, workspace=None, split=None):
+                        out_dtype=None, out=None, lse=None, workspace=None, split=None,
+                        prepared=None):
     """Attention forward merged with a running partial ``(partial_o, partial_lse)``
     over other key sets.  ``out``/``lse`` default to the partial itself (in-place
     update); query tiles with no visible pair in this call are then untouched.
-    ``split`` as in :func:`attn_fwd` (``out``/``lse`` must then be given and be
-    separate from the partial).  Returns ``(out, lse)``."""
+    ``split`` and ``prepared`` as in :func:`attn_fwd` (with ``split``,
+    ``out``/``lse`` must be given and be separate from the partial).  Returns
+    ``(out, lse)``."""
     _require_gpu(q, k, v, partial_o, partial_lse)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
@@ -357,13 +404,8 @@ def attn_fwd_accumulate(q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, k
         raise ValueError("the partial must have out's token stride")
     part.o_batch_stride = pbs
     part.lse_batch_stride = _batch_stride(partial_lse, 2)
-    ws_bytes = workspace_size(desc)
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-    _check(load_library().ra_attn_fwd_accumulate(
-        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_segment_ids), _ptr(q_segment_pos),
-        _ptr(kv_segment_ids), _ptr(kv_segment_pos), ctypes.byref(part), _ptr(out), _ptr(lse),
-        _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(q)))
+    _run_fwd(desc, q, k, v, q_segment_ids, q_segment_pos, kv_segment_ids, kv_segment_pos, part,
+             out, lse, workspace, prepared)
     return out, lse
 
 

@@ -221,6 +221,47 @@ ra_status ra_attn_fwd_accumulate(const ra_attn_desc *desc, const void *q, const 
                                  ra_stream_t stream);
 
 /*
+ * The forward with its per-call preparation split out, for repeated calls on
+ * one segment layout (the ring driver's steps: several calls read each K/V
+ * chunk, and the same calls recur every step).  The workspace of
+ * ra_attn_fwd is two parts:
+ *   schedule  the query/key tile summaries, the per-query-tile lists of key
+ *             tiles to visit and their visible-pair counts: a function of the
+ *             description (shapes, dtypes, head dims, mask) and of the four
+ *             segment id / position tensors' values only;
+ *   kv        the packed K/V tiles the bf16 kernel streams into LDS (with
+ *             their ids and positions): a function of k, v, kv_segment_ids and
+ *             kv_segment_pos only (empty for fp32 inputs).
+ * ra_attn_fwd_workspace_parts gives the bytes of each (their sum is
+ * ra_attn_fwd_workspace_size's, up to alignment).  ra_attn_fwd_ex is
+ * ra_attn_fwd (partial == NULL) or ra_attn_fwd_accumulate (partial != NULL)
+ * with the two parts in separate caller-owned buffers (256-byte aligned, not
+ * overlapping each other or any argument).  Without flags it writes both
+ * parts, then runs the attention; with RA_FWD_SCHEDULE_READY it skips the
+ * classification and reads schedule_ws as written by an earlier call with an
+ * equal description and equal segment id / position values; with
+ * RA_FWD_KV_READY it skips the packing and reads kv_ws as written by an
+ * earlier call with equal k, v, kv_segment_ids and kv_segment_pos values and
+ * equal shapes.  The library cannot check those two promises: a flag set on
+ * a buffer that holds anything else gives wrong results (the kernels clamp
+ * what they read from the schedule to the call's tile ranges, so they never
+ * read outside the buffers).  Results are bit-identical to ra_attn_fwd /
+ * ra_attn_fwd_accumulate.  Unknown flag bits are RA_ERR_SHAPE.
+ */
+#define RA_FWD_SCHEDULE_READY 1u
+#define RA_FWD_KV_READY 2u
+
+ra_status ra_attn_fwd_workspace_parts(const ra_attn_desc *desc, size_t *schedule_bytes,
+                                      size_t *kv_bytes);
+
+ra_status ra_attn_fwd_ex(const ra_attn_desc *desc, const void *q, const void *k, const void *v,
+                         const int32_t *q_segment_ids, const int32_t *q_segment_pos,
+                         const int32_t *kv_segment_ids, const int32_t *kv_segment_pos,
+                         const ra_partial *partial, void *o, float *lse, void *schedule_ws,
+                         size_t schedule_bytes, void *kv_ws, size_t kv_bytes, uint32_t flags,
+                         ra_stream_t stream);
+
+/*
  * The forward of ra_attn_fwd for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, and harnesses that
  * forbid hipMalloc.  Same arguments, rules and results as ra_attn_fwd

@@ -252,6 +252,53 @@ def test_noalloc_scratch_limit_and_validation(lib):
     assert call(_desc(head_dim=96)) == UNSUP
 
 
+def test_split_workspace_parts_and_validation(lib):
+    """ra_attn_fwd_workspace_parts splits ra_attn_fwd_workspace_size's bytes in two
+    (tile lists; packed K/V, empty for fp32), and ra_attn_fwd_ex checks both
+    buffers (size, alignment, overlaps with each other and with every argument)
+    and its flags before any HIP call."""
+    for kw in ({}, dict(qkv_dtype=ra.RA_F32, head_dim=64), dict(q_len=4096, kv_len=4096),
+               dict(head_dim=192, v_head_dim=128)):
+        d = _desc(**kw)
+        sb, kb = ra.workspace_parts(d)
+        assert sb + kb == ra.workspace_size(d) and sb > 0
+        assert (kb == 0) == (d.qkv_dtype == ra.RA_F32)
+    d = _desc()
+    sb, kb = ra.workspace_parts(d)
+
+    def call(sched=_p(9 << 32), sbytes=sb, kv=_p(10 << 32), kbytes=kb, flags=0, partial=None, **over):
+        args = dict(q=_p(0), k=_p(1 << 32), v=_p(2 << 32), qid=_p(3 << 32), qpos=_p(4 << 32),
+                    kid=_p(5 << 32), kpos=_p(6 << 32), o=_p(7 << 32), lse=_p(8 << 32))
+        args.update(over)
+        return lib.ra_attn_fwd_ex(ctypes.byref(d), args["q"], args["k"], args["v"], args["qid"],
+                                  args["qpos"], args["kid"], args["kpos"], partial, args["o"],
+                                  args["lse"], sched, ctypes.c_size_t(sbytes), kv,
+                                  ctypes.c_size_t(kbytes), ctypes.c_uint32(flags), None)
+    assert lib.ra_attn_fwd_ex(None, *([None] * 7), None, None, None, None, 0, None, 0, 0,
+                              None) == NULL
+    assert call(sched=None) == WS
+    assert call(sbytes=sb - 1) == WS
+    assert call(kv=None) == WS
+    assert call(kbytes=kb - 1) == WS
+    assert call(sched=_p((9 << 32) + 16)) == ALIGN
+    assert call(kv=_p((10 << 32) + 128)) == ALIGN
+    assert call(flags=4) == SHAPE
+    assert call(kv=_p((9 << 32) + ((sb + 255) // 256) * 256 - 256)) == ALIAS   # kv starts in sched
+    assert call(sched=_p(0)) == ALIAS                                          # sched over q
+    assert call(kv=_p(5 << 32)) == ALIAS                                       # kv over key ids
+    assert call(q=None) == NULL
+    assert call(o=_p(0)) == ALIAS
+    part = ra.Partial()
+    part.o, part.lse, part.dtype = FAKE + (11 << 32), FAKE + (12 << 32), ra.RA_F32
+    assert call(partial=ctypes.byref(part), kv=_p(11 << 32)) == ALIAS           # kv over the partial
+    bad = ra.Partial()
+    bad.o, bad.lse, bad.dtype = FAKE + (11 << 32), None, ra.RA_F32
+    assert call(partial=ctypes.byref(bad)) == NULL
+    d32 = _desc(qkv_dtype=ra.RA_F32, head_dim=64)
+    d = d32
+    assert call(sbytes=ra.workspace_parts(d32)[0] - 1, kv=None, kbytes=0) == WS
+
+
 def test_accumulate_validation(lib):
     d = _desc()
     part = ra.Partial()

@@ -163,6 +163,34 @@ def test_ring_with_plan_is_bit_identical():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("kind", ["dual_chunk", "striped"])
+def test_ring_repeated_calls_reuse_plan_schedules(kind):
+    """A plan keeps the device schedules of its ring's calls: a second ring_forward
+    with the same plan and buffers skips the classification and gives the same
+    bits; each call packs its K/V chunks anew, so new K/V values in the same
+    buffers give the result of a fresh run."""
+    b, t, hq, hkv = 2, 4096, 8, 2
+    ids, pos = _dev(*packed_metadata(b, t, 2, 1500))
+    q, k, v = _dev(*random_qkv(b, t, t, hq, hkv, 128, "bf16", seed=91))
+    kw = dict(causal=True, window=(700, 0))
+    halves = kind == "dual_chunk"
+    plan = bosf.ring_plan(ids, pos, 4, kind, 1, num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                          halves=halves, **kw)
+    bufs = bosf.RingBuffers.like(q, k, ids, 4, v=v)
+    o1, l1 = bosf.ring_forward(q, k, v, ids, pos, 4, kind, 1, bufs=bufs, plan=plan, **kw)
+    o1, l1 = o1.clone(), l1.clone()
+    assert plan.ready and plan.ready == set(plan.schedules)
+    o2, l2 = bosf.ring_forward(q, k, v, ids, pos, 4, kind, 1, bufs=bufs, plan=plan, **kw)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o0, l0 = bosf.ring_forward(q, k, v, ids, pos, 4, kind, 1, **kw)
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+    k2, v2 = (k * 0.5).contiguous(), v.flip(1).contiguous()
+    o3, l3 = bosf.ring_forward(q, k2, v2, ids, pos, 4, kind, 1, bufs=bufs, plan=plan, **kw)
+    o4, l4 = bosf.ring_forward(q, k2, v2, ids, pos, 4, kind, 1, **kw)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+    assert not torch.equal(o3, o1)
+
+
 @pytest.mark.parametrize("cp,window,dtype", [(4, (2048, 0), "bf16"), (2, (-1, -1), "bf16"),
                                              (8, (300, 0), "bf16"), (4, (500, 0), "f32")])
 def test_ring_inverse_folded_into_last_step_is_bit_identical(cp, window, dtype):

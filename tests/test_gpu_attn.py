@@ -104,6 +104,48 @@ def test_negative_segment_ids(dt, causal):
     compare(o, lse, ro, rl, dt, f"negative ids {dt} causal={causal}")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_prepared_forward_reuses_schedule_and_packing(dt):
+    """The forward with its workspace in two parts (ra_attn_fwd_ex): bit-identical
+    to ra_attn_fwd when it writes both parts, and when it reuses the schedule
+    and/or the packed K/V written by an earlier call on the same layout and
+    K/V -- also for another query range against the same K/V (packing reused,
+    schedule rewritten) and for the accumulating forward."""
+    rng = np.random.default_rng(81)
+    ids, pos = random_layout(rng, 2, 400, max_segments=4, pad_prob=0.2, pos_offset_max=3)
+    d = 128 if dt == "bf16" else 64
+    q, k, v = _dev(*random_qkv(2, 400, 400, 16, 2, d, dt, seed=82))
+    ids, pos = _dev(ids, pos)
+    kw = dict(causal=True, window=(90, 0))
+    ref = bosf.attn_fwd(q, k, v, ids, pos, ids, pos, **kw)
+    desc = bosf.make_desc(2, 400, 400, 16, 2, d, 0 if dt == "bf16" else 1, window=(90, 0))
+    sb, kb = bosf.workspace_parts(desc)
+    sched = torch.empty(sb, dtype=torch.uint8, device=DEV)
+    kvw = torch.empty(max(kb, 1), dtype=torch.uint8, device=DEV)
+    both = bosf.FWD_SCHEDULE_READY | bosf.FWD_KV_READY
+    for flags in (0, both, bosf.FWD_SCHEDULE_READY, bosf.FWD_KV_READY, both):
+        got = bosf.attn_fwd(q, k, v, ids, pos, ids, pos, prepared=(sched, kvw, flags), **kw)
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), flags
+    # the second half of the queries against the same K/V: the packing is reused
+    sub = slice(200, 400)
+    ref2 = bosf.attn_fwd(q[:, sub], k, v, ids[:, sub], pos[:, sub], ids, pos, **kw)
+    got2 = bosf.attn_fwd(q[:, sub], k, v, ids[:, sub], pos[:, sub], ids, pos,
+                         prepared=(sched, kvw, bosf.FWD_KV_READY), **kw)
+    assert torch.equal(got2[0], ref2[0]) and torch.equal(got2[1], ref2[1])
+    # accumulating forward on a partial, in place, with both parts reused
+    g = torch.Generator().manual_seed(83)
+    po = torch.randn((2, 400, 16, d), generator=g).to(DEV)
+    pl = torch.randn((2, 400, 16), generator=g).to(DEV)
+    ra_ = bosf.attn_fwd_accumulate(q, k, v, ids, pos, ids, pos, po.clone(), pl.clone(), **kw)
+    bosf.attn_fwd(q, k, v, ids, pos, ids, pos, prepared=(sched, kvw, 0), **kw)
+    ga = bosf.attn_fwd_accumulate(q, k, v, ids, pos, ids, pos, po.clone(), pl.clone(),
+                                  prepared=(sched, kvw, both), **kw)
+    assert torch.equal(ga[0], ra_[0]) and torch.equal(ga[1], ra_[1])
+    ro, rl = oracle.attention(q.cpu(), k.cpu(), v.cpu(), ids.cpu(), pos.cpu(), ids.cpu(),
+                              pos.cpu(), **kw)
+    compare(got[0], got[1], ro, rl, dt, "prepared forward")
+
+
 def test_packed_layout_scale_and_window_edges():
     """Packed slots with padding; a non-default scale; window exactly at 31/32/33."""
     ids, pos = packed_metadata(2, 512, 2, 200)
