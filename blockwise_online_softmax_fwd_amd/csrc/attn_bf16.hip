@@ -192,35 +192,45 @@ attn_fwd_bf16_kernel(AttnParams p) {
 
   // Work item; consecutive items stay on one XCD (blocks are dealt to the 8
   // XCDs round-robin, each XCD takes one contiguous run of items).
-  const int hcn = p.group / NH;
+  // The launch has one workgroup per item (fewer than 2^31 of them), so the
+  // index arithmetic is 32-bit: a 64-bit division is a long scalar routine.
+  const uint32_t hcn = (uint32_t)(p.group / NH);
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.nqt * hcn;
-  const int64_t per_xcd = gridDim.x / 8;
-  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (item >= nwork) return;
-  int64_t w = item;
+  const uint32_t per_xcd = gridDim.x / 8;
+  const uint32_t item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if ((int64_t)item >= nwork) return;
+  uint32_t w = item;
   const int hc = (int)(w % hcn);
   w /= hcn;
-  const int qt = (int)(w % p.nqt);
-  w /= p.nqt;
-  const int g = (int)(w % p.hkv);
-  const int b = (int)(w / p.hkv);
+  const int qt = (int)(w % (uint32_t)p.nqt);
+  w /= (uint32_t)p.nqt;
+  const int g = (int)(w % (uint32_t)p.hkv);
+  const int b = (int)(w / (uint32_t)p.hkv);
 
   const int h = g * p.group + hc * NH + (wave % NH);
   const int tq = qt * BM + (wave / NH) * 32 + col;
   const bool qvalid = tq < p.tq;
 
   const int64_t row = (int64_t)b * p.nqt + qt;
+  // The work list was written by an earlier kernel and is read-only here:
+  // read it through the constant address space so the loads are scalar and
+  // never wait behind the direct-to-LDS tile loads.  Its first entry is read
+  // together with the count (its address does not depend on the count), so
+  // the first tile's load waits for one scalar round trip, not two.
+  typedef const __attribute__((address_space(4))) uint32_t *const_list_t;
+  const const_list_t lst = (const_list_t)(p.list + row * p.nkt);
+  // (with no key tile the list is empty and the count's word stands in).  The
+  // empty asm takes both values at this point, so the compiler cannot sink the
+  // entry's load behind the test of the count.
+  const uint32_t e0 = *(p.nkt > 0 ? lst : (const_list_t)(p.count + row));
+  const int cnt = p.count[row];
+  asm volatile("" ::"s"(e0), "s"(cnt));
   // clamped so that a stale schedule can only give wrong results, never an
   // access outside the packed tiles
-  const int n = min(p.count[row], p.nkt);
+  const int n = min(cnt, p.nkt);
   // Accumulating in place into a partial: a query tile with nothing visible in
   // this call keeps its partial as it is.
   if (p.acc_in_place && n == 0) return;
-  // The work list was written by an earlier kernel and is read-only here:
-  // read it through the constant address space so the loads are scalar and
-  // never wait behind the direct-to-LDS tile loads.
-  typedef const __attribute__((address_space(4))) uint32_t *const_list_t;
-  const const_list_t lst = (const_list_t)(p.list + row * p.nkt);
   const int64_t tile0 = ((int64_t)b * p.hkv + g) * p.nkt;
   const char *kpack = (const char *)p.kpack;
   const char *vpack = (const char *)p.vpack;
@@ -404,7 +414,7 @@ attn_fwd_bf16_kernel(AttnParams p) {
   // statically: while tile it computes from one buffer, tile it+1 streams
   // into the other.
   if (n > 0) {
-    issue(t0, entry_tile(0));
+    issue(t0, min((int)(e0 & 0x7fffffffu), p.nkt - 1));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();

@@ -292,26 +292,31 @@ bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar tile offsets
   const int col = lane & 31, half = lane >> 5;
-  const int hcn = p.group / NH;
+  // One workgroup per item, fewer than 2^31: 32-bit index arithmetic.
+  const uint32_t hcn = (uint32_t)(p.group / NH);
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.nqt * hcn;
-  const int64_t per_xcd = gridDim.x / 8;
-  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (item >= nwork) return;
-  int64_t w = item;
+  const uint32_t per_xcd = gridDim.x / 8;
+  const uint32_t item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if ((int64_t)item >= nwork) return;
+  uint32_t w = item;
   const int hc = (int)(w % hcn);
   w /= hcn;
-  const int qt = (int)(w % p.nqt);
-  w /= p.nqt;
-  const int g = (int)(w % p.hkv);
-  const int b = (int)(w / p.hkv);
+  const int qt = (int)(w % (uint32_t)p.nqt);
+  w /= (uint32_t)p.nqt;
+  const int g = (int)(w % (uint32_t)p.hkv);
+  const int b = (int)(w / (uint32_t)p.hkv);
   const int h = g * p.group + hc * NH + (wave % NH);
   const int tq = qt * BM + (wave / NH) * 32 + col;
   const bool qvalid = tq < p.tq;
 
   const int64_t row = (int64_t)b * p.nqt + qt;
-  const int n = p.count[row];
   typedef const __attribute__((address_space(4))) uint32_t *const_list_t;
   const const_list_t lst = (const_list_t)(p.list + row * p.nkt);
+  // read together with the count (with no key tile the list is empty and the
+  // count's word stands in)
+  const uint32_t e0 = *(p.nkt > 0 ? lst : (const_list_t)(p.count + row));
+  const int n = p.count[row];
+  asm volatile("" ::"s"(e0), "s"(n));   // both loads issued before either is waited for
   const char *pack = (const char *)p.kvpack + ((int64_t)b * p.hkv + g) * p.nkt * TILE;
 
   auto issue = [&](Tile &dst, int kt) __attribute__((always_inline)) {
@@ -430,7 +435,7 @@ bwd_dq_kernel(BwdParams p) {
   // while tile it + 1 streams into the other.
   auto buffer = [&](int i) -> Tile & { return *reinterpret_cast<Tile *>(smem + i * TILE); };
   if (n > 0) {
-    issue(t0, entry_tile(0));
+    issue(t0, (int)(e0 & 0x7fffffffu));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
@@ -505,20 +510,26 @@ bwd_dkdv_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar tile offsets
   const int col = lane & 31, half = lane >> 5;
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.tnk;
-  const int64_t per_xcd = gridDim.x / 8;
-  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (item >= nwork) return;
-  const int kt = (int)(item % p.tnk);
-  const int g = (int)((item / p.tnk) % p.hkv);
-  const int b = (int)(item / ((int64_t)p.tnk * p.hkv));
+  // One workgroup per item, fewer than 2^31: 32-bit index arithmetic.
+  const uint32_t per_xcd = gridDim.x / 8;
+  const uint32_t item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if ((int64_t)item >= nwork) return;
+  const uint32_t rest = item / (uint32_t)p.tnk;
+  const int kt = (int)(item - rest * (uint32_t)p.tnk);
+  const int g = (int)(rest % (uint32_t)p.hkv);
+  const int b = (int)(rest / (uint32_t)p.hkv);
   const int key = kt * KT + wave * 32 + col;
   const bool kvalid = key < p.tk;
 
   const int64_t row = (int64_t)b * p.tnk + kt;
-  const int nq = p.tcount[row];
-  const int n = nq * p.group;         // visits: (query tile, head of the group)
   typedef const __attribute__((address_space(4))) uint32_t *const_list_t;
   const const_list_t lst = (const_list_t)(p.tlist + row * p.tnq);
+  // read together with the count (with no query tile the list is empty and
+  // the count's word stands in)
+  const uint32_t e0 = *(p.tnq > 0 ? lst : (const_list_t)(p.tcount + row));
+  const int nq = p.tcount[row];
+  asm volatile("" ::"s"(e0), "s"(nq));   // both loads issued before either is waited for
+  const int n = nq * p.group;         // visits: (query tile, head of the group)
 
   // Visit it = (head it / nq of the group, query tile it % nq of the list):
   // head by head, so workgroups of neighbouring key tiles (dealt to the same
@@ -695,7 +706,7 @@ bwd_dkdv_kernel(BwdParams p) {
   // the accumulators in one set of registers).
   auto buffer = [&](int i) -> Tile & { return *reinterpret_cast<Tile *>(smem + i * TILE); };
   if (n > 0) {
-    issue(t0, visit_tile(0));
+    issue(t0, ((int64_t)b * p.hq + g * p.group) * p.tnq + (int)(e0 & 0x7fffffffu));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
