@@ -618,12 +618,14 @@ bwd_dkdv_kernel(BwdParams p) {
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(ga + 16 * c),
                                                        *(const bf16x8 *)(vmine + 16 * c), dp, 0, 0, 0);
         }
-        // operand reads three at a time, each group followed by its two products
+        // operand reads three at a time, one group ahead of its two products
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
+        for (int c = 0; c < DC - 1; ++c) {
           __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       } else {
 #pragma unroll
         for (int c = 0; c < DC; ++c)
@@ -676,11 +678,13 @@ bwd_dkdv_kernel(BwdParams p) {
           dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[ch], dv[db], 0, 0, 0);
           dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, df[ch], dk[db], 0, 0, 0);
         }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * DB; ++i) {
+      for (int i = 0; i < 2 * DB - 1; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     } else {
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
