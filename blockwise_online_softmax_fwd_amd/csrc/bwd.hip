@@ -49,6 +49,21 @@ using namespace tiles;
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 16-byte MFMA operand taken across the rows of a row-major LDS block (row
+// stride R elements) with the LDS transpose load, which, in each group of 16
+// lanes, gives lane i the 16-bit element i % 4 of the 8-byte reads of lanes
+// 4j + i / 4, j = 0..3.  When lane 4j + s of the group reads columns
+// c0 + 4s .. c0 + 4s + 3 of row r0 + j, lane i receives column c0 + i of rows
+// r0 .. r0 + 3; the second load, 8 rows further on, gives rows r0 + 8 .. r0 + 11.
+__device__ __forceinline__ bf16x8 tr_operand(const bf16 *lanep, int R) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lanep));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lanep + 8 * R));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 constexpr int BN = kBnBf16;      // keys per tile of the dQ pass
 constexpr int BQ = kBwdQTile;    // queries per tile of the dK/dV pass
 constexpr float kLog2e = 1.4426950408889634f;
@@ -94,7 +109,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 // Row strides (elements) of the padded blocks.
 template <int D> constexpr int kRowN = D + 8;        // [token][d] rows
 constexpr int kRowTK = BN + 8;                       // K^T rows (64 keys)
-constexpr int kRowTQ = BQ + 8;                       // Q^T / dO^T rows (32 queries)
 
 template <int D, int DV>
 struct KvTile {                 // one packed tile of the dQ pass
@@ -106,10 +120,8 @@ struct KvTile {                 // one packed tile of the dQ pass
 
 template <int D, int DV>
 struct QTile {                  // one packed tile of the dK/dV pass
-  bf16 qn[BQ * kRowN<D>];       // [query][d]
-  bf16 don[BQ * kRowN<DV>];     // [query][d]
-  bf16 qt[D * kRowTQ];          // [d][query], token order vt_key
-  bf16 dot[DV * kRowTQ];        // [d][query], token order vt_key
+  bf16 qn[BQ * bwd_qrow(D)];    // [query][d]; the transposed operands are read
+  bf16 don[BQ * bwd_qrow(DV)];  // from these rows with the LDS transpose load
   float lse2[BQ];               // LSE * log2(e); +inf past the end or for a row without keys
   float dsum[BQ];               // rowsum(dO * O)
   int32_t qid[BQ];
@@ -172,11 +184,8 @@ __global__ __launch_bounds__(256) void bwd_pack_kv_kernel(BwdParams p) {
 template <int D, int DV>
 __global__ __launch_bounds__(256) void bwd_pack_q_kernel(BwdParams p) {
   constexpr int QC = D / 8, GC = DV / 8;            // 16-byte data chunks per row of Q, dO
-  constexpr int RN = kRowN<D> / 8, RNG = kRowN<DV> / 8;
-  constexpr int RT = kRowTQ / 8;
+  constexpr int RN = bwd_qrow(D) / 8, RNG = bwd_qrow(DV) / 8;
   static_assert(sizeof(QTile<D, DV>) == bwd_q_tile_bytes(D, DV), "packed Q/dO tile size");
-  __shared__ __attribute__((aligned(16))) bf16 qs[BQ][D + 8];
-  __shared__ __attribute__((aligned(16))) bf16 gs[BQ][DV + 8];
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t tile = ((int64_t)b * p.hq + h) * p.tnq + qt;
@@ -188,17 +197,13 @@ __global__ __launch_bounds__(256) void bwd_pack_q_kernel(BwdParams p) {
     const int r = u / RN, c = u % RN;
     const int t = qt * BQ + r;
     const bool in = t < p.tq && c < QC;
-    const u32x4 qv = in ? *(const u32x4 *)(qb + t * p.q_ts + c * 8) : zero;
-    *(u32x4 *)(out->qn + u * 8) = qv;
-    if (c < QC) *(u32x4 *)&qs[r][c * 8] = qv;
+    *(u32x4 *)(out->qn + u * 8) = in ? *(const u32x4 *)(qb + t * p.q_ts + c * 8) : zero;
   }
   for (int u = tid; u < BQ * RNG; u += 256) {
     const int r = u / RNG, c = u % RNG;
     const int t = qt * BQ + r;
     const bool in = t < p.tq && c < GC;
-    const u32x4 gv = in ? *(const u32x4 *)(gb + t * p.o_ts + c * 8) : zero;
-    *(u32x4 *)(out->don + u * 8) = gv;
-    if (c < GC) *(u32x4 *)&gs[r][c * 8] = gv;
+    *(u32x4 *)(out->don + u * 8) = in ? *(const u32x4 *)(gb + t * p.o_ts + c * 8) : zero;
   }
   if (tid < BQ) {
     const int t = qt * BQ + tid;
@@ -208,33 +213,6 @@ __global__ __launch_bounds__(256) void bwd_pack_q_kernel(BwdParams p) {
     out->dsum[tid] = in ? p.dsum[r] : 0.0f;
     out->qid[tid] = in ? p.qid[b * p.qm_bs + t] : 0;
     out->qpos[tid] = in ? p.qpos[b * p.qm_bs + t] : 0;
-  }
-  __syncthreads();
-  const uint16_t *qsu = (const uint16_t *)&qs[0][0];
-  const uint16_t *gsu = (const uint16_t *)&gs[0][0];
-  for (int u = tid; u < D * RT; u += 256) {
-    const int d = u / RT, c = u % RT;
-    u32x4 oq = zero;
-    if (c < BQ / 8) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t0 = vt_key(c * 8 + 2 * j), t1 = vt_key(c * 8 + 2 * j + 1);
-        oq[j] = (uint32_t)qsu[t0 * (D + 8) + d] | ((uint32_t)qsu[t1 * (D + 8) + d] << 16);
-      }
-    }
-    *(u32x4 *)(out->qt + u * 8) = oq;
-  }
-  for (int u = tid; u < DV * RT; u += 256) {
-    const int d = u / RT, c = u % RT;
-    u32x4 og = zero;
-    if (c < BQ / 8) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t0 = vt_key(c * 8 + 2 * j), t1 = vt_key(c * 8 + 2 * j + 1);
-        og[j] = (uint32_t)gsu[t0 * (DV + 8) + d] | ((uint32_t)gsu[t1 * (DV + 8) + d] << 16);
-      }
-    }
-    *(u32x4 *)(out->dot + u * 8) = og;
   }
 }
 
@@ -509,6 +487,11 @@ bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar tile offsets
   const int col = lane & 31, half = lane >> 5;
+  constexpr int RQ = bwd_qrow(D), RG = bwd_qrow(DV);   // Q and dO row strides in the tile
+  // transpose-load position of this lane: row 4 half + j and columns
+  // 16 (lane / 16 % 2) + 4 s .. + 3, where lane % 16 = 4 j + s
+  const int tr_row = 4 * half + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.tnk;
   // One workgroup per item, fewer than 2^31: 32-bit index arithmetic.
   const uint32_t per_xcd = gridDim.x / 8;
@@ -609,8 +592,8 @@ bwd_dkdv_kernel(BwdParams p) {
     // element r of the accumulator = query row 8(r/4) + 4 half + r%4.
     f32x16 s = {}, dp = {};
     {
-      const bf16 *qa = tl.qn + col * kRowN<D> + 8 * half;
-      const bf16 *ga = tl.don + col * kRowN<DV> + 8 * half;
+      const bf16 *qa = tl.qn + col * RQ + 8 * half;
+      const bf16 *ga = tl.don + col * RG + 8 * half;
       if constexpr (D == DV) {
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
@@ -666,22 +649,28 @@ bwd_dkdv_kernel(BwdParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end).
+    // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end).  The A
+    // operands (rows = head_dim, k = the 16 queries of step ch) are read across
+    // the Q and dO rows with the transpose load: a lane of half h takes the
+    // query rows 16 ch + 8 r + 4 h + j (r = 0, 1; j = 0..3), the order in which
+    // its P and dS values sit in the accumulator layout above.
+    const bf16 *gtr = tl.don + tr_row * RG + tr_col;
+    const bf16 *qtr = tl.qn + tr_row * RQ + tr_col;
     if constexpr (D == DV) {
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int off = (db * 32 + col) * kRowTQ + 16 * ch + 8 * half;
-          const bf16x8 ag = *(const bf16x8 *)(tl.dot + off);
-          const bf16x8 aq = *(const bf16x8 *)(tl.qt + off);
+          const bf16x8 ag = tr_operand(gtr + 16 * ch * RG + 32 * db, RG);
+          const bf16x8 aq = tr_operand(qtr + 16 * ch * RQ + 32 * db, RQ);
           dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[ch], dv[db], 0, 0, 0);
           dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, df[ch], dk[db], 0, 0, 0);
         }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      // operand loads four at a time, one group ahead of their two products
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int i = 0; i < 2 * DB - 1; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -689,17 +678,13 @@ bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
-        for (int db = 0; db < DBV; ++db) {
-          const int off = (db * 32 + col) * kRowTQ + 16 * ch + 8 * half;
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(tl.dot + off), pf[ch],
-                                                           dv[db], 0, 0, 0);
-        }
+        for (int db = 0; db < DBV; ++db)
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(gtr + 16 * ch * RG + 32 * db, RG),
+                                                           pf[ch], dv[db], 0, 0, 0);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int off = (db * 32 + col) * kRowTQ + 16 * ch + 8 * half;
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(tl.qt + off), df[ch],
-                                                           dk[db], 0, 0, 0);
-        }
+        for (int db = 0; db < DB; ++db)
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qtr + 16 * ch * RQ + 32 * db, RQ),
+                                                           df[ch], dk[db], 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);

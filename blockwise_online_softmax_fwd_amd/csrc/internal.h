@@ -135,17 +135,26 @@ constexpr int bwd_kv_waves(int d) { return d == 192 ? 4 : 8; }
 constexpr int bwd_kv_tile(int d) { return 32 * bwd_kv_waves(d); }
 
 // Bytes of one packed K/V tile of the dQ pass (K, V and K^T blocks, ids and
-// positions) and of one packed Q/dO tile of the dK/dV pass (Q, dO, Q^T, dO^T
-// blocks, then LSE*log2(e), rowsum(dO*O), ids and positions).  d is the head
-// dim of Q and K, dv that of V, O and dO.  Every bf16 row carries 8 elements
-// of padding.
+// positions) and of one packed Q/dO tile of the dK/dV pass (Q and dO rows,
+// then LSE*log2(e), rowsum(dO*O), ids and positions).  d is the head dim of Q
+// and K, dv that of V, O and dO.  K/V rows carry 8 elements of padding; a Q or
+// dO row of width w is bwd_qrow(w) elements long (see there).
 constexpr size_t bwd_kv_tile_bytes(int d, int dv) {
   return (size_t)kBnBf16 * (d + 8) * 2 + (size_t)kBnBf16 * (dv + 8) * 2 +
          (size_t)d * (kBnBf16 + 8) * 2 + 2 * kBnBf16 * 4;
 }
+// Row length of the packed Q and dO blocks.  The dK/dV pass reads them two
+// ways: 16-byte pieces of 16 consecutive rows (row-major operands), and, with
+// the LDS transpose load, 8-byte pieces of 4 consecutive rows (transposed
+// operands).  Over 64 four-byte banks the first is free of conflicts when the
+// row stride in words is 4 times an odd number modulo 64, the second when 4
+// consecutive rows start at least 8 words apart modulo 64.  Rows of 128 + 8
+// elements (68 words) fail the second; 128 + 24 (76 words) pass both, as do
+// 64 + 8 (36 words) and 192 + 8 (100 words).
+constexpr int bwd_qrow(int w) { return w == 128 ? w + 24 : w + 8; }
 constexpr size_t bwd_q_tile_bytes(int d, int dv) {
-  return (size_t)kBwdQTile * (d + 8) * 2 + (size_t)kBwdQTile * (dv + 8) * 2 +
-         (size_t)(d + dv) * (kBwdQTile + 8) * 2 + 4 * kBwdQTile * 4;
+  return (size_t)kBwdQTile * bwd_qrow(d) * 2 + (size_t)kBwdQTile * bwd_qrow(dv) * 2 +
+         4 * kBwdQTile * 4;
 }
 
 struct BwdLayout {
