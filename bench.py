@@ -298,10 +298,48 @@ def single_call(w, dev, warmup=2, iters=10):
             "call_TFLOPs": flops / (float(np.median(call_ms)) / 1000.0) / 1e12}
 
 
+def graph_ring(w, dev, inputs, steps=10, warmup=2):
+    """The fused, planned ring step of workload ``w`` captured once as a HIP
+    graph (``RingGraph``) and replayed: wall time per replay over ``steps``
+    replays bracketed by synchronisations, and whether the first replay's
+    output equals the eager driver's bit for bit."""
+    q, k, v, ids, pos = inputs
+    visible = visible_pairs(w, ids, pos, q.dtype)
+    flops = fwd_flops(w, visible)
+    plan = bosf.ring_plan(ids, pos, w.cp_size, w.reorder, w.stripe, num_q_heads=w.num_q_heads,
+                          num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, dtype=q.dtype,
+                          causal=w.causal, window=w.window, v_head_dim=w.dv,
+                          halves=w.reorder == "dual_chunk")
+    t0 = time.perf_counter()
+    graph = bosf.RingGraph(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe, plan=plan,
+                           causal=w.causal, window=w.window)
+    torch.cuda.synchronize()
+    capture_ms = (time.perf_counter() - t0) * 1000.0
+    o_e, l_e = bosf.ring_forward(q, k, v, ids, pos, w.cp_size, w.reorder, w.stripe, plan=plan,
+                                 causal=w.causal, window=w.window)
+    o_g, l_g = graph.replay()
+    same = bool(torch.equal(o_e, o_g) and torch.equal(l_e, l_g))
+    del o_e, l_e
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    del graph
+    return {"ms_per_step": ms, "TFLOPs": flops / (ms / 1000.0) / 1e12,
+            "capture_ms_incl_two_eager_steps": capture_ms, "first_replay_equals_eager": same,
+            "note": "one replay = the whole ring step (reorders, every attention call, folded "
+                    "inverse reorder) launched from a captured HIP graph"}
+
+
 def ring_pipeline(w, dev, steps=10, warmup=2):
     """The sharded workload as 4 shards x (4 attn_fwd + 3 attn_merge), every
     ring step launched (no plan), plus the fused, planned ring of the
-    headline path on the same inputs."""
+    headline path on the same inputs, launched call by call and replayed from
+    a captured HIP graph."""
     inputs = make_inputs(w, dev)
     res = {}
     for name, kw in (("unfused_4fwd_3merge", dict(unfused=True, plan_mode="none")),
@@ -317,6 +355,7 @@ def ring_pipeline(w, dev, steps=10, warmup=2):
         s["step_reorder_ms"] = sum(r["ev"].ms("reorder")) / steps
         s["step_inverse_reorder_ms"] = sum(r["ev"].ms("inverse_reorder")) / steps
         res[name] = s
+    res["fused_planned_graph_replay"] = graph_ring(w, dev, inputs, steps=steps, warmup=warmup)
     res["workload"] = f"{w.name}: {w.describe()}"
     return res
 
@@ -666,6 +705,10 @@ def main():
         s5["ring_plan_ms"] = r5["plan_ms"]
         other[f"w5_ring_{other_kind}{'1' if other_kind == 'striped' else ''}"] = s5
         del r5
+        torch.cuda.empty_cache()
+        log("workload 5 ring step replayed from a captured HIP graph")
+        other["w5_ring_graph_replay"] = graph_ring(get(5), dev, make_inputs(get(5), dev),
+                                                   steps=5, warmup=2)
         torch.cuda.empty_cache()
         for cfg in (2, 4):
             log(f"workload {cfg} (one call)")

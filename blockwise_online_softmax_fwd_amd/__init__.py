@@ -34,5 +34,5 @@ from .ringattn import (  # noqa: F401
     workspace_parts,
     workspace_size,
 )
-from .ring import (RingBuffers, allgather_forward, needs_reordered_q, ring_forward,  # noqa: F401
-                   ring_plan)
+from .ring import (RingBuffers, RingGraph, allgather_forward, needs_reordered_q,  # noqa: F401
+                   ring_forward, ring_plan)

@@ -487,6 +487,71 @@ def ring_forward(q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *
     return o, lse
 
 
+class RingGraph:
+    """One ring step (:func:`ring_forward` with a plan) captured as a HIP graph
+    and replayed with a single launch.
+
+    A ring step is a fixed sequence of library calls for a given segment
+    layout, mask, shard count, reorder and shape: the reorders of K, V and the
+    metadata, every attention call of every rank (each K/V chunk packed by
+    its first call), and the inverse reorder folded into the last calls.  On
+    small shards the step is bound by launching those calls one by one; a
+    replay of the captured graph launches them all at once.
+
+    The constructor copies ``q, k, v, ids, pos`` into tensors the graph owns,
+    runs the step twice eagerly on a side stream (this allocates the driver's
+    buffers and computes the plan's schedules, which the captured calls then
+    reuse, so the graph holds no classification) and captures the third run.
+    :meth:`replay` copies new Q, K, V values (same shapes and dtypes) into the
+    graph's inputs, replays, and returns the graph's ``(o, lse)``: the same
+    tensors every time, overwritten by each replay.  The segment ids and
+    positions are fixed at capture, since the plan is tied to them.  The
+    captured calls allocate nothing and clear nothing with a memset.
+    """
+
+    def __init__(self, q, k, v, ids, pos, cp_size, kind="dual_chunk", stripe_size=1, *, plan,
+                 scale=None, causal=True, window=(-1, -1), partial_dtype=torch.float32,
+                 out_dtype=None):
+        if not isinstance(plan, RingPlan):
+            raise TypeError("plan must come from ring_plan()")
+        if not q.is_cuda:
+            raise ValueError("RingGraph captures GPU work: q must be a device tensor")
+        self.q, self.k, self.v = q.clone(), k.clone(), v.clone()
+        self.ids, self.pos = ids.clone(), pos.clone()
+        self.cp_size = cp_size
+        self._kw = dict(kind=kind, stripe_size=stripe_size, scale=scale, causal=causal,
+                        window=window, plan=plan, partial_dtype=partial_dtype,
+                        out_dtype=out_dtype)
+        self.bufs = RingBuffers.like(self.q, self.k, self.ids, cp_size, partial_dtype, out_dtype,
+                                     v=self.v)
+        dev = q.device
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                self._step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.o, self.lse = self._step()
+
+    def _step(self):
+        return ring_forward(self.q, self.k, self.v, self.ids, self.pos, self.cp_size,
+                            bufs=self.bufs, **self._kw)
+
+    def replay(self, q=None, k=None, v=None):
+        """Copy the given inputs into the graph's own, replay, return ``(o, lse)``."""
+        for name, dst, src in (("q", self.q, q), ("k", self.k, k), ("v", self.v, v)):
+            if src is None:
+                continue
+            if src.shape != dst.shape or src.dtype != dst.dtype or src.device != dst.device:
+                raise ValueError(f"{name}: expected {tuple(dst.shape)} {dst.dtype} on {dst.device}, "
+                                 f"got {tuple(src.shape)} {src.dtype} on {src.device}")
+            dst.copy_(src)
+        self.graph.replay()
+        return self.o, self.lse
+
+
 def allgather_forward(q, k, v, ids, pos, cp_size, kind="striped", stripe_size=512, *, scale=None,
                       causal=True, window=(-1, -1), ranks=None, bufs: RingBuffers | None = None,
                       out_dtype=None, step_hook=None):
