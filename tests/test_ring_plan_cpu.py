@@ -57,3 +57,18 @@ def test_plan_refuses_another_layout_or_mask():
     with pytest.raises(ValueError):
         plan.check(ids2, pos, 4, "dual_chunk", 1, True, (-1, -1))
     assert needs_reordered_q(plan, 4)
+
+
+def test_ring_graph_refuses_before_any_gpu_work():
+    """RingGraph checks its plan and the inputs' device before it allocates
+    or captures anything."""
+    from blockwise_online_softmax_fwd_amd import RingGraph
+    ids, pos = packed_metadata(1, 1024, 2, 400)
+    q = torch.zeros((1, 1024, 4, 64), dtype=torch.bfloat16)
+    k = torch.zeros((1, 1024, 4, 64), dtype=torch.bfloat16)
+    plan = RingPlan(torch.ones((2, 2), dtype=torch.int64), ids, pos, 2, "dual_chunk", 1, True,
+                    (-1, -1))
+    with pytest.raises(TypeError):
+        RingGraph(q, k, k, ids, pos, 2, "dual_chunk", 1, plan=plan.counts)
+    with pytest.raises(ValueError, match="device tensor"):
+        RingGraph(q, k, k, ids, pos, 2, "dual_chunk", 1, plan=plan)
