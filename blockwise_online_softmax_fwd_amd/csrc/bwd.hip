@@ -13,12 +13,13 @@
 //    no key, so its probabilities come out 0 without special cases).
 //  * pack: per 64-key tile of one K/V head, K and V as [key][d] and K^T as
 //    [d][key] (the dQ pass); per 32-query tile of one query head, Q and dO as
-//    [query][d], Q^T and dO^T as [d][query], LSE*log2(e), D, ids and positions
-//    (the dK/dV pass).  Every row is padded by 16 bytes: 16 lanes reading the
-//    same 16-byte column of 16 consecutive rows then hit distinct LDS banks,
-//    and each lane's operand addresses differ by constants only (one address
-//    register per block instead of one per swizzled chunk).  Transposed blocks
-//    use the forward's token order inside 16-token chunks (vt_key).
+//    [query][d], LSE*log2(e), D, ids and positions (the dK/dV pass, which
+//    reads the transposes of Q and dO from those rows with the LDS transpose
+//    load).  Rows are padded instead of swizzled: 16 lanes reading the same
+//    16-byte column of 16 consecutive rows then hit distinct LDS banks, and
+//    each lane's operand addresses differ by constants only (one address
+//    register per block instead of one per swizzled chunk).  The K^T block
+//    uses the forward's token order inside 16-token chunks (vt_key).
 //  * dQ pass: the forward's workgroup shape and work lists.  Per key tile a
 //    wave forms S^T = K Q^T and dP^T = V dO^T, then dS^T, and accumulates
 //    dQ^T += K^T dS^T; S and dP never leave registers.
