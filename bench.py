@@ -51,6 +51,7 @@ from workloads import get, packed_metadata  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s (visible pairs) + % of bf16 MFMA peak, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_F32_VALU_TFLOPS = 157.3     # MI355X fp32 vector (256 CUs x 4 SIMDs x 64 flops/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -269,7 +270,9 @@ def forward_summary(res):
 # ----------------------------------------------------------------------------- other measurements
 
 def single_call(w, dev, warmup=2, iters=10):
-    """One attn_fwd over a whole unsplit workload: call and kernel times."""
+    """One attn_fwd over a whole unsplit workload: call and kernel times; the
+    kernel's rate against the bf16 matrix peak (bf16 inputs) or the fp32 vector
+    peak (fp32 inputs, whose kernel runs on the vector unit)."""
     q, k, v, ids, pos = make_inputs(w, dev)
     visible = visible_pairs(w, ids, pos, q.dtype)
     flops = fwd_flops(w, visible)
@@ -290,11 +293,14 @@ def single_call(w, dev, warmup=2, iters=10):
     call_ms = timed(call, warmup, iters)
     kern_ms = [a.elapsed_time(b) for a, b in kev[warmup:]]
     km = float(np.median(kern_ms))
+    bf16 = w.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_VALU_TFLOPS
     return {"workload": f"{w.name}: {w.describe()}", "visible_pairs": visible, "flops": flops,
             "call_ms_median": float(np.median(call_ms)), "call_ms_min": float(min(call_ms)),
             "kernel_ms_median": km, "kernel_ms_min": float(min(kern_ms)),
             "kernel_TFLOPs": flops / (km / 1000.0) / 1e12,
-            "kernel_frac_of_peak": flops / (km / 1000.0) / 1e12 / PEAK_BF16_TFLOPS,
+            "bound": "mfma" if bf16 else "alu", "peak_TFLOPs": peak,
+            "kernel_frac_of_peak": flops / (km / 1000.0) / 1e12 / peak,
             "call_TFLOPs": flops / (float(np.median(call_ms)) / 1000.0) / 1e12}
 
 
@@ -710,10 +716,15 @@ def main():
         other["w5_ring_graph_replay"] = graph_ring(get(5), dev, make_inputs(get(5), dev),
                                                    steps=5, warmup=2)
         torch.cuda.empty_cache()
-        for cfg in (2, 4):
+        for cfg in (1, 2, 4, 6):
             log(f"workload {cfg} (one call)")
             other[f"w{cfg}_single_call"] = single_call(get(cfg), dev)
             torch.cuda.empty_cache()
+        # the fp32 path (vector unit) at the sliding-window workload's shape
+        w4f = dataclasses.replace(get(4), dtype="f32", name="causal_swa4096_gqa_f32")
+        log("workload 4's shape in fp32 (one call)")
+        other["w4_shape_f32_single_call"] = single_call(w4f, dev, warmup=1, iters=3)
+        torch.cuda.empty_cache()
         log("workload 3 ring pipeline")
         other["w3_ring_pipeline"] = ring_pipeline(get(3), dev)
         torch.cuda.empty_cache()
