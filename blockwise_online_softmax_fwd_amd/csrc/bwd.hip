@@ -15,7 +15,8 @@
 //    [d][key] (the dQ pass); per 32-query tile of one query head, Q and dO as
 //    [query][d], LSE*log2(e), D, ids and positions (the dK/dV pass, which
 //    reads the transposes of Q and dO from those rows with the LDS transpose
-//    load).  Rows are padded instead of swizzled: 16 lanes reading the same
+//    load, and takes a tile's queries in the order bwd_qperm, in which the
+//    per-query values are stored).  Rows are padded instead of swizzled: 16 lanes reading the same
 //    16-byte column of 16 consecutive rows then hit distinct LDS banks, and
 //    each lane's operand addresses differ by constants only (one address
 //    register per block instead of one per swizzled chunk).  The K^T block
@@ -57,12 +58,24 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // stride R elements) with the LDS transpose load, which, in each group of 16
 // lanes, gives lane i the 16-bit element i % 4 of the 8-byte reads of lanes
 // 4j + i / 4, j = 0..3.  When lane 4j + s of the group reads columns
-// c0 + 4s .. c0 + 4s + 3 of row r0 + j, lane i receives column c0 + i of rows
-// r0 .. r0 + 3; the second load, 8 rows further on, gives rows r0 + 8 .. r0 + 11.
+// c0 + 4s .. c0 + 4s + 3 of row r_j, lane i receives column c0 + i of rows
+// r_0 .. r_3; the second load, 2 rows further on, gives rows r_j + 2.
 __device__ __forceinline__ bf16x8 tr_operand(const bf16 *lanep, int R) {
   const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lanep));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lanep + 8 * R));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lanep + 2 * R));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Query order of the dK/dV pass inside a 32-query tile.  Row i of the score
+// accumulator (A-operand lane i, i = 16c + 8b + 4h + j) holds query
+// 16c + 4j + 2b + h of the tile.  The transposed operands of step c, half h,
+// then take rows 4j + (const) of the packed block, 4 rows apart, and the
+// row-major operands of lanes 0..15 (or 16..31) still take 16 distinct rows of
+// one 16-row half; both read patterns are then free of bank conflicts with
+// rows of w + 8 elements.  The packed tile keeps Q and dO in token order and
+// stores its per-query values (LSE, D, ids, positions) in this order.
+__host__ __device__ constexpr int bwd_qperm(int i) {
+  return (i & 16) | ((i & 3) << 2) | (((i >> 3) & 1) << 1) | ((i >> 2) & 1);
 }
 
 constexpr int BN = kBnBf16;      // keys per tile of the dQ pass
@@ -206,8 +219,8 @@ __global__ __launch_bounds__(256) void bwd_pack_q_kernel(BwdParams p) {
     const bool in = t < p.tq && c < GC;
     *(u32x4 *)(out->don + u * 8) = in ? *(const u32x4 *)(gb + t * p.o_ts + c * 8) : zero;
   }
-  if (tid < BQ) {
-    const int t = qt * BQ + tid;
+  if (tid < BQ) {   // per-query values in the pass's query order
+    const int t = qt * BQ + bwd_qperm(tid);
     const bool in = t < p.tq;
     const int64_t r = ((int64_t)b * p.tq + t) * p.hq + h;
     out->lse2[tid] = in ? p.lse2[r] : INFINITY;
@@ -489,9 +502,9 @@ bwd_dkdv_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar tile offsets
   const int col = lane & 31, half = lane >> 5;
   constexpr int RQ = bwd_qrow(D), RG = bwd_qrow(DV);   // Q and dO row strides in the tile
-  // transpose-load position of this lane: row 4 half + j and columns
-  // 16 (lane / 16 % 2) + 4 s .. + 3, where lane % 16 = 4 j + s
-  const int tr_row = 4 * half + ((lane & 15) >> 2);
+  // transpose-load position of this lane: row 4 j + half and columns
+  // 16 (lane / 16 % 2) + 4 s .. + 3, where lane % 16 = 4 j + s (bwd_qperm)
+  const int tr_row = 4 * ((lane & 15) >> 2) + half;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.tnk;
   // One workgroup per item, fewer than 2^31: 32-bit index arithmetic.
@@ -590,11 +603,13 @@ bwd_dkdv_kernel(BwdParams p) {
 
   auto compute = [&](const Tile &tl, bool masked) __attribute__((always_inline)) {
     // S = Q K^T and dP = dO V^T for the 32 queries of the tile: lane = key,
-    // element r of the accumulator = query row 8(r/4) + 4 half + r%4.
+    // element r of the accumulator = row 8(r/4) + 4 half + r%4, which holds
+    // query bwd_qperm(row) of the tile; the per-query values sit in row order.
     f32x16 s = {}, dp = {};
     {
-      const bf16 *qa = tl.qn + col * RQ + 8 * half;
-      const bf16 *ga = tl.don + col * RG + 8 * half;
+      const int qrow = bwd_qperm(col);
+      const bf16 *qa = tl.qn + qrow * RQ + 8 * half;
+      const bf16 *ga = tl.don + qrow * RG + 8 * half;
       if constexpr (D == DV) {
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
@@ -653,8 +668,9 @@ bwd_dkdv_kernel(BwdParams p) {
     // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end).  The A
     // operands (rows = head_dim, k = the 16 queries of step ch) are read across
     // the Q and dO rows with the transpose load: a lane of half h takes the
-    // query rows 16 ch + 8 r + 4 h + j (r = 0, 1; j = 0..3), the order in which
-    // its P and dS values sit in the accumulator layout above.
+    // accumulator rows 16 ch + 8 r + 4 h + j (r = 0, 1; j = 0..3), the order in
+    // which its P and dS values sit in the accumulator layout above, i.e. the
+    // packed rows 16 ch + 4 j + 2 r + h.
     const bf16 *gtr = tl.don + tr_row * RG + tr_col;
     const bf16 *qtr = tl.qn + tr_row * RQ + tr_col;
     if constexpr (D == DV) {

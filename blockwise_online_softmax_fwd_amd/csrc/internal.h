@@ -143,15 +143,16 @@ constexpr size_t bwd_kv_tile_bytes(int d, int dv) {
   return (size_t)kBnBf16 * (d + 8) * 2 + (size_t)kBnBf16 * (dv + 8) * 2 +
          (size_t)d * (kBnBf16 + 8) * 2 + 2 * kBnBf16 * 4;
 }
-// Row length of the packed Q and dO blocks.  The dK/dV pass reads them two
-// ways: 16-byte pieces of 16 consecutive rows (row-major operands), and, with
-// the LDS transpose load, 8-byte pieces of 4 consecutive rows (transposed
-// operands).  Over 64 four-byte banks the first is free of conflicts when the
-// row stride in words is 4 times an odd number modulo 64, the second when 4
-// consecutive rows start at least 8 words apart modulo 64.  Rows of 128 + 8
-// elements (68 words) fail the second; 128 + 24 (76 words) pass both, as do
-// 64 + 8 (36 words) and 192 + 8 (100 words).
-constexpr int bwd_qrow(int w) { return w == 128 ? w + 24 : w + 8; }
+// Row length of the packed Q and dO blocks: 8 elements of padding.  The dK/dV
+// pass reads them two ways: 16-byte pieces of 16 rows (row-major operands) and,
+// with the LDS transpose load, 8-byte pieces of 4 rows, 32 lanes of which (two
+// neighbouring 32-byte column pieces of the same 4 rows) are served together.
+// Over 64 four-byte banks the first is free of conflicts when the 16 rows start
+// 4 words apart modulo 64, the second when the 4 rows start 16 words apart.
+// Rows of w + 8 elements (68, 36 or 100 words for w = 128, 64, 192) pass the
+// first for any 16 consecutive rows and the second for rows 4 apart, which is
+// the order in which the pass takes the queries of a tile (bwd_qperm).
+constexpr int bwd_qrow(int w) { return w + 8; }
 constexpr size_t bwd_q_tile_bytes(int d, int dv) {
   return (size_t)kBwdQTile * bwd_qrow(d) * 2 + (size_t)kBwdQTile * bwd_qrow(dv) * 2 +
          4 * kBwdQTile * 4;

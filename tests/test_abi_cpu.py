@@ -438,9 +438,9 @@ def _bwd(lib, d, ws_bytes=1 << 34, grad=ra.RA_F32, **over):
 def test_bwd_workspace_size():
     d = _desc(q_len=4096, kv_len=4096)
     n = ra.bwd_workspace_size(d)
-    # packed Q and dO rows alone (2 batch rows x Tq x Hq rows of 152 bf16 each, 128 of
+    # packed Q and dO rows alone (2 batch rows x Tq x Hq rows of 136 bf16 each, 128 of
     # data plus padding), plus the packed K/V tiles (K, V and K^T per key tile)
-    q_rows = 2 * 2 * 4096 * 16 * 152 * 2
+    q_rows = 2 * 2 * 4096 * 16 * 136 * 2
     kv_tiles = 2 * 2 * (4096 // 64) * (64 * 136 * 2 * 2 + 128 * 72 * 2)
     assert n > q_rows + kv_tiles
     assert ra.bwd_workspace_size(_desc(q_len=64, kv_len=64)) < n
