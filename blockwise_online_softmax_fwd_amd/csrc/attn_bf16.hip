@@ -350,8 +350,8 @@ attn_fwd_bf16_kernel(AttnParams p) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int kk = kb * 32 + 8 * r4 + 4 * half;
-          const int4 ids = *(const int4 *)&tl.meta[kk];
-          const int4 pss = *(const int4 *)&tl.meta[BN + kk];
+          const i32x4 ids = *(const i32x4 *)&tl.meta[kk];
+          const i32x4 pss = *(const i32x4 *)&tl.meta[BN + kk];
           s[kb][4 * r4 + 0] = lm(ids.x, pss.x) ? s[kb][4 * r4 + 0] : -INFINITY;
           s[kb][4 * r4 + 1] = lm(ids.y, pss.y) ? s[kb][4 * r4 + 1] : -INFINITY;
           s[kb][4 * r4 + 2] = lm(ids.z, pss.z) ? s[kb][4 * r4 + 2] : -INFINITY;

@@ -15,6 +15,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Per-token ids and positions are read from LDS as this vector type, not as
+// HIP's int4 struct: the compiler puts a wait for every LDS DMA in flight in
+// front of a struct read, but not in front of a vector read.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // Token (0..15) stored at column x (0..15) of a 16-token chunk of a transposed
 // block.  In the accumulator of v_mfma_f32_32x32x16_bf16 a lane of half h holds

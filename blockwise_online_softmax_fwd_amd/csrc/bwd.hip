@@ -60,7 +60,12 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // 4j + i / 4, j = 0..3.  When lane 4j + s of the group reads columns
 // c0 + 4s .. c0 + 4s + 3 of row r_j, lane i receives column c0 + i of rows
 // r_0 .. r_3; the second load, 2 rows further on, gives rows r_j + 2.
-__device__ __forceinline__ bf16x8 tr_operand(const bf16 *lanep, int R) {
+//
+// The block is published by an explicit wait for the tile loads and a
+// barrier.  The compiler would also wait for every LDS DMA still in flight
+// (the next tile's, into another buffer) before a transpose load; through a
+// restrict pointer it does not.
+__device__ __forceinline__ bf16x8 tr_operand(const bf16 *__restrict__ lanep, int R) {
   const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lanep));
   const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lanep + 2 * R));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -396,8 +401,8 @@ bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int kk = kb * 32 + 8 * r4 + 4 * half;
-          const int4 ids = *(const int4 *)&tl.meta[kk];
-          const int4 pss = *(const int4 *)&tl.meta[BN + kk];
+          const i32x4 ids = *(const i32x4 *)&tl.meta[kk];
+          const i32x4 pss = *(const i32x4 *)&tl.meta[BN + kk];
           s[4 * r4 + 0] = lm(ids.x, pss.x) ? s[4 * r4 + 0] : -INFINITY;
           s[4 * r4 + 1] = lm(ids.y, pss.y) ? s[4 * r4 + 1] : -INFINITY;
           s[4 * r4 + 2] = lm(ids.z, pss.z) ? s[4 * r4 + 2] : -INFINITY;
@@ -640,8 +645,8 @@ bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int qq = 8 * r4 + 4 * half;
-        const int4 ids = *(const int4 *)&tl.qid[qq];
-        const int4 pss = *(const int4 *)&tl.qpos[qq];
+        const i32x4 ids = *(const i32x4 *)&tl.qid[qq];
+        const i32x4 pss = *(const i32x4 *)&tl.qpos[qq];
         s[4 * r4 + 0] = km(ids.x, pss.x) ? s[4 * r4 + 0] : -INFINITY;
         s[4 * r4 + 1] = km(ids.y, pss.y) ? s[4 * r4 + 1] : -INFINITY;
         s[4 * r4 + 2] = km(ids.z, pss.z) ? s[4 * r4 + 2] : -INFINITY;
