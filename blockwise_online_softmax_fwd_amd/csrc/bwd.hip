@@ -536,15 +536,11 @@ bwd_dkdv_kernel(BwdParams p) {
   // Visit it = (head it / nq of the group, query tile it % nq of the list):
   // head by head, so workgroups of neighbouring key tiles (dealt to the same
   // XCD) read the same Q tiles within a few visits of each other.
-  auto visit_tile = [&](int it) {
-    const int hi = it / nq;
-    const int qtile = (int)(lst[it - hi * nq] & 0x7fffffffu);
-    const int h = g * p.group + hi;
-    return ((int64_t)b * p.hq + h) * p.tnq + qtile;
+  auto entry_tile = [&](int hi, uint32_t e) {
+    return ((int64_t)b * p.hq + g * p.group + hi) * p.tnq + (int)(e & 0x7fffffffu);
   };
   const bool ragged_q = (p.tq % BQ) != 0;
-  auto visit_masked = [&](int it) {
-    const uint32_t e = lst[it % nq];
+  auto entry_masked = [&](uint32_t e) {
     return (e >> 31) != 0 || (ragged_q && (int)(e & 0x7fffffffu) == p.tnq - 1) || !kvalid;
   };
   auto issue = [&](Tile &dst, int64_t tile) __attribute__((always_inline)) {
@@ -606,7 +602,11 @@ bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dv[db][r] = 0.0f;
 
-  auto compute = [&](const Tile &tl, bool masked) __attribute__((always_inline)) {
+  // dst / next: the buffer and tile of the next visit (next < 0: none), whose
+  // loads are issued between P / dS and the two accumulations, so the load
+  // path is busy while this wave runs its products rather than at the top of
+  // the visit, when every wave issues at once.
+  auto compute = [&](const Tile &tl, bool masked, Tile &dst, int64_t next) __attribute__((always_inline)) {
     // S = Q K^T and dP = dO V^T for the 32 queries of the tile: lane = key,
     // element r of the accumulator = row 8(r/4) + 4 half + r%4, which holds
     // query bwd_qperm(row) of the tile; the per-query values sit in row order.
@@ -670,6 +670,8 @@ bwd_dkdv_kernel(BwdParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (next >= 0) issue(dst, next);
+    __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end).  The A
     // operands (rows = head_dim, k = the 16 queries of step ch) are read across
     // the Q and dO rows with the transpose load: a lane of half h takes the
@@ -714,18 +716,41 @@ bwd_dkdv_kernel(BwdParams p) {
 
   // Double-buffered loop with one body: visit it computes from buffer it & 1
   // while visit it + 1 streams into the other (a single copy of the body keeps
-  // the accumulators in one set of registers).
+  // the accumulators in one set of registers); the other buffer was last read
+  // before the previous barrier.
   auto buffer = [&](int i) -> Tile & { return *reinterpret_cast<Tile *>(smem + i * TILE); };
+  //
+  // The list entry of visit it + 2 is loaded during visit it, as a vector load
+  // (the index is forced into a vector register), so the end-of-visit wait
+  // for the tile covers it and no scalar load is left in flight among the LDS
+  // reads; (head, list position) advance by counters.
   if (n > 0) {
-    issue(t0, ((int64_t)b * p.hq + g * p.group) * p.tnq + (int)(e0 & 0x7fffffffu));
+    issue(t0, entry_tile(0, e0));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
+  const uint32_t *lst_v = p.tlist + row * p.tnq;
+  uint32_t ecur = e0;                      // entry of visit it
+  int h1 = nq == 1 ? 1 : 0, q1 = nq == 1 ? 0 : 1;   // visit it + 1
+  uint32_t e1v = 0;                        // its entry, in every lane
+  if (n > 1) e1v = lst_v[q1];
   for (int it = 0; it < n; ++it) {
     const int cur = it & 1;
-    if (it + 1 < n) issue(buffer(cur ^ 1), visit_tile(it + 1));
+    const uint32_t e1 = __builtin_amdgcn_readfirstlane(e1v);
+    const int64_t next = it + 1 < n ? entry_tile(h1, e1) : -1;
+    const bool masked = entry_masked(ecur);
+    ecur = e1;
+    if (++q1 == nq) {
+      q1 = 0;
+      ++h1;
+    }
+    if (it + 2 < n) {
+      int qv = q1;
+      asm volatile("" : "+v"(qv));
+      e1v = lst_v[qv];
+    }
     __builtin_amdgcn_sched_barrier(0);
-    compute(buffer(cur), visit_masked(it));
+    compute(buffer(cur), masked, buffer(cur ^ 1), next);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
