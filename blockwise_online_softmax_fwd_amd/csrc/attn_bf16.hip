@@ -190,15 +190,15 @@ attn_fwd_bf16_kernel(AttnParams p) {
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  // Work item; consecutive items stay on one XCD (blocks are dealt to the 8
-  // XCDs round-robin, each XCD takes one contiguous run of items).
-  // The launch has one workgroup per item (fewer than 2^31 of them), so the
-  // index arithmetic is 32-bit: a 64-bit division is a long scalar routine.
+  // Work item (xcd_item): (b, g, query tile, head chunk), head chunk fastest.
   const uint32_t hcn = (uint32_t)(p.group / NH);
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.nqt * hcn;
-  const uint32_t per_xcd = gridDim.x / 8;
-  const uint32_t item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if ((int64_t)item >= nwork) return;
+  const int64_t item_or_none = xcd_item(nwork, [&](uint32_t it) {
+    const uint32_t r = it / hcn;   // (b, g, qt) with qt fastest
+    return p.count[(r / ((uint32_t)p.nqt * (uint32_t)p.hkv)) * (uint32_t)p.nqt + r % (uint32_t)p.nqt];
+  });
+  if (item_or_none < 0) return;
+  const uint32_t item = (uint32_t)item_or_none;
   uint32_t w = item;
   const int hc = (int)(w % hcn);
   w /= hcn;

@@ -289,13 +289,15 @@ bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar tile offsets
   const int col = lane & 31, half = lane >> 5;
-  // One workgroup per item, fewer than 2^31: 32-bit index arithmetic.
+  // Work item (xcd_item): (b, g, query tile, head chunk), head chunk fastest.
   const uint32_t hcn = (uint32_t)(p.group / NH);
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.nqt * hcn;
-  const uint32_t per_xcd = gridDim.x / 8;
-  const uint32_t item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if ((int64_t)item >= nwork) return;
-  uint32_t w = item;
+  const int64_t item_or_none = xcd_item(nwork, [&](uint32_t it) {
+    const uint32_t r = it / hcn;   // (b, g, qt) with qt fastest
+    return p.count[(r / ((uint32_t)p.nqt * (uint32_t)p.hkv)) * (uint32_t)p.nqt + r % (uint32_t)p.nqt];
+  });
+  if (item_or_none < 0) return;
+  uint32_t w = (uint32_t)item_or_none;
   const int hc = (int)(w % hcn);
   w /= hcn;
   const int qt = (int)(w % (uint32_t)p.nqt);
@@ -511,11 +513,13 @@ bwd_dkdv_kernel(BwdParams p) {
   // 16 (lane / 16 % 2) + 4 s .. + 3, where lane % 16 = 4 j + s (bwd_qperm)
   const int tr_row = 4 * ((lane & 15) >> 2) + half;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Work item (xcd_item): (b, g, key tile), key tile fastest.
   const int64_t nwork = (int64_t)p.batch * p.hkv * p.tnk;
-  // One workgroup per item, fewer than 2^31: 32-bit index arithmetic.
-  const uint32_t per_xcd = gridDim.x / 8;
-  const uint32_t item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if ((int64_t)item >= nwork) return;
+  const int64_t item_or_none = xcd_item(nwork, [&](uint32_t it) {
+    return p.tcount[(it / ((uint32_t)p.tnk * (uint32_t)p.hkv)) * (uint32_t)p.tnk + it % (uint32_t)p.tnk];
+  });
+  if (item_or_none < 0) return;
+  const uint32_t item = (uint32_t)item_or_none;
   const uint32_t rest = item / (uint32_t)p.tnk;
   const int kt = (int)(item - rest * (uint32_t)p.tnk);
   const int g = (int)(rest % (uint32_t)p.hkv);
