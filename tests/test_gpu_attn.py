@@ -52,6 +52,10 @@ SMALL = [
     (2, 300, 517, 16, 2, 128, "bf16", True, (-1, -1), False),
     (1, 517, 300, 8, 2, 64, "bf16", False, (50, 50), False),
     (2, 64, 640, 16, 1, 128, "bf16", True, (200, 0), False),
+    # 45 work items in runs of 6: counts rise along each run, so the runs are
+    # dealt in reverse, the last one with 3 items and 3 positions past the end
+    (1, 1440, 1440, 8, 1, 128, "bf16", True, (-1, -1), True),
+    (1, 1440, 1440, 8, 1, 128, "bf16", True, (300, 0), True),
     (1, 256, 256, 4, 4, 64, "f32", True, (-1, -1), True),
     (2, 111, 111, 4, 2, 128, "f32", True, (20, 0), True),
     (1, 99, 140, 6, 1, 64, "f32", False, (-1, 3), False),

@@ -74,6 +74,10 @@ SMALL = [
     (1, 517, 300, 8, 2, 64, False, (50, 50), False),
     (2, 64, 640, 16, 1, 128, True, (200, 0), False),
     (1, 700, 45, 4, 2, 128, False, (-1, -1), False),
+    # dK/dV pass: 45 key-tile items in runs of 6, later keys seen by more
+    # queries (window (0, -1)), so runs are dealt in reverse, the last one
+    # with 3 items and 3 positions past the end
+    (5, 2304, 2304, 8, 1, 64, False, (0, -1), True),
 ]
 
 
