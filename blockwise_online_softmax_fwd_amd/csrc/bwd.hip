@@ -364,9 +364,7 @@ bwd_dq_kernel(BwdParams p) {
     }
   }
   const bool ragged = (p.tk % BN) != 0;
-  auto entry_tile = [&](int it) { return (int)(lst[it] & 0x7fffffffu); };
-  auto entry_masked = [&](int it) {
-    const uint32_t e = lst[it];
+  auto entry_masked = [&](uint32_t e) {
     return (e >> 31) != 0 || (ragged && (int)(e & 0x7fffffffu) == p.nkt - 1);
   };
   const float c2 = p.scale_log2;
@@ -393,7 +391,9 @@ bwd_dq_kernel(BwdParams p) {
   // One tile, one 32-key block at a time: S^T and dP^T, the mask (boundary
   // tiles only), dS^T = P^T (dP^T - D) with P^T = 2^(s c2 - LSE log2 e) packed
   // to bf16 B operands, then dQ^T += K^T dS^T over the block's two 16-key chunks.
-  auto compute = [&](const Tile &tl, bool masked) __attribute__((always_inline)) {
+  // The next tile (next >= 0) streams into dst from between the two blocks,
+  // rather than from the top of the tile, when every wave issues at once.
+  auto compute = [&](const Tile &tl, bool masked, Tile &dst, int next) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s, dp;
@@ -427,22 +427,39 @@ bwd_dq_kernel(BwdParams p) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (kb == 0 && next >= 0) issue(dst, next);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Double-buffered loop with one body: tile it computes from buffer it & 1
-  // while tile it + 1 streams into the other.
+  // while tile it + 1 streams into the other (last read before the previous
+  // barrier).  The list entry of tile it + 2 is loaded during tile it as a
+  // vector load (the index is forced into a vector register), so the
+  // end-of-tile wait covers it and no scalar load sits among the LDS reads.
   auto buffer = [&](int i) -> Tile & { return *reinterpret_cast<Tile *>(smem + i * TILE); };
   if (n > 0) {
     issue(t0, (int)(e0 & 0x7fffffffu));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
+  const uint32_t *lst_v = p.list + row * p.nkt;
+  uint32_t ecur = e0;            // entry of tile it
+  uint32_t e1v = 0;              // entry of tile it + 1, in every lane
+  if (n > 1) e1v = lst_v[1];
   for (int it = 0; it < n; ++it) {
     const int cur = it & 1;
-    if (it + 1 < n) issue(buffer(cur ^ 1), entry_tile(it + 1));
+    const uint32_t e1 = __builtin_amdgcn_readfirstlane(e1v);
+    const int next = it + 1 < n ? (int)(e1 & 0x7fffffffu) : -1;
+    const bool masked = entry_masked(ecur);
+    ecur = e1;
+    if (it + 2 < n) {
+      int qv = it + 2;
+      asm volatile("" : "+v"(qv));
+      e1v = lst_v[qv];
+    }
     __builtin_amdgcn_sched_barrier(0);
-    compute(buffer(cur), entry_masked(it));
+    compute(buffer(cur), masked, buffer(cur ^ 1), next);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
