@@ -35,6 +35,7 @@
 
 #include "bf16_tiles.h"
 #include "internal.h"
+#include "xcd_order.h"
 #include "lse_merge.h"
 
 namespace ra {

@@ -32,6 +32,7 @@
 #include <math.h>
 
 #include "internal.h"
+#include "xcd_order.h"
 #include "lse_merge.h"
 
 namespace ra {
@@ -89,8 +90,13 @@ attn_fwd_f32_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
-  // one workgroup per item (fewer than 2^31): 32-bit index arithmetic
-  uint32_t w = blockIdx.x;
+  // Work item (xcd_item): (b, h, query tile), query tile fastest.
+  const int64_t nwork = (int64_t)p.batch * p.hq * p.nqt;
+  const int64_t item_or_none = xcd_item(nwork, [&](uint32_t it) {
+    return p.count[(it / ((uint32_t)p.nqt * (uint32_t)p.hq)) * (uint32_t)p.nqt + it % (uint32_t)p.nqt];
+  });
+  if (item_or_none < 0) return;
+  uint32_t w = (uint32_t)item_or_none;
   const int qt = (int)(w % (uint32_t)p.nqt);
   w /= (uint32_t)p.nqt;
   const int h = (int)(w % (uint32_t)p.hq);
@@ -289,11 +295,12 @@ template <int D>
 hipError_t launch_d(const AttnParams &p, bool out_bf16, hipStream_t stream) {
   const int64_t nwork = (int64_t)p.batch * p.hq * p.nqt;
   if (nwork == 0) return hipSuccess;
+  const int64_t grid = (nwork + 7) / 8 * 8;   // whole runs for the 8 XCDs (xcd_item)
   if (out_bf16)
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, true>), dim3((unsigned)nwork), dim3(128), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, true>), dim3((unsigned)grid), dim3(128), 0, stream,
                        p);
   else
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, false>), dim3((unsigned)nwork), dim3(128), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, false>), dim3((unsigned)grid), dim3(128), 0, stream,
                        p);
   return hipGetLastError();
 }

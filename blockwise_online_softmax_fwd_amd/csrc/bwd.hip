@@ -43,6 +43,7 @@
 
 #include "bf16_tiles.h"
 #include "internal.h"
+#include "xcd_order.h"
 
 namespace ra {
 namespace {
