@@ -90,36 +90,52 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ----------------------------------------------------------------------------- prep
 
-// DV: head dim of O and dO.
+// DV: head dim of O and dO.  Token by token: the hq rows of a token are
+// contiguous, so a row's index needs no division; several rows per thread
+// are in flight at once.
 template <int DV, bool OBF>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   constexpr int TPR = DV / 4;      // threads per row, 4 elements each
   constexpr int RPB = 256 / TPR;   // rows per block and step
-  const int64_t rows = (int64_t)p.batch * p.tq * p.hq;
+  constexpr int UN = 8;            // steps whose loads are issued together
+  const int64_t tokens = (int64_t)p.batch * p.tq;
   const int sub = threadIdx.x % TPR;
-  const int64_t per_b = (int64_t)p.tq * p.hq;
-  for (int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR; r < rows;
-       r += (int64_t)gridDim.x * RPB) {
-    const int64_t b = r / per_b, rr = r - b * per_b;   // rr = t * hq + h
-    const int64_t t = rr / p.hq, h = rr - t * p.hq;
-    const int64_t col = t * p.o_ts + h * DV + sub * 4;
-    const bf16x4 dov = *(const bf16x4 *)((const bf16 *)p.dout + b * p.do_bs + col);
-    float dot = 0.0f;
-    if (OBF) {
-      const bf16x4 ov = *(const bf16x4 *)((const bf16 *)p.o + b * p.o_bs + col);
+  const int hq = p.hq;
+  for (int64_t tok = blockIdx.x; tok < tokens; tok += gridDim.x) {
+    const int64_t b = tok / p.tq, t = tok - b * p.tq;
+    const bf16 *dob = (const bf16 *)p.dout + b * p.do_bs + t * p.o_ts + sub * 4;
+    const int64_t ooff = b * p.o_bs + t * p.o_ts + sub * 4;
+    for (int h0 = threadIdx.x / TPR; h0 < hq; h0 += RPB * UN) {
+      float dot[UN];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dot = fmaf((float)dov[e], (float)ov[e], dot);
-    } else {
-      const f32x4 ov = *(const f32x4 *)((const float *)p.o + b * p.o_bs + col);
+      for (int u = 0; u < UN; ++u) {
+        const int h = h0 + u * RPB;
+        dot[u] = 0.0f;
+        if (h < hq) {
+          const bf16x4 dov = *(const bf16x4 *)(dob + (int64_t)h * DV);
+          if (OBF) {
+            const bf16x4 ov = *(const bf16x4 *)((const bf16 *)p.o + ooff + (int64_t)h * DV);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dot = fmaf((float)dov[e], ov[e], dot);
-    }
+            for (int e = 0; e < 4; ++e) dot[u] = fmaf((float)dov[e], (float)ov[e], dot[u]);
+          } else {
+            const f32x4 ov = *(const f32x4 *)((const float *)p.o + ooff + (int64_t)h * DV);
 #pragma unroll
-    for (int off = TPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, TPR);
-    if (sub == 0) {
-      const float l = p.lse[b * p.lse_bs + rr];
-      p.dsum[r] = dot;
-      p.lse2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
+            for (int e = 0; e < 4; ++e) dot[u] = fmaf((float)dov[e], ov[e], dot[u]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int h = h0 + u * RPB;   // the same for the TPR lanes of a row
+#pragma unroll
+        for (int off = TPR / 2; off > 0; off >>= 1) dot[u] += __shfl_xor(dot[u], off, TPR);
+        if (sub == 0 && h < hq) {
+          const int64_t r = tok * hq + h;
+          const float l = p.lse[b * p.lse_bs + t * hq + h];
+          p.dsum[r] = dot[u];
+          p.lse2[r] = l == -INFINITY ? INFINITY : l * kLog2e;
+        }
+      }
     }
   }
 }
@@ -206,25 +222,40 @@ __global__ __launch_bounds__(256) void bwd_pack_q_kernel(BwdParams p) {
   constexpr int QC = D / 8, GC = DV / 8;            // 16-byte data chunks per row of Q, dO
   constexpr int RN = bwd_qrow(D) / 8, RNG = bwd_qrow(DV) / 8;
   static_assert(sizeof(QTile<D, DV>) == bwd_q_tile_bytes(D, DV), "packed Q/dO tile size");
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // heads fastest: neighbouring blocks read neighbouring pieces of the same
+  // token rows and of the same lines of the per-row values
+  const int h = blockIdx.x, qt = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t tile = ((int64_t)b * p.hq + h) * p.tnq + qt;
   QTile<D, DV> *out = (QTile<D, DV> *)((char *)p.qpack + tile * sizeof(QTile<D, DV>));
   const bf16 *qb = (const bf16 *)p.q + b * p.q_bs + (int64_t)h * D;
   const bf16 *gb = (const bf16 *)p.dout + b * p.do_bs + (int64_t)h * DV;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int u = tid; u < BQ * RN; u += 256) {
+  // every load of this thread is issued before its first store
+  constexpr int NQ = (BQ * RN + 255) / 256, NG = (BQ * RNG + 255) / 256;
+  u32x4 qv[NQ], gv[NG];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int u = tid + 256 * i;
     const int r = u / RN, c = u % RN;
     const int t = qt * BQ + r;
-    const bool in = t < p.tq && c < QC;
-    *(u32x4 *)(out->qn + u * 8) = in ? *(const u32x4 *)(qb + t * p.q_ts + c * 8) : zero;
+    const bool in = u < BQ * RN && t < p.tq && c < QC;
+    qv[i] = in ? *(const u32x4 *)(qb + t * p.q_ts + c * 8) : zero;
   }
-  for (int u = tid; u < BQ * RNG; u += 256) {
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int u = tid + 256 * i;
     const int r = u / RNG, c = u % RNG;
     const int t = qt * BQ + r;
-    const bool in = t < p.tq && c < GC;
-    *(u32x4 *)(out->don + u * 8) = in ? *(const u32x4 *)(gb + t * p.o_ts + c * 8) : zero;
+    const bool in = u < BQ * RNG && t < p.tq && c < GC;
+    gv[i] = in ? *(const u32x4 *)(gb + t * p.o_ts + c * 8) : zero;
   }
+#pragma unroll
+  for (int i = 0; i < NQ; ++i)
+    if (tid + 256 * i < BQ * RN) *(u32x4 *)(out->qn + (tid + 256 * i) * 8) = qv[i];
+#pragma unroll
+  for (int i = 0; i < NG; ++i)
+    if (tid + 256 * i < BQ * RNG) *(u32x4 *)(out->don + (tid + 256 * i) * 8) = gv[i];
   if (tid < BQ) {   // per-query values in the pass's query order
     const int t = qt * BQ + bwd_qperm(tid);
     const bool in = t < p.tq;
@@ -889,11 +920,9 @@ BwdLayout bwd_workspace_layout(int32_t batch, int32_t tq, int32_t hq, int32_t hk
 
 hipError_t launch_bwd_prep(const BwdParams &p, int32_t v_head_dim, bool o_bf16,
                            hipStream_t stream) {
-  const int64_t rows = (int64_t)p.batch * p.tq * p.hq;
-  if (rows == 0) return hipSuccess;
-  const int64_t rpb = 256 / (v_head_dim / 4);
-  int64_t blocks = (rows + rpb - 1) / rpb;
-  if (blocks > 16384) blocks = 16384;
+  const int64_t tokens = (int64_t)p.batch * p.tq;
+  if (tokens == 0 || p.hq == 0) return hipSuccess;
+  const int64_t blocks = tokens < 65536 ? tokens : 65536;   // a token per block and pass
   const dim3 grid((unsigned)blocks);
   if (v_head_dim == 128) {
     if (o_bf16) hipLaunchKernelGGL((bwd_prep_kernel<128, true>), grid, dim3(256), 0, stream, p);
@@ -916,7 +945,7 @@ hipError_t pack_dd(const BwdParams &p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (p.tnq > 0)
-    hipLaunchKernelGGL((bwd_pack_q_kernel<D, DV>), dim3(p.tnq, p.hq, p.batch), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_pack_q_kernel<D, DV>), dim3(p.hq, p.tnq, p.batch), dim3(256), 0,
                        stream, p);
   return hipGetLastError();
 }
