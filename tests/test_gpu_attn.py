@@ -60,6 +60,9 @@ SMALL = [
     (2, 111, 111, 4, 2, 128, "f32", True, (20, 0), True),
     (1, 99, 140, 6, 1, 64, "f32", False, (-1, 3), False),
     (2, 70, 70, 2, 2, 128, "f32", True, (0, 0), True),
+    # fp32 kernel: 45 items (9 heads x 5 query tiles of 64) in runs of 6, the
+    # last one rising (dealt in reverse) with 3 positions past the end
+    (1, 320, 320, 9, 3, 64, "f32", True, (-1, -1), True),
 ]
 
 
