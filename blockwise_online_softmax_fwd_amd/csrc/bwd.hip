@@ -346,7 +346,8 @@ bwd_dq_kernel(BwdParams p) {
   // read together with the count (with no key tile the list is empty and the
   // count's word stands in)
   const uint32_t e0 = *(p.nkt > 0 ? lst : (const_list_t)(p.count + row));
-  const int n = p.count[row];
+  // clamped so that a schedule that does not fit can never send a read past its list
+  const int n = min((int)p.count[row], p.nkt);
   asm volatile("" ::"s"(e0), "s"(n));   // both loads issued before either is waited for
   const char *pack = (const char *)p.kvpack + ((int64_t)b * p.hkv + g) * p.nkt * TILE;
 
@@ -582,7 +583,7 @@ bwd_dkdv_kernel(BwdParams p) {
   // read together with the count (with no query tile the list is empty and
   // the count's word stands in)
   const uint32_t e0 = *(p.tnq > 0 ? lst : (const_list_t)(p.tcount + row));
-  const int nq = p.tcount[row];
+  const int nq = min((int)p.tcount[row], p.tnq);   // clamped like the dQ pass's count
   asm volatile("" ::"s"(e0), "s"(nq));   // both loads issued before either is waited for
   const int n = nq * p.group;         // visits: (query tile, head of the group)
 
